@@ -1,0 +1,229 @@
+// extern "C" entry points of libqlora_nf4: argument checks, workspace layout and
+// kernel sequencing. Every step of the layer runs in the kernels of quantize.hip
+// and gemm.hip; this file does no arithmetic on the data.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/qlora_nf4.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    g_err = std::string(where) + ": " + hipGetErrorString(e);
+    return -4;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+constexpr int64_t kMaxBlocks = (int64_t{1} << 32) - 1;
+
+bool nf4_counts(int64_t d_out, int64_t d_in, int64_t* n, int64_t* n_b, int64_t* n_g) {
+    if (d_out < 1 || d_in < 1) return false;
+    if (d_out > (int64_t{1} << 40) / d_in) return false;
+    *n = d_out * d_in;
+    *n_b = (*n + qn::kBlock - 1) / qn::kBlock;
+    *n_g = (*n_b + qn::kGroup - 1) / qn::kGroup;
+    return *n_b <= kMaxBlocks;
+}
+
+struct QuantWs {
+    int64_t absmax_off, limbs_off, bytes;
+    int grid;
+};
+
+QuantWs quant_ws(int64_t n_b) {
+    QuantWs w{};
+    w.grid = qn::quant_grid(n_b);
+    w.absmax_off = 0;
+    w.limbs_off = align_up(n_b * 4, 256);
+    w.bytes = w.limbs_off + align_up(static_cast<int64_t>(w.grid) * qn::kLimbs * 8, 256);
+    return w;
+}
+
+struct LinWs {
+    int64_t what, lora, adapt, adapt2, t, bytes;
+    int r_pad;
+};
+
+LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    LinWs w{};
+    w.r_pad = static_cast<int>(align_up(r, 64));
+    int64_t off = 0;
+    w.what = off;   off += align_up(2 * d_out * d_in, 256);                        // W_hat or W_hat^T
+    w.lora = off;   off += align_up(2 * d_seq * w.r_pad, 256);                     // s(XA^T) or s(dY B)
+    w.adapt = off;  off += align_up(2 * (d_out > d_in ? d_out : d_in) * w.r_pad, 256);  // B padded or A^T padded
+    w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T
+    w.t = off;      off += align_up(4 * static_cast<int64_t>(r), 256);              // fp32 A x (GEMV)
+    w.bytes = off;
+    return w;
+}
+
+int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                 int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r,
+                 const uint16_t* in, int64_t d_seq, uint16_t* out, void* ws, int64_t ws_bytes,
+                 LinWs* lw) {
+    if (!codes || !qconst || !qscale || !qmean || !A || !B || !in || !out || !ws)
+        return fail(-1, "null pointer argument");
+    if (d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1");
+    if (r < 1 || r > 256) return fail(-1, "r must be in [1, 256]");
+    if (!aligned(codes, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(in, 16) ||
+        !aligned(out, 16) || !aligned(ws, 256) || !aligned(qscale, 4) || !aligned(qmean, 4))
+        return fail(-1, "misaligned pointer (16 B for arrays, 256 B for the workspace)");
+    if (d_in % 64 != 0 || d_out % 64 != 0) return fail(-2, "d_in and d_out must be multiples of 64");
+    if (d_in > INT32_MAX || d_out > INT32_MAX || d_seq > INT32_MAX) return fail(-2, "dimension too large");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-2, "weight too large");
+    // the GEMM addresses each operand with 32-bit byte offsets
+    const int64_t kMaxBytes = int64_t{1} << 32;
+    if (2 * n >= kMaxBytes || 2 * d_seq * (d_out > d_in ? d_out : d_in) >= kMaxBytes)
+        return fail(-2, "an operand reaches 4 GiB");
+    *lw = linear_ws(d_out, d_in, d_seq, r);
+    if (ws_bytes < lw->bytes) return fail(-3, "workspace too small");
+    return 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qn_version(void) { return 100; }
+
+const char* qn_last_error(void) { return g_err.c_str(); }
+
+int qn_codebook(float* out16) {
+    if (!out16) return fail(-1, "null pointer argument");
+    std::memcpy(out16, qn::tables().code, sizeof(float) * 16);
+    return 0;
+}
+
+int qn_nf4_sizes(int64_t d_out, int64_t d_in, int64_t* codes_bytes, int64_t* n_blocks, int64_t* n_groups) {
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
+    if (codes_bytes) *codes_bytes = n_b * (qn::kBlock / 2);
+    if (n_blocks) *n_blocks = n_b;
+    if (n_groups) *n_groups = n_g;
+    return 0;
+}
+
+int64_t nf4_quantize_workspace_bytes(int64_t d_out, int64_t d_in) {
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return 0;
+    return quant_ws(n_b).bytes;
+}
+
+int nf4_quantize(const float* W, int64_t d_out, int64_t d_in, uint8_t* codes, int8_t* qconst,
+                 float* qscale, float* qmean, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!W || !codes || !qconst || !qscale || !qmean || !workspace) return fail(-1, "null pointer argument");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(workspace, 256) || !aligned(qscale, 4) ||
+        !aligned(qmean, 4))
+        return fail(-1, "misaligned pointer");
+    const QuantWs w = quant_ws(n_b);
+    if (workspace_bytes < w.bytes) return fail(-3, "workspace too small");
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = qn::launch_quantize(W, n, n_b, n_g, codes, qconst, qscale, qmean,
+                                       reinterpret_cast<float*>(ws + w.absmax_off),
+                                       reinterpret_cast<unsigned long long*>(ws + w.limbs_off), w.grid,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "nf4_quantize");
+    return 0;
+}
+
+int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                       int64_t d_out, int64_t d_in, uint16_t* W_bf16, void* stream) {
+    if (!codes || !qconst || !qscale || !qmean || !W_bf16) return fail(-1, "null pointer argument");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
+    if (!aligned(codes, 16) || !aligned(W_bf16, 16) || !aligned(qscale, 4) || !aligned(qmean, 4))
+        return fail(-1, "misaligned pointer");
+    hipError_t e = qn::launch_dequant_rows(codes, qconst, qscale, qmean, n, W_bf16,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "nf4_double_dequant");
+    return 0;
+}
+
+int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
+    return linear_ws(d_out, d_in, d_seq, r).bytes;
+}
+
+int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                     int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
+                     const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    LinWs lw;
+    int rc = check_linear(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, X, d_seq, Y, workspace,
+                          workspace_bytes, &lw);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e;
+    if (d_seq == 1) {
+        e = qn::launch_gemv_nf4(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, s, X, Y,
+                                reinterpret_cast<float*>(ws + lw.t), st);
+        if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
+        return 0;
+    }
+    uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);
+    uint16_t* t = reinterpret_cast<uint16_t*>(ws + lw.lora);
+    const uint16_t* q2 = B;
+    if (r != lw.r_pad) {
+        uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
+        if ((e = qn::launch_pad_cols(B, d_out, r, bpad, lw.r_pad, st)) != hipSuccess)
+            return hip_fail(e, "qlora_linear_fwd (pad B)");
+        q2 = bpad;
+    }
+    if ((e = qn::launch_dequant_rows(codes, qconst, qscale, qmean, d_out * d_in, what, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (dequant)");
+    if ((e = qn::launch_lora_prepass(X, d_in, d_seq, d_in, A, d_in, r, s, t, lw.r_pad, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (A X)");
+    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, q2, lw.r_pad, lw.r_pad, Y, d_out,
+                                d_seq, d_out, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (gemm)");
+    return 0;
+}
+
+int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                       int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
+                       const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+    LinWs lw;
+    int rc = check_linear(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, dY, d_seq, dX, workspace,
+                          workspace_bytes, &lw);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* whatT = reinterpret_cast<uint16_t*>(ws + lw.what);
+    uint16_t* u = reinterpret_cast<uint16_t*>(ws + lw.lora);
+    uint16_t* atpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
+    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + lw.adapt2);
+    hipError_t e;
+    if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (B^T)");
+    if ((e = qn::launch_transpose_pad(A, r, d_in, atpad, lw.r_pad, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (A^T)");
+    if ((e = qn::launch_dequant_transposed(codes, qconst, qscale, qmean, d_out, d_in, whatT, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (dequant)");
+    if ((e = qn::launch_lora_prepass(dY, d_out, d_seq, d_out, bt, d_out, r, s, u, lw.r_pad, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (B^T dY)");
+    if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
+                                d_in, d_seq, d_in, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (gemm)");
+    return 0;
+}
+
+}  // extern "C"

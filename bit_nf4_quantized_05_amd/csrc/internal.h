@@ -1,0 +1,59 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qn {
+
+constexpr int kBlock = 64;        // weights per NF4 block
+constexpr int kGroup = 256;       // block constants per double-quantisation group
+constexpr int kInt8Step = 127;    // symmetric INT8 code range [-127, 127]
+constexpr int kLimbs = 10;        // 32-bit limbs of the exact constant sum (covers 2^320)
+constexpr int kCells = 32;        // [-1, 1] split into 32 equal cells for the code search
+
+// Constant tables, built once on the host and passed to kernels by value.
+struct NF4Tables {
+    float code[16];                 // code book, ascending, code[7] == +0
+    float cell_thr[kCells];         // the single code threshold inside cell c, or +inf
+    uint32_t cell_base[kCells];     // number of thresholds below the cell's lower edge
+};
+
+// Returns the process-wide tables (built on first use, thread-safe).
+const NF4Tables& tables();
+
+// ---- quantize.hip ----
+int quant_grid(int64_t n_b);
+hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
+                           uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
+                           float* ws_absmax, unsigned long long* ws_limbs, int grid,
+                           hipStream_t st);
+hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                               const float* qmean, int64_t n, uint16_t* out, hipStream_t st);
+hipError_t launch_dequant_transposed(const uint8_t* codes, const int8_t* qconst,
+                                     const float* qscale, const float* qmean, int64_t d_out,
+                                     int64_t d_in, uint16_t* outT, hipStream_t st);
+
+// ---- gemm.hip ----
+// C[M,N] = bf16( P[M,K1] Q[N,K1]^T + P2[M,K2] Q2[N,K2]^T ), all row-major, K contiguous.
+// K1, K2 multiples of 64 (K2 may be 0); N multiple of 4.
+hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
+                          const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
+                          int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                          hipStream_t st);
+// OUT[M, r_pad] = bf16( s * P[M,K] R[r,K]^T ), zero in columns r..r_pad-1; K % 64 == 0.
+hipError_t launch_lora_prepass(const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
+                               const uint16_t* R, int64_t ldr, int r, float s,
+                               uint16_t* OUT, int r_pad, hipStream_t st);
+// dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
+hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
+                                uint16_t* dst, int64_t ld_dst, hipStream_t st);
+// dst[i, j] = j < cols ? src[i, j] : 0, for i < rows, j < ld_dst.
+hipError_t launch_pad_cols(const uint16_t* src, int64_t rows, int64_t cols,
+                           uint16_t* dst, int64_t ld_dst, hipStream_t st);
+// y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes.
+hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                           const float* qmean, int64_t d_out, int64_t d_in,
+                           const uint16_t* A, const uint16_t* B, int r, float s,
+                           const uint16_t* x, uint16_t* y, float* ws_t, hipStream_t st);
+
+}  // namespace qn

@@ -1,0 +1,144 @@
+/*
+ * qlora_nf4.h - C ABI of the MI355X (gfx950) QLoRA NF4 linear-layer library.
+ *
+ * The library implements the QLoRA linear layer described on these pages:
+ *   [P1] whoami-wesleyyou.top, "LoRA 与 QLoRA" (sections "LoRA", "1. NF4",
+ *        "2. Double Quantization (DQ)");
+ *   [P2] learn.ifs.name, Dettmers et al. 2023 deck "3 QLoRA Finetuning", cards 1-4;
+ *   [P4] jjjymmm.cn 2024/03 blog, sections "4-bit NormalFloat(NF4)",
+ *        "Double Quantization" and "QLoRA".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - W0 is d_out x d_in, row-major (d_in contiguous), float32 on input.
+ *  - Activations follow the pages' x in R^{d_in x d_seq} [P1 LoRA], stored as
+ *    a torch-style [d_seq, d_in] row-major array: each token's d_in features
+ *    are contiguous. Y and dY are [d_seq, d_out], dX is [d_seq, d_in].
+ *  - A is r x d_in and B is d_out x r, both row-major [P1 LoRA shapes].
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Every pointer argument is a DEVICE pointer (memory of the current HIP
+ *    device), 16-byte aligned, unless stated otherwise. The caller allocates
+ *    and owns every buffer, including workspaces; the library allocates no
+ *    device memory and keeps no per-call state, so calls on different streams
+ *    with different buffers may run concurrently.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on that stream and returns; outputs are ready once the
+ *    stream has reached the enqueued work. Outputs are overwritten, never
+ *    accumulated into.
+ *  - Quantised format (one NF4 + DQ weight):
+ *      n   = d_out * d_in,  n_b = ceil(n / 64) blocks,  n_g = ceil(n_b / 256) groups
+ *      codes  uint8 [n_b * 32] : 4-bit code of flat element 2i in the low nibble of
+ *                                byte i, element 2i+1 in the high nibble; the flat
+ *                                index is row-major over W0; elements past n are
+ *                                zero padding and hold the exact-zero code 7.
+ *      qconst int8  [n_b]      : 8-bit code of each block's absmax constant.
+ *      qscale float [n_g]      : per-group scale b_g of the centred constants.
+ *      qmean  float [1]        : mean mu of all block constants.
+ *
+ * Return codes: 0 success; -1 invalid argument (null or misaligned pointer,
+ * non-positive size, ...); -2 unsupported shape; -3 workspace too small;
+ * -4 HIP launch error. On a non-zero return nothing has been enqueued (except
+ * for -4, where earlier kernels of the same call may have been). A short text
+ * for the last error of the calling thread is returned by qn_last_error().
+ * Asynchronous device faults surface at the caller's next synchronisation.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Library version, as major*10000 + minor*100 + patch. */
+int qn_version(void);
+
+/* Text describing the last non-zero return on the calling thread ("" if none).
+ * The pointer stays valid until the next library call on the same thread. */
+const char* qn_last_error(void);
+
+/* Copies the library's 16-entry float32 NF4 code book into host memory `out16`
+ * (ascending; entry 7 is the exact zero). Built from normal quantiles with
+ * separate negative and positive halves sharing one zero [P2 card 3; P1 1. NF4;
+ * P4 quant book]. Host pointer. Returns 0 or -1 (null pointer). */
+int qn_codebook(float* out16);
+
+/* Sizes of the quantised buffers for a d_out x d_in weight, in elements:
+ * codes bytes (n_b*32), qconst entries (n_b), qscale entries (n_g).
+ * Host pointers; any of them may be NULL. Returns 0, or -1 if a size is < 1. */
+int qn_nf4_sizes(int64_t d_out, int64_t d_in, int64_t* codes_bytes,
+                 int64_t* n_blocks, int64_t* n_groups);
+
+/* Workspace bytes nf4_quantize needs for a d_out x d_in weight (0 on bad sizes). */
+int64_t nf4_quantize_workspace_bytes(int64_t d_out, int64_t d_in);
+
+/*
+ * nf4_quantize - block-wise NF4 quantisation with Double Quantisation.
+ *   [P1 归一化与匹配 and 2. DQ; P2 cards 2-4; P4 NF4 and Double Quantization]
+ * Level 1, per block j of 64 consecutive flat elements: a_j = max|w|; each w is
+ * normalised x = w / a_j (IEEE float32 division) and coded as the nearest of the
+ * 16 code-book values, the lower index on an exact tie; a block of zeros codes
+ * to 7.  Level 2: mu = the mean of all a_j, rounded once to float32; per group
+ * g of 256 consecutive blocks, d_j = a_j - mu, b_g = max|d_j|, and
+ * qconst_j = round-half-even((d_j / b_g) * 127) in [-127, 127] (0 if b_g = 0),
+ * each step one float32 operation.
+ *   W          [d_out*d_in] float32, finite values (non-finite input: unspecified codes)
+ *   codes, qconst, qscale, qmean : outputs, sizes as in qn_nf4_sizes
+ *   workspace  >= nf4_quantize_workspace_bytes(d_out, d_in) bytes of device memory
+ * Any d_out, d_in >= 1 (n need not be a multiple of 64). Result is
+ * deterministic and bit-identical for every launch configuration.
+ */
+int nf4_quantize(const float* W, int64_t d_out, int64_t d_in,
+                 uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
+                 void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * nf4_double_dequant - constants first, then weights, to BF16.
+ *   [P4 QLoRA: doubleDequant; P1 2. DQ a_hat = mu + b r_hat; P1 4-bit -> BF16]
+ * a_hat_j = mu + b_g * (qconst_j / 127) (separate float32 multiply and add),
+ * w_hat = bf16_round_nearest_even(code_book[code] * a_hat_j).
+ *   W_bf16 [d_out*d_in] uint16 output, row-major like W0.
+ * Any d_out, d_in >= 1.
+ */
+int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                       const float* qmean, int64_t d_out, int64_t d_in,
+                       uint16_t* W_bf16, void* stream);
+
+/* Workspace bytes qlora_linear_fwd / qlora_linear_bwd_x need (0 on bad sizes). */
+int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+
+/*
+ * qlora_linear_fwd - Y = dequant(W) X + s B (A X) with BF16 operands.
+ *   [P1 LoRA: y = W0 x + s B(A x), sequence input x in R^{d_in x d_seq};
+ *    P1 1. NF4: 4-bit -> dequant -> BF16 -> GEMM; P2 card 1]
+ *   A [r, d_in], B [d_out, r], X [d_seq, d_in] bf16; Y [d_seq, d_out] bf16 output
+ *   (float32 accumulation, one final round to nearest even).
+ *   s is the LoRA scale (float32).
+ * Requires d_in % 64 == 0 and d_out % 64 == 0 (-2 otherwise), 1 <= r <= 256,
+ * d_seq >= 1. d_seq == 1 runs a streaming GEMV over the packed codes.
+ */
+int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                     const float* qmean, int64_t d_out, int64_t d_in,
+                     const uint16_t* A, const uint16_t* B, int r, float s,
+                     const uint16_t* X, int64_t d_seq, uint16_t* Y,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd_x - input gradient dX = dequant(W)^T dY + s A^T (B^T dY).
+ *   [P2 card 1: gradients flow through the dequantised weights, only A and B
+ *    are trained; the formula is the adjoint of the forward above]
+ *   dY [d_seq, d_out] bf16; dX [d_seq, d_in] bf16 output. Same shape rules as
+ *   qlora_linear_fwd.
+ */
+int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                       const float* qmean, int64_t d_out, int64_t d_in,
+                       const uint16_t* A, const uint16_t* B, int r, float s,
+                       const uint16_t* dY, int64_t d_seq, uint16_t* dX,
+                       void* workspace, int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_NF4_H */

@@ -1,0 +1,94 @@
+"""Host-only checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments before touching a GPU. Also checks
+that the library's independently built NF4 code book has the same float32 bits
+as the oracle's (a host-side table query, no device work)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_05_amd as qn
+from bit_nf4_quantized_05_amd import _lib
+from oracle import nf4_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert {"nf4_quantize", "nf4_double_dequant", "qlora_linear_fwd", "qlora_linear_bwd_x"} <= set(names)
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must mirror the header"
+
+
+def test_version_and_sizes():
+    assert qn.version() >= 100
+    assert qn.nf4_sizes(256, 256) == (32768, 1024, 4)
+    assert qn.nf4_sizes(3, 50) == (3 * 32, 3, 1)
+    assert qn.nf4_sizes(28672, 8192) == (28672 * 8192 // 2, 3670016, 14336)
+    assert qn.quantize_workspace_bytes(4096, 4096) >= 262144 * 4
+    assert qn.linear_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 4096 * 4096
+    assert qn.quantize_workspace_bytes(0, 5) == 0
+    assert qn.linear_workspace_bytes(64, 64, 1, 0) == 0
+
+
+def test_library_code_book_bits_equal_oracle():
+    lib_cb = np.array(qn.codebook(), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), O.codebook().view(np.uint32))
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address: every call below fails validation first
+
+
+def test_argument_validation_without_device_work():
+    lib = _lib.lib()
+    # null pointers -> -1
+    assert lib.nf4_quantize(None, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert b"null" in lib.qn_last_error()
+    # non-positive sizes -> -1
+    assert lib.nf4_quantize(FAKE, 0, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    # misaligned weight pointer -> -1
+    assert lib.nf4_quantize(FAKE + 4, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    # workspace too small -> -3
+    assert lib.nf4_quantize(FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == -3
+    # linear: d_in not a multiple of 64 -> -2
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 96, FAKE, FAKE, 8, 2.0, FAKE, 16, FAKE, FAKE, 1 << 30, None]
+    assert lib.qlora_linear_fwd(*args) == -2
+    assert lib.qlora_linear_bwd_x(*args) == -2
+    # r out of range -> -1
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 0, 2.0, FAKE, 16, FAKE, FAKE, 1 << 30, None]
+    assert lib.qlora_linear_fwd(*args) == -1
+    args[8] = 257
+    assert lib.qlora_linear_fwd(*args) == -1
+    # workspace too small -> -3
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, 16, FAKE, FAKE, 16, None]
+    assert lib.qlora_linear_fwd(*args) == -3
+    assert lib.qlora_linear_bwd_x(*args) == -3
+    # null output -> -1
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, 16, None, FAKE, 1 << 30, None]
+    assert lib.qlora_linear_fwd(*args) == -1
+    assert lib.nf4_double_dequant(FAKE, FAKE, FAKE, FAKE, 64, 64, None, None) == -1
+
+
+def test_codebook_null_pointer():
+    assert _lib.lib().qn_codebook(None) == -1
+
+
+def test_missing_library_is_an_error(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(_lib.QLoRAError):
+        _lib.lib()
+    monkeypatch.undo()
+    assert isinstance(_lib.lib(), ctypes.CDLL)

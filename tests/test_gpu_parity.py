@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact: NF4 codes, INT8 constant codes, group scales, the mean, dequantised
+bf16 weights. Tolerance (see parity.py): forward and input-gradient products.
+Small and ragged shapes are checked in full; the full-size layers are checked
+in full where the oracle is cheap (second-level constants, the GEMV) and on
+sampled blocks / rows / columns / tokens elsewhere.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_05_amd as qn
+import workloads as WL
+from oracle import nf4_oracle as O
+from parity import OracleLayer, bf16_bits, bf16_f64, check_close, dev, to_gpu_bf16, to_gpu_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _normal(shape, seed, sigma=0.02):
+    return (np.random.default_rng(seed).standard_normal(shape) * sigma).astype(np.float32)
+
+
+def _gpu_quantize(w: np.ndarray):
+    q = qn.quantize(to_gpu_f32(w))
+    torch.cuda.synchronize()
+    return q
+
+
+def _assert_quant_equal(q, ref, sel_blocks=None):
+    assert np.array_equal(q.qmean.cpu().numpy().view(np.uint32), ref["qmean"].view(np.uint32)), "qmean"
+    assert np.array_equal(q.qscale.cpu().numpy().view(np.uint32), ref["qscale"].view(np.uint32)), "qscale"
+    assert np.array_equal(q.qconst.cpu().numpy(), ref["qconst"]), "qconst"
+    got = q.codes.cpu().numpy()
+    if sel_blocks is None:
+        assert np.array_equal(got, ref["codes"]), "codes"
+    else:
+        got_b = got.reshape(-1, 32)[sel_blocks]
+        assert np.array_equal(got_b, ref["codes"].reshape(-1, 32)), "codes (sampled blocks)"
+
+
+def _tie_matrix():
+    """Blocks whose normalised values sit exactly on, just below and just above
+    every code midpoint, plus -0.0, subnormals, tiny and huge absmax blocks."""
+    cb = O.codebook().astype(np.float64)
+    vals = []
+    for k in range(15):
+        m = np.float32((cb[k] + cb[k + 1]) / 2)
+        vals += [m, np.nextafter(m, np.float32(-2)), np.nextafter(m, np.float32(2))]
+    vals = np.array(vals, np.float32)                       # 45 values in [-1, 1]
+    rows = []
+    for scale in (1.0, 0.5, 3.0e-3, 1.0e30, 1.0e-36):
+        b = np.zeros(64, np.float32)
+        b[0] = 1.0
+        b[1:46] = vals
+        b[46] = -0.0
+        b[47] = -1.0
+        b[48] = 1e-45
+        rows.append((b * np.float32(scale)).astype(np.float32))
+    rows.append(np.full(64, -0.0, np.float32))                # all -0: absmax 0
+    rows.append(np.full(64, 7.0e-45, np.float32))             # subnormal absmax
+    rows.append(np.linspace(-1, 1, 64).astype(np.float32))
+    return np.stack(rows)
+
+
+SMALL = [
+    ("tiny_256x256", lambda: WL.make_weight(WL.CONFIGS["tiny"])),
+    ("ragged_3x50", lambda: _normal((3, 50), 1)),
+    ("one_1x1", lambda: np.array([[0.7]], np.float32)),
+    ("ragged_100x37", lambda: _normal((100, 37), 2)),
+    ("partial_group_1000x67", lambda: _normal((1000, 67), 3)),
+    ("rows_64x16448", lambda: _normal((64, 64 * 257), 4)),
+    ("tail_5x32771", lambda: _normal((5, 32771), 5)),
+    ("zeros_128x128", lambda: np.zeros((128, 128), np.float32)),
+    ("constant_64x256", lambda: np.full((64, 256), 0.5, np.float32)),
+    ("ties_and_specials", _tie_matrix),
+    ("outliers_512x1024", lambda: WL.make_weight(WL.custom("o", 512, 1024, 1, 8, outlier_frac=0.001))),
+    ("wide_range_300x512", lambda: (_normal((300, 512), 6) * np.exp(
+        np.random.default_rng(7).uniform(-40, 40, (300, 1))).astype(np.float32)).astype(np.float32)),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_quantize_and_dequant_bit_exact_small(name, make):
+    w = make()
+    _say(f"[quantize] {name} shape={w.shape}")
+    q = _gpu_quantize(w)
+    ref = O.quantize(w)
+    _assert_quant_equal(q, ref)
+    wh = qn.double_dequant(q)
+    torch.cuda.synchronize()
+    want = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], *w.shape)
+    assert np.array_equal(bf16_bits(wh), want)
+
+
+def test_quantize_is_deterministic_and_reusable():
+    w = _normal((777, 320), 11)
+    q1 = _gpu_quantize(w)
+    q2 = qn.quantize(to_gpu_f32(w), out=qn.alloc_weight(777, 320, dev()))
+    torch.cuda.synchronize()
+    for a, b in ((q1.codes, q2.codes), (q1.qconst, q2.qconst), (q1.qscale, q2.qscale), (q1.qmean, q2.qmean)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+FULL = ["decode", "mlp_up", "mlp_down", "large"]
+
+
+@pytest.mark.parametrize("cfg_name", FULL)
+def test_quantize_full_size(cfg_name):
+    cfg = WL.CONFIGS[cfg_name]
+    _say(f"[quantize full] {cfg_name} {cfg.d_out}x{cfg.d_in}")
+    w = WL.make_weight(cfg)
+    q = _gpu_quantize(w)
+    ol = OracleLayer(w)
+    n_b = ol.absmax.size
+    rng = np.random.default_rng(99)
+    sel = np.unique(np.concatenate([np.arange(64), n_b - 64 + np.arange(64), rng.choice(n_b, 4096, replace=False)]))
+    ref = {"qmean": np.array([ol.mu], np.float32), "qscale": ol.qscale, "qconst": ol.qconst,
+           "codes": O.pack_codes(ol.codes_of(sel))}
+    _assert_quant_equal(q, ref, sel_blocks=sel)
+    # dequantised rows (bit-exact) on a sample of rows
+    rows = np.unique(np.concatenate([[0, cfg.d_out - 1], rng.choice(cfg.d_out, 32, replace=False)]))
+    wh = qn.double_dequant(q)
+    torch.cuda.synchronize()
+    got = bf16_bits(wh[torch.from_numpy(rows).to(dev())])
+    assert np.array_equal(got, ol.rows(rows))
+
+
+# ---------------------------------------------------------------- products
+
+def _layer(cfg):
+    w = WL.make_weight(cfg)
+    a, b = WL.make_lora(cfg)
+    return w, a, b
+
+
+def _fwd_bwd_full_check(cfg, check_bwd=True):
+    w, a, b = _layer(cfg)
+    q = _gpu_quantize(w)
+    ref = O.quantize(w)
+    wh = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], cfg.d_out, cfg.d_in)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    x = WL.make_x(cfg)
+    y = qn.linear_fwd(q, A, B, cfg.s, to_gpu_bf16(x))
+    torch.cuda.synchronize()
+    check_close(bf16_f64(y), O.linear_fwd(wh, a, b, cfg.s, x), f"fwd {cfg.name}")
+    if check_bwd:
+        dy = WL.make_dy(cfg)
+        dx = qn.linear_bwd_x(q, A, B, cfg.s, to_gpu_bf16(dy))
+        torch.cuda.synchronize()
+        check_close(bf16_f64(dx), O.linear_bwd_x(wh, a, b, cfg.s, dy), f"bwd_x {cfg.name}")
+
+
+LINEAR_SMALL = [
+    WL.CONFIGS["tiny"],
+    WL.custom("ragged", 320, 192, 300, 100, s=1.5),
+    WL.custom("r1", 64, 64, 5, 1, s=0.5),
+    WL.custom("r256", 128, 256, 2, 256, s=2.0),
+    WL.custom("tall", 576, 128, 513, 64, s=1.0, outlier_frac=0.01),
+    WL.custom("long_k", 256, 2048, 96, 16, s=2.0),
+    WL.custom("gemv_small", 192, 320, 1, 8, s=2.0),
+    WL.custom("gemv_r64", 512, 1024, 1, 64, s=1.0),
+]
+
+
+@pytest.mark.parametrize("cfg", LINEAR_SMALL, ids=[c.name for c in LINEAR_SMALL])
+def test_linear_fwd_bwd_small(cfg):
+    _say(f"[linear] {cfg.name} d_out={cfg.d_out} d_in={cfg.d_in} d_seq={cfg.d_seq} r={cfg.r}")
+    _fwd_bwd_full_check(cfg)
+
+
+def test_identity_input_returns_dequantised_weight_exactly():
+    cfg = WL.custom("eye", 192, 256, 256, 8)
+    w, a, b = _layer(cfg)
+    q = _gpu_quantize(w)
+    ref = O.quantize(w)
+    wh = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], cfg.d_out, cfg.d_in)
+    A = to_gpu_bf16(a)
+    zeroB = torch.zeros(cfg.d_out, cfg.r, dtype=torch.bfloat16, device=dev())
+    eye_in = torch.eye(cfg.d_in, dtype=torch.bfloat16, device=dev())
+    y = qn.linear_fwd(q, A, zeroB, 2.0, eye_in)           # Y[t, o] = W_hat[o, t]
+    eye_out = torch.eye(cfg.d_out, dtype=torch.bfloat16, device=dev())
+    dx = qn.linear_bwd_x(q, A, zeroB, 2.0, eye_out)        # dX[t, i] = W_hat[t, i]
+    torch.cuda.synchronize()
+    # compare values (+0 == -0): one nonzero product per dot product is exact
+    assert np.array_equal(bf16_f64(y), O.bf16_bits_to_f32(wh).astype(np.float64).T)
+    assert np.array_equal(bf16_f64(dx), O.bf16_bits_to_f32(wh).astype(np.float64))
+
+
+def test_decode_gemv_full_size():
+    cfg = WL.CONFIGS["decode"]
+    _say("[gemv] decode 4096x4096 d_seq=1 r=16")
+    _fwd_bwd_full_check(cfg, check_bwd=True)
+
+
+@pytest.mark.parametrize("cfg_name", ["prefill", "mlp_up", "mlp_down", "large"])
+def test_linear_full_size_sampled(cfg_name):
+    cfg = WL.CONFIGS[cfg_name]
+    _say(f"[linear full] {cfg_name} d_out={cfg.d_out} d_in={cfg.d_in} d_seq={cfg.d_seq} r={cfg.r}")
+    w, a, b = _layer(cfg)
+    q = _gpu_quantize(w)
+    del w
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    ol = OracleLayer(WL.make_weight(cfg))
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([[0, cfg.d_seq - 1], rng.choice(cfg.d_seq, 62, replace=False)]))
+    rows = np.unique(np.concatenate([[0, cfg.d_out - 1], rng.choice(cfg.d_out, 62, replace=False)]))
+    cblk = np.unique(np.concatenate([[0, cfg.d_in // 64 - 1], rng.choice(cfg.d_in // 64, 2, replace=False)]))
+    tt = torch.from_numpy(toks).to(dev())
+
+    x = WL.make_x(cfg)
+    y = qn.linear_fwd(q, A, B, cfg.s, to_gpu_bf16(x))
+    torch.cuda.synchronize()
+    got = bf16_f64(y[tt][:, torch.from_numpy(rows).to(dev())])
+    del y
+    ref = O.linear_fwd(ol.rows(rows), a, b[rows], cfg.s, x[toks])
+    check_close(got, ref, f"fwd {cfg_name} (sampled)")
+    del x
+
+    dy = WL.make_dy(cfg)
+    dx = qn.linear_bwd_x(q, A, B, cfg.s, to_gpu_bf16(dy))
+    torch.cuda.synchronize()
+    cols = (cblk[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    got = bf16_f64(dx[tt][:, torch.from_numpy(cols).to(dev())])
+    ref = O.linear_bwd_x(ol.col_blocks(cblk), a[:, cols], b, cfg.s, dy[toks])
+    check_close(got, ref, f"bwd_x {cfg_name} (sampled)")
