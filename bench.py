@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the QLoRA NF4 linear-layer hot path on one MI355X.
+
+One step = every stage of the path on the 4096 x 4096 layer (NF4 blocks of 64,
+DQ groups of 256, LoRA r = 16, s = 2), inputs already resident in HBM:
+    nf4_quantize(W)                  block absmax, NF4 codes, DQ constants
+    qlora_linear_fwd(X), d_seq=4096  dequant + A X pre-pass + fused MFMA GEMM
+    qlora_linear_bwd_x(dY)           transposed dequant + B^T dY + fused MFMA GEMM
+    qlora_linear_fwd(x), d_seq=1     streaming GEMV on one of 32 rotated layer copies
+`value` = algorithmic flops of the step (both GEMMs with their LoRA terms and the
+GEMV; quantisation counts 0 flops) / step time, in TFLOP/s.
+
+Also reported: per-kernel average durations (HIP events recorded by the library
+on the kernel's own stream during the timed steps), the MFMA roofline fraction of
+the dominant kernel (the GEMM), the decode path's effective GB/s over 32 layer
+copies (> 256 MB, beyond the Infinity Cache), and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "QLoRA linear TFLOP/s (prefill/bwd) + effective GB/s (d_seq=1) at 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-copies", type=int, default=32)
+    ap.add_argument("--decode-iters", type=int, default=256)
+    ap.add_argument("--cpu-tokens", type=int, default=512,
+                    help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline)")
+    return ap.parse_args()
+
+
+def decode_bytes(cfg) -> int:
+    """Algorithmic HBM bytes of one d_seq = 1 call: packed codes, INT8 constants,
+    group scales, mean, A, B, x and y."""
+    n = cfg.d_out * cfg.d_in
+    n_b = n // 64
+    n_g = -(-n_b // 256)
+    return n // 2 + n_b + 4 * n_g + 4 + 2 * cfg.r * (cfg.d_in + cfg.d_out) + 2 * cfg.d_in + 2 * cfg.d_out
+
+
+def cpu_baseline(cfg, tokens: int) -> dict:
+    """The oracle, as it stands, on a bounded sample: full quantise + dequantise of
+    W, then forward and input gradient for `tokens` tokens in float64."""
+    import numpy as np
+    import workloads as WL
+    from oracle import nf4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    w = WL.make_weight(cfg)
+    a, b = WL.make_lora(cfg)
+    x = WL.make_x(cfg)[:tokens]
+    dy = WL.make_dy(cfg)[:tokens]
+    t0 = time.perf_counter()
+    q = O.quantize(w)
+    wh = O.double_dequant(q["codes"], q["qconst"], q["qscale"], q["qmean"], cfg.d_out, cfg.d_in)
+    O.linear_fwd(wh, a, b, cfg.s, x)
+    O.linear_bwd_x(wh, a, b, cfg.s, dy)
+    dt = time.perf_counter() - t0
+    flops = 2 * (2 * cfg.d_out * cfg.d_in * tokens + 2 * cfg.r * tokens * (cfg.d_in + cfg.d_out))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": (f"{cfg.d_out}x{cfg.d_in} layer: full NF4+DQ quantise and bf16 dequantise, then "
+                       f"fwd + dX for {tokens} of the {cfg.d_seq} tokens in float64 (numpy; BLAS threads = cores)")}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU path is design-only in this library.", flush=True)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_05_amd as qn
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    cfg = WL.CONFIGS["prefill"]
+    dcfg = WL.CONFIGS["decode"]
+    assert (cfg.d_out, cfg.d_in, cfg.r, cfg.s) == (dcfg.d_out, dcfg.d_in, dcfg.r, dcfg.s)
+
+    def bf16(bits):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    log("[bench] generating inputs")
+    W = torch.from_numpy(WL.make_weight(cfg)).to(dev)
+    a_bits, b_bits = WL.make_lora(cfg)
+    A, B = bf16(a_bits), bf16(b_bits)
+    X = bf16(WL.make_x(cfg))
+    dY = bf16(WL.make_dy(cfg))
+    x1 = bf16(WL.make_x(dcfg))
+
+    q = qn.quantize(W)
+    qws = torch.empty(qn.quantize_workspace_bytes(cfg.d_out, cfg.d_in), dtype=torch.uint8, device=dev)
+    lws = torch.empty(qn.linear_workspace_bytes(cfg.d_out, cfg.d_in, cfg.d_seq, cfg.r), dtype=torch.uint8,
+                      device=dev)
+    dws = torch.empty(qn.linear_workspace_bytes(dcfg.d_out, dcfg.d_in, 1, dcfg.r), dtype=torch.uint8, device=dev)
+    Y = torch.empty(cfg.d_seq, cfg.d_out, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(cfg.d_seq, cfg.d_in, dtype=torch.bfloat16, device=dev)
+    y1 = torch.empty(1, dcfg.d_out, dtype=torch.bfloat16, device=dev)
+    copies = []
+    for _ in range(args.decode_copies):
+        c = qn.alloc_weight(dcfg.d_out, dcfg.d_in, dev)
+        for dst, src in ((c.codes, q.codes), (c.qconst, q.qconst), (c.qscale, q.qscale), (c.qmean, q.qmean)):
+            dst.copy_(src)
+        copies.append(c)
+    torch.cuda.synchronize()
+
+    def step(i):
+        qn.quantize(W, out=q, workspace=qws)
+        qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=lws)
+        qn.linear_bwd_x(q, A, B, cfg.s, dY, out=dX, workspace=lws)
+        qn.linear_fwd(copies[i % len(copies)], A, B, dcfg.s, x1, out=y1, workspace=dws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, library kernel timing on
+    log(f"[bench] timing {args.steps} steps")
+    qn.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = qn.profile_read()
+    qn.profile_enable(False)
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_flops = 2 * cfg.fwd_flops() + dcfg.fwd_flops()
+    value = step_flops / (elapsed / args.steps) / 1e12
+    kernels = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in sorted(prof.items())}
+    log("[bench] kernels:", json.dumps(kernels))
+
+    # dominant kernel: the fused GEMM (fwd and dX launches have equal algorithmic flops)
+    g_n, g_ms = prof["gemm_nt_kernel"]
+    gemm_flops = 2 * cfg.d_seq * cfg.d_out * cfg.d_in + 2 * cfg.d_seq * cfg.d_out * cfg.r
+    achieved = gemm_flops / (g_ms / g_n * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "gemm_nt_kernel", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None}
+
+    # ---- decode (d_seq = 1) over rotated layer copies
+    log(f"[bench] decode: {args.decode_iters} calls over {len(copies)} copies")
+    for i in range(len(copies)):
+        qn.linear_fwd(copies[i], A, B, dcfg.s, x1, out=y1, workspace=dws)
+    torch.cuda.synchronize()
+    qn.profile_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.decode_iters):
+        qn.linear_fwd(copies[i % len(copies)], A, B, dcfg.s, x1, out=y1, workspace=dws)
+    torch.cuda.synchronize()
+    d_elapsed = time.perf_counter() - t0
+    dprof = qn.profile_read()
+    qn.profile_enable(False)
+    nbytes = decode_bytes(dcfg)
+    gv_n, gv_ms = dprof["gemv_nf4_kernel"]
+    ax_n, ax_ms = dprof["lora_ax_kernel"]
+    kern_us = 1e3 * (gv_ms / gv_n + ax_ms / ax_n)
+    decode = {"metric": "effective GB/s (d_seq=1)", "value": round(nbytes / (kern_us * 1e-6) / 1e9, 1),
+              "unit": "GB/s", "bytes_per_call": nbytes, "kernel_us": round(kern_us, 3),
+              "gemv_kernel_us": round(1e3 * gv_ms / gv_n, 3),
+              "call_us_back_to_back": round(1e6 * d_elapsed / args.decode_iters, 3),
+              "copies": len(copies),
+              "roofline": {"bound": "hbm", "kernel": "gemv_nf4_kernel + lora_ax_kernel",
+                           "achieved": round(nbytes / (kern_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": round(nbytes / (kern_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                           "traffic": None}}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian weights and activations, workloads.py)",
+        "config": {"workload": "4096x4096 NF4/64+DQ/256 layer, r=16 s=2: quantize + fwd and dX at d_seq=4096 "
+                               "+ decode GEMV at d_seq=1",
+                   "d_out": cfg.d_out, "d_in": cfg.d_in, "d_seq": cfg.d_seq, "r": cfg.r, "s": cfg.s,
+                   "decode_copies": len(copies)},
+        "roofline": roofline,
+        "decode": decode,
+        "kernels": kernels,
+    }
+    if args.cpu_tokens > 0:
+        log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     linear_fwd,
     linear_workspace_bytes,
     nf4_sizes,
+    profile_enable,
+    profile_read,
     quantize,
     quantize_workspace_bytes,
     version,

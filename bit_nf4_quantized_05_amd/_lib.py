@@ -36,6 +36,8 @@ SIGNATURES = {
                                   _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_float,
                                     _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "qn_profile_enable": (_c_int, [_c_int]),
+    "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
 }
 
 _lib = None
@@ -192,3 +194,25 @@ def linear_bwd_x(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, dY: t
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """qlora_linear_bwd_x: dX [d_seq, d_in] = dY W_hat + s (dY B) A."""
     return _linear("qlora_linear_bwd_x", q, A, B, s, dY, q.d_out, q.d_in, out, workspace)
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (clearing old records) or stop per-kernel event timing in the library."""
+    _check(lib().qn_profile_enable(1 if on else 0), "qn_profile_enable")
+
+
+def profile_read(cap: int = 64) -> dict:
+    """{kernel name: (launches, total ms)} of the kernels timed since profile_enable."""
+    name_len = 96
+    names = ctypes.create_string_buffer(name_len * cap)
+    launches = (ctypes.c_int64 * cap)()
+    total = (ctypes.c_double * cap)()
+    n = lib().qn_profile_read(ctypes.addressof(names), name_len, ctypes.addressof(launches),
+                              ctypes.addressof(total), cap)
+    if n < 0:
+        _check(n, "qn_profile_read")
+    out = {}
+    for i in range(min(n, cap)):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (int(launches[i]), float(total[i]))
+    return out

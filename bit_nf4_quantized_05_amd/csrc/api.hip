@@ -3,9 +3,13 @@
 // and gemm.hip; this file does no arithmetic on the data.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/qlora_nf4.h"
 #include "internal.h"
@@ -97,7 +101,84 @@ int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale
 
 }  // namespace
 
+// ---- optional kernel timing -------------------------------------------------
+namespace qn {
+namespace {
+struct ProfRec {
+    const char* name;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_prof;
+
+void prof_clear_locked() {
+    for (auto& r : g_prof) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_prof.clear();
+}
+}  // namespace
+
+void* prof_begin(hipStream_t st) {
+    if (!g_prof_on.load(std::memory_order_relaxed)) return nullptr;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventRecord(e, st) != hipSuccess) {
+        (void)hipEventDestroy(e);
+        return nullptr;
+    }
+    return e;
+}
+
+void prof_end(void* token, const char* name, hipStream_t st) {
+    if (!token) return;
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipEventDestroy(static_cast<hipEvent_t>(token));
+        return;
+    }
+    (void)hipEventRecord(e, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({name, static_cast<hipEvent_t>(token), e});
+}
+}  // namespace qn
+
 extern "C" {
+
+int qn_profile_enable(int on) {
+    std::lock_guard<std::mutex> lk(qn::g_prof_mu);
+    qn::prof_clear_locked();
+    qn::g_prof_on.store(on != 0);
+    return 0;
+}
+
+int qn_profile_read(char* names, int name_len, int64_t* launches, double* total_ms, int cap) {
+    if (!names || !launches || !total_ms || name_len < 2 || cap < 0) return fail(-1, "bad argument");
+    std::lock_guard<std::mutex> lk(qn::g_prof_mu);
+    std::map<std::string, std::pair<int64_t, double>> agg;
+    for (auto& r : qn::g_prof) {
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "qn_profile_read");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "qn_profile_read");
+        auto& a = agg[r.name];
+        a.first += 1;
+        a.second += ms;
+    }
+    int i = 0;
+    for (auto& kv : agg) {
+        if (i >= cap) break;
+        std::strncpy(names + static_cast<size_t>(i) * name_len, kv.first.c_str(), name_len - 1);
+        names[static_cast<size_t>(i) * name_len + name_len - 1] = 0;
+        launches[i] = kv.second.first;
+        total_ms[i] = kv.second.second;
+        ++i;
+    }
+    return static_cast<int>(agg.size());
+}
 
 int qn_version(void) { return 100; }
 

@@ -416,7 +416,7 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.P = P; g.ldp = ldp; g.Q = Q; g.ldq = ldq; g.kt1 = static_cast<int>(K1 / BK);
     g.P2 = P2; g.ldp2 = ldp2; g.Q2 = Q2; g.ldq2 = ldq2; g.kt2 = static_cast<int>(K2 / BK);
     g.C = C; g.ldc = ldc; g.M = static_cast<int>(M); g.N = static_cast<int>(N);
-    hipLaunchKernelGGL(gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(kGT), 0, st, g);
+    QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(kGT), 0, st, g);
     return hipGetLastError();
 }
 
@@ -426,10 +426,10 @@ hipError_t launch_lora_prepass(const uint16_t* P, int64_t ldp, int64_t M, int64_
     const dim3 grid(static_cast<unsigned>((M + 31) / 32));
     const int Mi = static_cast<int>(M), Ki = static_cast<int>(K);
     switch (r_pad / 32) {
-        case 2: hipLaunchKernelGGL(lora_prepass_kernel<2>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 4: hipLaunchKernelGGL(lora_prepass_kernel<4>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 6: hipLaunchKernelGGL(lora_prepass_kernel<6>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 8: hipLaunchKernelGGL(lora_prepass_kernel<8>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
+        case 2: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<2>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
+        case 4: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<4>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
+        case 6: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<6>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
+        case 8: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<8>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -438,7 +438,7 @@ hipError_t launch_lora_prepass(const uint16_t* P, int64_t ldp, int64_t M, int64_
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st) {
     const int64_t total = cols * ld_dst;
-    hipLaunchKernelGGL(transpose_pad_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
+    QN_LAUNCH("transpose_pad_kernel", st, transpose_pad_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
                        src, rows, cols, dst, ld_dst);
     return hipGetLastError();
 }
@@ -446,7 +446,7 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
 hipError_t launch_pad_cols(const uint16_t* src, int64_t rows, int64_t cols,
                            uint16_t* dst, int64_t ld_dst, hipStream_t st) {
     const int64_t total = rows * ld_dst;
-    hipLaunchKernelGGL(pad_cols_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
+    QN_LAUNCH("pad_cols_kernel", st, pad_cols_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
                        src, rows, cols, dst, ld_dst);
     return hipGetLastError();
 }
@@ -455,10 +455,10 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const flo
                            const float* qmean, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_t, hipStream_t st) {
-    hipLaunchKernelGGL(lora_ax_kernel, dim3(r), dim3(256), 0, st, A, static_cast<int>(d_in), x, s, ws_t);
+    QN_LAUNCH("lora_ax_kernel", st, lora_ax_kernel, dim3(r), dim3(256), 0, st, A, static_cast<int>(d_in), x, s, ws_t);
     const int64_t rows_per_wg = 4 * kRowsPerWave;
     const dim3 grid(static_cast<unsigned>((d_out + rows_per_wg - 1) / rows_per_wg));
-    hipLaunchKernelGGL(gemv_nf4_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint4*>(codes),
+    QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel, grid, dim3(256), 0, st, reinterpret_cast<const uint4*>(codes),
                        qconst, qscale, qmean, static_cast<int>(d_out), static_cast<int>(d_in), x, B, r,
                        ws_t, y, tables());
     return hipGetLastError();

@@ -21,6 +21,19 @@ struct NF4Tables {
 // Returns the process-wide tables (built on first use, thread-safe).
 const NF4Tables& tables();
 
+// Optional kernel timing (see qn_profile_enable): a launch is wrapped as
+//   void* t = prof_begin(st); launch...; prof_end(t, "name", st);
+// Both are no-ops (nullptr token) while timing is off.
+void* prof_begin(hipStream_t st);
+void prof_end(void* token, const char* name, hipStream_t st);
+
+#define QN_LAUNCH(NAME, ST, ...)                         \
+    do {                                                 \
+        void* qn_tok_ = ::qn::prof_begin(ST);            \
+        hipLaunchKernelGGL(__VA_ARGS__);                 \
+        ::qn::prof_end(qn_tok_, NAME, ST);               \
+    } while (0)
+
 // ---- quantize.hip ----
 int quant_grid(int64_t n_b);
 hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,

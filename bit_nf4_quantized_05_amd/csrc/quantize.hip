@@ -331,10 +331,10 @@ hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
                            float* ws_absmax, unsigned long long* ws_limbs, int grid,
                            hipStream_t st) {
     const NF4Tables& tab = tables();
-    hipLaunchKernelGGL(quant_blocks, dim3(grid), dim3(kThreads), 0, st, W, n, n_b,
+    QN_LAUNCH("quant_blocks", st, quant_blocks, dim3(grid), dim3(kThreads), 0, st, W, n, n_b,
                        reinterpret_cast<uint32_t*>(codes), ws_absmax, ws_limbs, tab);
-    hipLaunchKernelGGL(mean_finalize, dim3(1), dim3(kThreads), 0, st, ws_limbs, grid, n_b, qmean);
-    hipLaunchKernelGGL(dq_encode, dim3(static_cast<unsigned>(n_g)), dim3(kThreads), 0, st,
+    QN_LAUNCH("mean_finalize", st, mean_finalize, dim3(1), dim3(kThreads), 0, st, ws_limbs, grid, n_b, qmean);
+    QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(n_g)), dim3(kThreads), 0, st,
                        ws_absmax, n_b, qmean, qconst, qscale);
     return hipGetLastError();
 }
@@ -343,7 +343,7 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const
                                const float* qmean, int64_t n, uint16_t* out, hipStream_t st) {
     const int64_t threads = (n + 7) / 8;
     const int64_t grid = (threads + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(dequant_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st,
+    QN_LAUNCH("dequant_rows", st, dequant_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st,
                        reinterpret_cast<const uint32_t*>(codes), qconst, qscale, qmean, n, out, tables());
     return hipGetLastError();
 }
@@ -352,7 +352,7 @@ hipError_t launch_dequant_transposed(const uint8_t* codes, const int8_t* qconst,
                                      const float* qscale, const float* qmean, int64_t d_out,
                                      int64_t d_in, uint16_t* outT, hipStream_t st) {
     dim3 grid(static_cast<unsigned>(d_in / 64), static_cast<unsigned>((d_out + 63) / 64));
-    hipLaunchKernelGGL(dequant_transposed, grid, dim3(kThreads), 0, st, codes, qconst, qscale,
+    QN_LAUNCH("dequant_transposed", st, dequant_transposed, grid, dim3(kThreads), 0, st, codes, qconst, qscale,
                        qmean, d_out, d_in, outT, tables());
     return hipGetLastError();
 }

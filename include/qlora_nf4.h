@@ -138,6 +138,20 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
                        const uint16_t* dY, int64_t d_seq, uint16_t* dX,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing, off by default. While enabled, the library brackets every kernel
+ * it launches with a pair of HIP events recorded on that kernel's stream, so the
+ * elapsed time of each kernel is measured on the stream it runs on.
+ *   qn_profile_enable(1) clears old records and starts recording; (0) stops and clears.
+ *   qn_profile_read waits for the recorded events and fills, per distinct kernel
+ *   (up to `cap` of them), its name (NUL-terminated, truncated to name_len bytes,
+ *   row i at names + i*name_len), launch count and total milliseconds. Host
+ *   pointers. Returns the number of distinct kernels, or -1 on a bad argument,
+ *   -4 on a HIP error.
+ */
+int qn_profile_enable(int on);
+int qn_profile_read(char* names, int name_len, int64_t* launches, double* total_ms, int cap);
+
 #ifdef __cplusplus
 }
 #endif
