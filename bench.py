@@ -11,7 +11,8 @@ DQ groups of 256, LoRA r = 16, s = 2), inputs already resident in HBM:
 GEMV; quantisation counts 0 flops) / step time, in TFLOP/s.
 
 Also reported: per-kernel average durations (HIP events recorded by the library
-on the kernel's own stream during the timed steps), the MFMA roofline fraction of
+on each kernel's own stream, in a second pass of the same K steps right after the
+timed one, so the event records do not perturb `value`), the MFMA roofline fraction of
 the dominant kernel (the GEMM), the decode path's effective GB/s over 32 layer
 copies (> 256 MB, beyond the Infinity Cache), and the CPU oracle timed on a
 bounded sample of the same workload.
@@ -42,8 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-copies", type=int, default=32)
     ap.add_argument("--decode-iters", type=int, default=256)
-    ap.add_argument("--cpu-tokens", type=int, default=512,
-                    help="tokens of the workload the CPU oracle runs (0 = skip the CPU baseline)")
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the prefill workload the CPU oracle runs (0 = skip the CPU baseline)")
     return ap.parse_args()
 
 
@@ -56,9 +57,10 @@ def decode_bytes(cfg) -> int:
     return n // 2 + n_b + 4 * n_g + 4 + 2 * cfg.r * (cfg.d_in + cfg.d_out) + 2 * cfg.d_in + 2 * cfg.d_out
 
 
-def cpu_baseline(cfg, tokens: int) -> dict:
-    """The oracle, as it stands, on a bounded sample: full quantise + dequantise of
-    W, then forward and input gradient for `tokens` tokens in float64."""
+def cpu_baseline(cfg, dcfg, tokens: int) -> dict:
+    """The oracle, as it stands, on the step's workload (or a token sample of it):
+    full quantise + dequantise of W, forward and input gradient for `tokens`
+    tokens, and the d_seq = 1 forward, in float64 with numpy."""
     import numpy as np
     import workloads as WL
     from oracle import nf4_oracle as O
@@ -71,17 +73,20 @@ def cpu_baseline(cfg, tokens: int) -> dict:
     a, b = WL.make_lora(cfg)
     x = WL.make_x(cfg)[:tokens]
     dy = WL.make_dy(cfg)[:tokens]
+    x1 = WL.make_x(dcfg)
     t0 = time.perf_counter()
     q = O.quantize(w)
     wh = O.double_dequant(q["codes"], q["qconst"], q["qscale"], q["qmean"], cfg.d_out, cfg.d_in)
     O.linear_fwd(wh, a, b, cfg.s, x)
     O.linear_bwd_x(wh, a, b, cfg.s, dy)
+    O.linear_fwd(wh, a, b, dcfg.s, x1)
     dt = time.perf_counter() - t0
-    flops = 2 * (2 * cfg.d_out * cfg.d_in * tokens + 2 * cfg.r * tokens * (cfg.d_in + cfg.d_out))
+    flops = 2 * (2 * cfg.d_out * cfg.d_in * tokens + 2 * cfg.r * tokens * (cfg.d_in + cfg.d_out)) + dcfg.fwd_flops()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": dt,
-            "sample": (f"{cfg.d_out}x{cfg.d_in} layer: full NF4+DQ quantise and bf16 dequantise, then "
-                       f"fwd + dX for {tokens} of the {cfg.d_seq} tokens in float64 (numpy; BLAS threads = cores)")}
+            "seconds": round(dt, 3),
+            "sample": (f"{cfg.d_out}x{cfg.d_in} layer: full NF4+DQ quantise and bf16 dequantise, fwd + dX for "
+                       f"{tokens} of the {cfg.d_seq} tokens and the d_seq=1 forward, float64 numpy "
+                       f"(BLAS threads = cores)")}
 
 
 def main():
@@ -143,21 +148,29 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, library kernel timing on
+    # ---- timed region: K steps
     log(f"[bench] timing {args.steps} steps")
-    qn.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    prof = qn.profile_read()
-    qn.profile_enable(False)
     ms_per_step = elapsed * 1e3 / args.steps
     step_flops = 2 * cfg.fwd_flops() + dcfg.fwd_flops()
     value = step_flops / (elapsed / args.steps) / 1e12
-    kernels = {k: {"launches": n, "avg_us": 1e3 * ms / n} for k, (n, ms) in sorted(prof.items())}
+
+    # ---- the same K steps again with the library's per-kernel HIP events on
+    log(f"[bench] profiled pass of {args.steps} steps")
+    qn.profile_enable(True)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof_elapsed = time.perf_counter() - t0
+    prof = qn.profile_read()
+    qn.profile_enable(False)
+    kernels = {k: {"launches": n, "avg_us": round(1e3 * ms / n, 3)} for k, (n, ms) in sorted(prof.items())}
     log("[bench] kernels:", json.dumps(kernels))
 
     # dominant kernel: the fused GEMM (fwd and dX launches have equal algorithmic flops)
@@ -215,10 +228,11 @@ def main():
         "roofline": roofline,
         "decode": decode,
         "kernels": kernels,
+        "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
     }
     if args.cpu_tokens > 0:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(cfg, dcfg, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -261,19 +261,14 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
     }
     uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);
     uint16_t* t = reinterpret_cast<uint16_t*>(ws + lw.lora);
-    const uint16_t* q2 = B;
-    if (r != lw.r_pad) {
-        uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
-        if ((e = qn::launch_pad_cols(B, d_out, r, bpad, lw.r_pad, st)) != hipSuccess)
-            return hip_fail(e, "qlora_linear_fwd (pad B)");
-        q2 = bpad;
-    }
-    if ((e = qn::launch_dequant_rows(codes, qconst, qscale, qmean, d_out * d_in, what, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_fwd (dequant)");
-    if ((e = qn::launch_lora_prepass(X, d_in, d_seq, d_in, A, d_in, r, s, t, lw.r_pad, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_fwd (A X)");
-    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, q2, lw.r_pad, lw.r_pad, Y, d_out,
-                                d_seq, d_out, st)) != hipSuccess)
+    uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
+    const bool pad = r != lw.r_pad;
+    // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
+    if ((e = qn::launch_prologue(codes, qconst, qscale, qmean, d_out, d_in, false, what, X, d_in, d_seq, d_in,
+                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (prologue)");
+    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
+                                d_out, d_seq, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (gemm)");
     return 0;
 }
@@ -293,14 +288,13 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
     uint16_t* atpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
     uint16_t* bt = reinterpret_cast<uint16_t*>(ws + lw.adapt2);
     hipError_t e;
+    // B^T (the pre-pass needs K-contiguous rows of B^T)
     if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (B^T)");
-    if ((e = qn::launch_transpose_pad(A, r, d_in, atpad, lw.r_pad, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_bwd_x (A^T)");
-    if ((e = qn::launch_dequant_transposed(codes, qconst, qscale, qmean, d_out, d_in, whatT, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_bwd_x (dequant)");
-    if ((e = qn::launch_lora_prepass(dY, d_out, d_seq, d_out, bt, d_out, r, s, u, lw.r_pad, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_bwd_x (B^T dY)");
+    // dequant W_hat^T + U = s (dY B) + A^T padded to r_pad columns, in one launch
+    if ((e = qn::launch_prologue(codes, qconst, qscale, qmean, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
+                                 bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_bwd_x (prologue)");
     if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
                                 d_in, d_seq, d_in, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (gemm)");

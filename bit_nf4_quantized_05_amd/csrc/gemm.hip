@@ -11,14 +11,20 @@
 // so it costs r extra K (1.6 % of the flops at r = 64, K = 4096).
 //
 // gemm_nt: 256x256 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
-// 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (fp32). K-steps of
-// 64 are double-buffered in LDS (2 x 64 KB); rows of 128 B are stored with their
-// eight 16-byte chunks XOR-swizzled by (row & 7) so that the 32-row fragment reads
-// (ds_read_b128) hit every bank once. Tiles are handed to the 8 XCDs in contiguous
-// ranges so each XCD's L2 sees a compact block of P and Q panels.
+// 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (fp32, in AGPRs).
+// K-steps of 32 go through five LDS stages (5 x 32 KB) filled by buffer_load ... lds
+// four steps ahead, so each step's barrier only certifies data that landed long
+// before, and the next step's first fragments are read before the barrier; rows of
+// 64 B are stored with their 16-byte chunks XOR-swizzled by ((row >> 2) & 3), which
+// makes the 32-row fragment reads (ds_read_b128) free of bank conflicts on the
+// 64-bank LDS. Tiles are handed to the 8 XCDs in contiguous ranges so each XCD's L2
+// sees a compact block of P and Q panels.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "nf4_device.h"
+
+#include <algorithm>
 
 namespace qn {
 namespace {
@@ -30,13 +36,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo);
-    const __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
 typedef const __attribute__((address_space(1))) void* global_ptr;
@@ -55,16 +54,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
 // ---------------------------------------------------------------------------
 // Main NT GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 256, BK = 32;
 constexpr int kGT = 256;                       // threads
-constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (2048)
+constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (1024)
 constexpr int kGroupM = 4;                     // tile rows per raster group
 
-// Two LDS stages as two distinct objects, so the compiler can tell that reads of
-// one stage do not depend on the in-flight direct-to-LDS loads into the other.
-// Each holds [P tile | Q tile], 2 x 2048 chunks = 64 KB.
-__shared__ uint4 g_stage0[2 * kChunks];
-__shared__ uint4 g_stage1[2 * kChunks];
+// Five LDS stages (the whole 160 KB) as distinct objects, so the compiler can tell
+// that reads of one stage do not depend on in-flight direct-to-LDS loads into
+// another. Each holds [P tile | Q tile] = 2 x 1024 chunks = 32 KB.
+__shared__ uint4 g_st0[2 * kChunks];
+__shared__ uint4 g_st1[2 * kChunks];
+__shared__ uint4 g_st2[2 * kChunks];
+__shared__ uint4 g_st3[2 * kChunks];
+__shared__ uint4 g_st4[2 * kChunks];
 
 // Scheduling hints: interleave `n` groups of (1 LDS read, 2 MFMA).
 #define QN_INTERLEAVE_DS_MFMA(n)                                  \
@@ -79,42 +81,23 @@ struct GemmArgs {
     const uint16_t* P2; int64_t ldp2;
     const uint16_t* Q2; int64_t ldq2; int kt2;
     uint16_t* C; int64_t ldc; int M, N, tiles_m, tiles_n;
+    uint32_t bytesP, bytesQ, bytesP2, bytesQ2;   // buffer extents for the load descriptors
 };
 
-// Issue the direct-to-LDS loads of K-step kt into `stage` (64 rows per wave, both
-// operands). Offsets are 32-bit per lane on a wave-uniform base pointer.
-__device__ __forceinline__ void gemm_issue(const GemmArgs& g, int kt, uint4* stage, int wave,
-                                           const uint32_t* rowP, const uint32_t* rowQ, uint32_t kc16) {
-    const bool main = kt < g.kt1;
-    const int64_t kb = static_cast<int64_t>(main ? kt : kt - g.kt1) * (BK * 2);
-    const char* bp = reinterpret_cast<const char*>(main ? g.P : g.P2) + kb;
-    const char* bq = reinterpret_cast<const char*>(main ? g.Q : g.Q2) + kb;
-    const uint32_t lp = static_cast<uint32_t>((main ? g.ldp : g.ldp2) * 2);
-    const uint32_t lq = static_cast<uint32_t>((main ? g.ldq : g.ldq2) * 2);
-    uint4* sp = stage + wave * 512;
-    uint4* sq = sp + kChunks;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        load_lds16(bp + (rowP[j] * lp + kc16), sp + 64 * j);
-        load_lds16(bq + (rowQ[j] * lq + kc16), sq + 64 * j);
-    }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
 }
 
-// fragments of k16 sub-step kk: f[0..3] = P (m sub-tiles), f[4..7] = Q (n sub-tiles)
-__device__ __forceinline__ void gemm_frags(const uint4* stage, uint32_t pidx, uint32_t qidx, uint4* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = stage[pidx + i * 256];
-        f[4 + i] = stage[qidx + i * 256];
-    }
-}
-
-__device__ __forceinline__ void gemm_mfmas(f32x16 (&acc)[4][4], const uint4* f) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(f[4 + a], f[b], acc[a][b]);
-}
+// s_waitcnt vmcnt(n) (n < 64; vmcnt is bits [3:0] and [15:14]), other counters untouched
+#define QN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8))
+// Workgroup barrier without the memory fence __syncthreads() adds (which would wait
+// for every in-flight load, including the stages fetched ahead). The loads a barrier
+// certifies are waited for explicitly with QN_WAIT_VM before it; LDS has no cache.
+// The "memory" clobber keeps the compiler from moving memory accesses across it.
+#define QN_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 __global__ __launch_bounds__(kGT, 1)
 void gemm_nt_kernel(GemmArgs g) {
@@ -136,114 +119,202 @@ void gemm_nt_kernel(GemmArgs g) {
     const int tn = (logical % gsize) / gm;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // ---- global -> LDS: direct 16-byte loads into LDS (global_load_lds_dwordx4).
-    // One instruction fills a 1 KB LDS segment = 8 rows x 8 chunks; lane i lands at
-    // chunk i of the segment, i.e. row i/8, stored chunk i%8, so it fetches the
-    // global chunk (i%8) ^ (row & 7) = (i%8) ^ (i/8) of that row (XOR swizzle).
-    // Wave w fills rows 64w .. 64w+63 of both operand tiles.
-    const uint32_t kc16 = static_cast<uint32_t>((lane & 7) ^ (lane >> 3)) * 16u;
-    uint32_t rowP[8], rowQ[8];                  // clamped rows (ragged M / N tiles)
+    // ---- global -> LDS with buffer_load ... lds (16 B per lane).
+    // A tile row is 32 bf16 = 64 B = 4 chunks of 16 B; chunk c of tile row `row` is
+    // stored at position c ^ ((row >> 2) & 3). The LDS has 64 banks of 4 B, so four
+    // consecutive rows cover all banks once, and 16 lanes reading one logical chunk
+    // of 16 consecutive rows hit 16 distinct 4-bank groups. One load fills a 1 KB
+    // segment = 16 rows: lane i lands at row i/4, position i%4, so it fetches chunk
+    // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ (i/16) (rows of a segment start at a
+    // multiple of 16). Wave w fills rows 64w .. 64w+63 of both operand tiles; the
+    // per-lane byte offsets are fixed for the whole K loop, the K position goes in
+    // the scalar offset.
+    const uint32_t kc16 = static_cast<uint32_t>((lane & 3) ^ (lane >> 4)) * 16u;
+    uint32_t voP[4], voQ[4], voP2[4], voQ2[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        rowP[j] = static_cast<uint32_t>(min(m0 + 64 * wave + 8 * j + (lane >> 3), M - 1));
-        rowQ[j] = static_cast<uint32_t>(min(n0 + 64 * wave + 8 * j + (lane >> 3), N - 1));
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t rp = static_cast<uint32_t>(min(m0 + 64 * wave + 16 * j + (lane >> 2), M - 1));
+        const uint32_t rq = static_cast<uint32_t>(min(n0 + 64 * wave + 16 * j + (lane >> 2), N - 1));
+        voP[j] = rp * static_cast<uint32_t>(g.ldp * 2) + kc16;
+        voQ[j] = rq * static_cast<uint32_t>(g.ldq * 2) + kc16;
+        voP2[j] = rp * static_cast<uint32_t>(g.ldp2 * 2) + kc16;
+        voQ2[j] = rq * static_cast<uint32_t>(g.ldq2 * 2) + kc16;
     }
+    const __amdgpu_buffer_rsrc_t rsP = make_rsrc(g.P, g.bytesP);
+    const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(g.Q, g.bytesQ);
+    const __amdgpu_buffer_rsrc_t rsP2 = make_rsrc(g.P2, g.bytesP2);
+    const __amdgpu_buffer_rsrc_t rsQ2 = make_rsrc(g.Q2, g.bytesQ2);
     const int KT = g.kt1 + g.kt2;
 
-    // fragment read indices (in 16-byte chunks) per k16 sub-step
+#define QN_ISSUE(KTV, ST)                                                                         \
+    {                                                                                             \
+        const int kk_ = (KTV);                                                                    \
+        uint4* sp_ = (ST) + wave * 256;                                                           \
+        uint4* sq_ = sp_ + kChunks;                                                               \
+        if (kk_ < g.kt1) {                                                                        \
+            const int so_ = kk_ * (BK * 2);                                                       \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)(sp_ + 64 * j), 16, voP[j], so_, 0, 0); \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(sq_ + 64 * j), 16, voQ[j], so_, 0, 0); \
+            }                                                                                     \
+        } else {                                                                                  \
+            const int so_ = (kk_ - g.kt1) * (BK * 2);                                             \
+            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP2, (lds_ptr_t)(sp_ + 64 * j), 16, voP2[j], so_, 0, 0); \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ2, (lds_ptr_t)(sq_ + 64 * j), 16, voQ2[j], so_, 0, 0); \
+            }                                                                                     \
+        }                                                                                         \
+    }
+
+    // ---- fragments: 16-row x 32-K reads per k16 sub-step kk (0, 1)
     const uint32_t frow = lane & 31;
-    const uint32_t fsw = lane & 7;
-    const uint32_t prow = (wm * 128 + frow) * 8;
-    const uint32_t qrow = kChunks + (wn * 128 + frow) * 8;
-    uint32_t ch[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) ch[kk] = (2 * kk + (lane >> 5)) ^ fsw;
+    const uint32_t fsw = (frow >> 2) & 3;      // (row >> 2) & 3 of this lane's fragment rows
+    const uint32_t prow = (wm * 128 + frow) * 4;
+    const uint32_t qrow = kChunks + (wn * 128 + frow) * 4;
+    const uint32_t ch0 = (0 + (lane >> 5)) ^ fsw;
+    const uint32_t ch1 = (2 + (lane >> 5)) ^ fsw;
+    // f[0..3] = Q fragments (n sub-tiles), f[4..7] = P fragments (m sub-tiles), read in
+    // the order the MFMAs below consume them
+#define QN_FRAGS(ST, CH, F)                                             \
+    {                                                                   \
+        F[0] = (ST)[qrow + (CH)];                                       \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) F[4 + i] = (ST)[prow + i * 128 + (CH)]; \
+        _Pragma("unroll") for (int i = 1; i < 4; ++i) F[i] = (ST)[qrow + i * 128 + (CH)];     \
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+#define QN_MFMAS(F)                                                            \
+    _Pragma("unroll") for (int a = 0; a < 4; ++a)                              \
+        _Pragma("unroll") for (int b = 0; b < 4; ++b)                          \
+            acc[a][b] = mfma32(F[a], F[4 + b], acc[a][b]);
 
     uint4 fa[8], fb[8];
-    gemm_issue(g, 0, g_stage0, wave, rowP, rowQ, kc16);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    gemm_frags(g_stage0, prow + ch[0], qrow + ch[0], fa);
-
-    // One K-step on stage CUR while stage NXT receives step kt+1. Enters with the
-    // kk = 0 fragments of CUR in fa, leaves with the kk = 0 fragments of NXT in fa.
-#define QN_STEP(KTV, CUR, NXT)                                                  \
-    {                                                                           \
-        const int kt_ = (KTV);                                                  \
-        const bool more_ = kt_ + 1 < KT;                                        \
-        if (more_) gemm_issue(g, kt_ + 1, NXT, wave, rowP, rowQ, kc16);         \
-        gemm_frags(CUR, prow + ch[1], qrow + ch[1], fb);                        \
-        gemm_mfmas(acc, fa);                                                    \
-        QN_INTERLEAVE_DS_MFMA(8);                                               \
-        gemm_frags(CUR, prow + ch[2], qrow + ch[2], fa);                        \
-        gemm_mfmas(acc, fb);                                                    \
-        QN_INTERLEAVE_DS_MFMA(8);                                               \
-        gemm_frags(CUR, prow + ch[3], qrow + ch[3], fb);                        \
-        gemm_mfmas(acc, fa);                                                    \
-        QN_INTERLEAVE_DS_MFMA(8);                                               \
-        __builtin_amdgcn_s_waitcnt(0);                                          \
-        __syncthreads();                                                        \
-        if (more_) gemm_frags(NXT, prow + ch[0], qrow + ch[0], fa);             \
-        gemm_mfmas(acc, fb);                                                    \
-        QN_INTERLEAVE_DS_MFMA(8);                                               \
+    // Invariant at the top of step k: stages k and k+1 are complete and certified by
+    // a barrier, the kk = 0 fragments of step k are in fa, the loads of steps k+2 and
+    // k+3 may still be in flight. Stage (k+4)%5 was last read in step k-1, before its
+    // barrier, so step k refills it with step k+4.
+#define QN_STEP(KTV, CUR, NXT, FAR)                                            \
+    {                                                                          \
+        const int k_ = (KTV);                                                  \
+        if (k_ + 4 < KT) QN_ISSUE(k_ + 4, FAR)                                 \
+        QN_FRAGS(CUR, ch1, fb)                                                 \
+        QN_MFMAS(fa)                                                           \
+        QN_INTERLEAVE_DS_MFMA(8);                                              \
+        if (k_ + 1 < KT) QN_FRAGS(NXT, ch0, fa)                                \
+        QN_MFMAS(fb)                                                           \
+        QN_INTERLEAVE_DS_MFMA(8);                                              \
+        if (k_ + 4 < KT) { QN_WAIT_VM(16); } else if (k_ + 3 < KT) { QN_WAIT_VM(8); } else { QN_WAIT_VM(0); } \
+        QN_BARRIER();                                                          \
     }
+
+    QN_ISSUE(0, g_st0)
+    if (KT > 1) QN_ISSUE(1, g_st1)
+    if (KT > 2) QN_ISSUE(2, g_st2)
+    if (KT > 3) QN_ISSUE(3, g_st3)
+    if (KT > 3) { QN_WAIT_VM(16); } else if (KT > 2) { QN_WAIT_VM(8); } else { QN_WAIT_VM(0); }
+    QN_BARRIER();
+    QN_FRAGS(g_st0, ch0, fa)
 
     int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-        QN_STEP(kt, g_stage0, g_stage1)
-        QN_STEP(kt + 1, g_stage1, g_stage0)
+    for (; kt + 5 <= KT; kt += 5) {
+        QN_STEP(kt, g_st0, g_st1, g_st4)
+        QN_STEP(kt + 1, g_st1, g_st2, g_st0)
+        QN_STEP(kt + 2, g_st2, g_st3, g_st1)
+        QN_STEP(kt + 3, g_st3, g_st4, g_st2)
+        QN_STEP(kt + 4, g_st4, g_st0, g_st3)
     }
-    if (kt < KT) QN_STEP(kt, g_stage0, g_stage1)
+    if (kt < KT) QN_STEP(kt, g_st0, g_st1, g_st4)
+    if (kt + 1 < KT) QN_STEP(kt + 1, g_st1, g_st2, g_st0)
+    if (kt + 2 < KT) QN_STEP(kt + 2, g_st2, g_st3, g_st1)
+    if (kt + 3 < KT) QN_STEP(kt + 3, g_st3, g_st4, g_st2)
 #undef QN_STEP
+#undef QN_MFMAS
+#undef QN_FRAGS
+#undef QN_ISSUE
 
-    // ---- epilogue: lane holds C[m][n..n+3] for 4 groups per accumulator
+    // ---- epilogue. Every wave is past the last barrier, so the LDS stages are free
+    // and no load is in flight. The bf16 C tile (256 rows x 512 B) goes to LDS: rows
+    // 64q .. 64q+63 in stage q (q = 0..3), 16-byte chunk j of row r at position
+    // j ^ (r & 31) (two-pass, conflict-free 8-byte writes, conflict-free 16-byte
+    // reads); then each row leaves as 512 contiguous bytes, 16 B per lane.
+    // The lane holds C[m][n..n+3] for m = tile row frow + 32 b + 128 wm and
+    // n = 8 gq + 4 (lane >> 5) + 32 a + 128 wn.
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const int m = m0 + wm * 128 + b * 32 + frow;
-        if (m >= M) continue;
+        const int rl = wm * 128 + b * 32 + static_cast<int>(frow);
+        uint4* arr = (b < 2) ? (wm ? g_st2 : g_st0) : (wm ? g_st3 : g_st1);
+        char* rowp = reinterpret_cast<char*>(arr) + (rl & 63) * 512;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int n = n0 + wn * 128 + a * 32 + 8 * gq + 4 * (lane >> 5);
-                if (n < N) {
-                    uint2 o;
-                    o.x = pack_bf16x2(acc[a][b][4 * gq + 0], acc[a][b][4 * gq + 1]);
-                    o.y = pack_bf16x2(acc[a][b][4 * gq + 2], acc[a][b][4 * gq + 3]);
-                    *reinterpret_cast<uint2*>(g.C + static_cast<int64_t>(m) * g.ldc + n) = o;
-                }
+                const int nl = wn * 128 + a * 32 + 8 * gq + 4 * (lane >> 5);
+                uint2 o;
+                o.x = pack_bf16x2(acc[a][b][4 * gq + 0], acc[a][b][4 * gq + 1]);
+                o.y = pack_bf16x2(acc[a][b][4 * gq + 2], acc[a][b][4 * gq + 3]);
+                *reinterpret_cast<uint2*>(rowp + (((nl >> 3) ^ (rl & 31)) << 4) + ((nl & 7) << 1)) = o;
             }
         }
     }
+    __syncthreads();
+    const int cj = tid & 31;                     // 16-byte chunk of the row
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const int r = i * 8 + (tid >> 5);
+        const uint4* arr = i < 8 ? g_st0 : (i < 16 ? g_st1 : (i < 24 ? g_st2 : g_st3));
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(arr) + (r & 63) * 512 +
+                                                        ((cj ^ (r & 31)) << 4));
+        const int m = m0 + r;
+        const int n = n0 + cj * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(g.C + static_cast<int64_t>(m) * g.ldc + n) = v;
+    }
 }
 
+// ---------------------------------------------------------------------------
+// Prologue of a linear call: one launch whose workgroups take three independent
+// jobs, all memory-bound, so they overlap on the chip:
+//   [0, n_pre)            LoRA pre-pass  OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T),
+//                         32 tokens per workgroup, the 4 waves on K-quarters,
+//                         summed through LDS; columns r..r_pad-1 come out 0.
+//   [n_pre, +n_adapt)     adapter layout: B padded to r_pad columns (forward) or
+//                         A^T padded to r_pad columns (input gradient).
+//   [.., +n_deq)          double dequantisation to bf16: W_hat row-major
+//                         (forward) or W_hat^T through a 64x64 LDS tile (dX).
+// ---------------------------------------------------------------------------
+struct PrologueArgs {
+    const uint8_t* codes; const int8_t* qconst; const float* qscale; const float* qmean;
+    int64_t d_out, d_in;
+    int transposed;                 // dequant to W_hat^T [d_in, d_out] instead of W_hat
+    uint16_t* what;
+    const uint16_t* P; int64_t ldp; int M, K;
+    const uint16_t* R; int64_t ldr; int r; float s;
+    uint16_t* OUT; int r_pad;
+    int adapt_mode;                 // 0 none, 1 pad columns, 2 transpose + pad
+    const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
+    int n_pre, n_adapt, n_deq;
+};
 
-// ---------------------------------------------------------------------------
-// LoRA pre-pass: OUT[M, r_pad] = bf16(s * P[M, K] R[r, K]^T). One workgroup per
-// 32 rows of P; the four waves take quarters of K and are summed through LDS.
-// ---------------------------------------------------------------------------
+constexpr int kDeqIters = 4;                     // 8-weight groups per thread per workgroup
+constexpr int kDeqPerWG = 256 * 8 * kDeqIters;   // weights per row-major dequant workgroup
+constexpr int kTP = 64 + 8;                      // LDS pitch (bf16) of the transpose tile
+
 template <int NT>
-__global__ __launch_bounds__(256)
-void lora_prepass_kernel(const uint16_t* __restrict__ P, int64_t ldp, int M, int K,
-                         const uint16_t* __restrict__ R, int64_t ldr, int r, float s,
-                         uint16_t* __restrict__ OUT, int r_pad) {
-    __shared__ f32x16 red[2][NT][64];
+__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* lds) {
+    f32x16* red = reinterpret_cast<f32x16*>(lds);      // [2][NT][64]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int m0 = blockIdx.x * 32;
-    const int64_t rowm = min(m0 + (lane & 31), M - 1);
-    const int nchunk = K / 64;                 // whole 64-wide K chunks, split over 4 waves
+    const int m0 = b * 32;
+    const int64_t rowm = min(m0 + (lane & 31), a.M - 1);
+    const int nchunk = a.K / 64;                       // whole 64-wide K chunks, split over 4 waves
     const int kbeg = (wave * nchunk / 4) * 64;
     const int kend = ((wave + 1) * nchunk / 4) * 64;
     const int ksub = 8 * (lane >> 5);
-    const uint16_t* prow = P + rowm * ldp + ksub;
+    const uint16_t* prow = a.P + rowm * a.ldp + ksub;
     f32x16 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
@@ -252,8 +323,8 @@ void lora_prepass_kernel(const uint16_t* __restrict__ P, int64_t ldp, int M, int
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int rr = t * 32 + (lane & 31);
-        rok[t] = rr < r;
-        rrow[t] = R + static_cast<int64_t>(rok[t] ? rr : 0) * ldr + ksub;
+        rok[t] = rr < a.r;
+        rrow[t] = a.R + static_cast<int64_t>(rok[t] ? rr : 0) * a.ldr + ksub;
     }
     for (int k = kbeg; k < kend; k += 64) {
         uint4 pf[4];
@@ -272,33 +343,138 @@ void lora_prepass_kernel(const uint16_t* __restrict__ P, int64_t ldp, int M, int
     // sum the four K-quarters: waves 2,3 -> 0,1, then 1 -> 0
     if (wave >= 2)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) red[wave - 2][t][lane] = acc[t];
+        for (int t = 0; t < NT; ++t) red[((wave - 2) * NT + t) * 64 + lane] = acc[t];
     __syncthreads();
     if (wave < 2)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] += red[wave][t][lane];
+        for (int t = 0; t < NT; ++t) acc[t] += red[(wave * NT + t) * 64 + lane];
     __syncthreads();
     if (wave == 1)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) red[0][t][lane] = acc[t];
+        for (int t = 0; t < NT; ++t) red[t * 64 + lane] = acc[t];
     __syncthreads();
     if (wave != 0) return;
     const int m = m0 + (lane & 31);
-    if (m >= M) return;
+    if (m >= a.M) return;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const f32x16 v = acc[t] + red[0][t][lane];
+        const f32x16 v = acc[t] + red[t * 64 + lane];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
-            if (n < r_pad) {
+            if (n < a.r_pad) {
                 uint2 o;
-                o.x = pack_bf16x2(s * v[4 * gq + 0], s * v[4 * gq + 1]);
-                o.y = pack_bf16x2(s * v[4 * gq + 2], s * v[4 * gq + 3]);
-                *reinterpret_cast<uint2*>(OUT + static_cast<int64_t>(m) * r_pad + n) = o;
+                o.x = pack_bf16x2(a.s * v[4 * gq + 0], a.s * v[4 * gq + 1]);
+                o.y = pack_bf16x2(a.s * v[4 * gq + 2], a.s * v[4 * gq + 3]);
+                *reinterpret_cast<uint2*>(a.OUT + static_cast<int64_t>(m) * a.r_pad + n) = o;
             }
         }
     }
+}
+
+// Adapter layouts; destination is [rows, r_pad] (pad) or [acols, r_pad] (transpose).
+__device__ __forceinline__ void adapt_job(const PrologueArgs& a, int b) {
+    const int64_t total = (a.adapt_mode == 1 ? a.arows : a.acols) * a.r_pad;
+    for (int64_t idx = static_cast<int64_t>(b) * 256 + threadIdx.x; idx < total;
+         idx += static_cast<int64_t>(a.n_adapt) * 256) {
+        const int64_t i = idx / a.r_pad, j = idx % a.r_pad;
+        uint16_t v = 0;
+        if (a.adapt_mode == 1) {
+            if (j < a.acols) v = a.asrc[i * a.acols + j];          // B [arows, acols=r] -> [arows, r_pad]
+        } else {
+            if (j < a.arows) v = a.asrc[j * a.acols + i];          // A [arows=r, acols] -> A^T [acols, r_pad]
+        }
+        a.adst[idx] = v;
+    }
+}
+
+__device__ __forceinline__ void dequant_rows_job(const PrologueArgs& a, int b, const float* s_code) {
+    const int64_t n = a.d_out * a.d_in;           // multiple of 64 on this path
+    const float mu = a.qmean[0];
+    const uint32_t* codes32 = reinterpret_cast<const uint32_t*>(a.codes);
+    int64_t t[kDeqIters];
+    uint32_t word[kDeqIters];
+    int8_t q[kDeqIters];
+    float bs[kDeqIters];
+#pragma unroll
+    for (int it = 0; it < kDeqIters; ++it) {
+        t[it] = static_cast<int64_t>(b) * (kDeqPerWG / 8) + it * 256 + threadIdx.x;
+        const bool ok = t[it] * 8 < n;
+        const int64_t blk = ok ? t[it] >> 3 : 0;
+        word[it] = ok ? codes32[t[it]] : 0u;
+        q[it] = a.qconst[blk];
+        bs[it] = a.qscale[blk / kGroup];
+    }
+#pragma unroll
+    for (int it = 0; it < kDeqIters; ++it) {
+        if (t[it] * 8 >= n) break;
+        const float ahat = block_constant(q[it], bs[it], mu);
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = s_code[(word[it] >> (4 * e)) & 0xFu] * ahat;
+        uint4 o;
+        o.x = pack_bf16x2(w[0], w[1]);
+        o.y = pack_bf16x2(w[2], w[3]);
+        o.z = pack_bf16x2(w[4], w[5]);
+        o.w = pack_bf16x2(w[6], w[7]);
+        *reinterpret_cast<uint4*>(a.what + t[it] * 8) = o;
+    }
+}
+
+__device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, int b, const float* s_code,
+                                                       uint16_t* tile) {
+    const int tid = threadIdx.x;
+    const int tiles_i = static_cast<int>(a.d_in / 64);
+    const int64_t i0 = static_cast<int64_t>(b % tiles_i) * 64;
+    const int64_t o0 = static_cast<int64_t>(b / tiles_i) * 64;
+    const int ol = tid >> 2;             // local row o (becomes the output column)
+    const int q4 = tid & 3;              // which 16 of the 64 columns
+    const int64_t o = o0 + ol;
+    if (o < a.d_out) {
+        const int64_t e0 = o * a.d_in + i0 + q4 * 16;
+        const int64_t blk = e0 >> 6;
+        const float ahat = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
+        const uint2 cw = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t word = e < 8 ? cw.x : cw.y;
+            tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
+        }
+    }
+    __syncthreads();
+    const int il = tid >> 2;
+    const int seg = (tid & 3) * 16;
+    const int64_t i = i0 + il;
+    const int64_t oc = o0 + seg;
+    if (oc < a.d_out) {                  // d_out % 64 == 0 on this path: whole 16-wide segments
+        const uint4* src = reinterpret_cast<const uint4*>(&tile[il * kTP + seg]);
+        uint4* dst = reinterpret_cast<uint4*>(a.what + i * a.d_out + oc);
+        dst[0] = src[0];
+        dst[1] = src[1];
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(256)
+void prologue_kernel(PrologueArgs a, NF4Tables tab) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int b = blockIdx.x;
+    if (b < a.n_pre) {
+        prepass_job<NT>(a, b, lds);
+        return;
+    }
+    if (b < a.n_pre + a.n_adapt) {
+        adapt_job(a, b - a.n_pre);
+        return;
+    }
+    float* s_code = reinterpret_cast<float*>(lds);
+    if (threadIdx.x < 16) s_code[threadIdx.x] = tab.code[threadIdx.x];
+    __syncthreads();
+    const int bd = b - a.n_pre - a.n_adapt;
+    if (a.transposed)
+        dequant_transposed_job(a, bd, s_code, reinterpret_cast<uint16_t*>(lds + 64));
+    else
+        dequant_rows_job(a, bd, s_code);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,14 +486,6 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t r
     if (idx >= cols * ld_dst) return;
     const int64_t j = idx / ld_dst, i = idx % ld_dst;
     dst[idx] = i < rows ? src[i * cols + j] : static_cast<uint16_t>(0);
-}
-
-__global__ void pad_cols_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
-                                uint16_t* __restrict__ dst, int64_t ld_dst) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= rows * ld_dst) return;
-    const int64_t i = idx / ld_dst, j = idx % ld_dst;
-    dst[idx] = j < cols ? src[i * cols + j] : static_cast<uint16_t>(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -346,11 +514,29 @@ void lora_ax_kernel(const uint16_t* __restrict__ A, int d_in, const uint16_t* __
     if (threadIdx.x == 0) t[k] = s * (red[0] + red[1] + red[2] + red[3]);
 }
 
-// One wave per row at a time; lane j takes blocks j, j+64, ... of the row. Per block
+// Each wave takes kRowsPerWave consecutive rows; lane j takes blocks j, j+64, ... of
+// every row, so its x blocks are loaded once for all the rows. All code words,
+// constants and scales of the wave's rows are loaded before any arithmetic. Per block
 // the 32 code bytes are looked up as bf16 code pairs and dotted with bf16 x pairs
 // (v_dot2_f32_bf16); the block constant a_hat multiplies the block's partial sum
 // once (a per-block scale factors out of the sum over the block).
 constexpr int kRowsPerWave = 4;
+
+__device__ __forceinline__ float gemv_block(const uint4 c0, const uint4 c1, const uint4* xv, const uint32_t* lut2) {
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float part = 0.0f;
+#pragma unroll
+    for (int w4 = 0; w4 < 8; ++w4) {
+        const uint32_t xw[4] = {xv[w4].x, xv[w4].y, xv[w4].z, xv[w4].w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lut2[byte]),
+                                                   __builtin_bit_cast(bf16x2, xw[b]), part, false);
+        }
+    }
+    return part;
+}
 
 __global__ __launch_bounds__(256)
 void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__ qconst,
@@ -370,36 +556,49 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
     const int wave = tid >> 6;
     const float mu = qmean[0];
     const int nbpr = d_in / 64;
-    const uint32_t* x32 = reinterpret_cast<const uint32_t*>(x);
-    const int rowbase = (blockIdx.x * 4 + wave) * kRowsPerWave;
-    for (int rr = 0; rr < kRowsPerWave; ++rr) {
-        const int o = rowbase + rr;
-        if (o >= d_out) break;
-        float acc = 0.0f;
-        for (int jb = lane; jb < nbpr; jb += 64) {
+    const int row0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
+    if (row0 >= d_out) return;
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    float acc[kRowsPerWave];
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) acc[rr] = 0.0f;
+    for (int jb = lane; jb < nbpr; jb += 64) {
+        uint4 c[kRowsPerWave][2];
+        int8_t q[kRowsPerWave];
+        float bsc[kRowsPerWave];
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerWave; ++rr) {
+            const int o = min(row0 + rr, d_out - 1);
             const int64_t blk = static_cast<int64_t>(o) * nbpr + jb;
-            const uint4 c0 = codes[blk * 2];
-            const uint4 c1 = codes[blk * 2 + 1];
-            const float ahat = mu + qscale[blk >> 8] * qlut[qconst[blk] + 128];
-            const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const uint4* xb = reinterpret_cast<const uint4*>(x32 + static_cast<int64_t>(jb) * 32);
-            float part = 0.0f;
-#pragma unroll
-            for (int w4 = 0; w4 < 8; ++w4) {
-                const uint4 xv = xb[w4];
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
-                    part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lut2[byte]),
-                                                           __builtin_bit_cast(bf16x2, xw[b]), part, false);
-                }
-            }
-            acc += ahat * part;
+            c[rr][0] = codes[blk * 2];
+            c[rr][1] = codes[blk * 2 + 1];
+            q[rr] = qconst[blk];
+            bsc[rr] = qscale[blk >> 8];
         }
-        for (int k = lane; k < r; k += 64) acc += bf16_to_f32(B[static_cast<int64_t>(o) * r + k]) * s_t[k];
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-        if (lane == 0) y[o] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc));
+        uint4 xv[8];
+#pragma unroll
+        for (int w4 = 0; w4 < 8; ++w4) xv[w4] = x4[static_cast<int64_t>(jb) * 8 + w4];
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerWave; ++rr) {
+            const float ahat = mu + bsc[rr] * qlut[q[rr] + 128];
+            acc[rr] += ahat * gemv_block(c[rr][0], c[rr][1], xv, lut2);
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+        const int o = min(row0 + rr, d_out - 1);
+        for (int k = lane; k < r; k += 64) acc[rr] += bf16_to_f32(B[static_cast<int64_t>(o) * r + k]) * s_t[k];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerWave; ++rr) acc[rr] += __shfl_xor(acc[rr], off);
+    if (lane < kRowsPerWave) {
+        float v = acc[0];
+#pragma unroll
+        for (int rr = 1; rr < kRowsPerWave; ++rr)
+            if (lane == rr) v = acc[rr];
+        if (row0 + lane < d_out) y[row0 + lane] = bf16_bits(v);
     }
 }
 
@@ -416,20 +615,43 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.P = P; g.ldp = ldp; g.Q = Q; g.ldq = ldq; g.kt1 = static_cast<int>(K1 / BK);
     g.P2 = P2; g.ldp2 = ldp2; g.Q2 = Q2; g.ldq2 = ldq2; g.kt2 = static_cast<int>(K2 / BK);
     g.C = C; g.ldc = ldc; g.M = static_cast<int>(M); g.N = static_cast<int>(N);
+    // every operand is < 4 GiB (checked by the caller): the extents fit 32 bits
+    g.bytesP = static_cast<uint32_t>(2 * ldp * M);
+    g.bytesQ = static_cast<uint32_t>(2 * ldq * N);
+    g.bytesP2 = static_cast<uint32_t>(2 * ldp2 * M);
+    g.bytesQ2 = static_cast<uint32_t>(2 * ldq2 * N);
     QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(kGT), 0, st, g);
     return hipGetLastError();
 }
 
-hipError_t launch_lora_prepass(const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
-                               const uint16_t* R, int64_t ldr, int r, float s,
-                               uint16_t* OUT, int r_pad, hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>((M + 31) / 32));
-    const int Mi = static_cast<int>(M), Ki = static_cast<int>(K);
-    switch (r_pad / 32) {
-        case 2: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<2>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 4: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<4>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 6: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<6>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
-        case 8: QN_LAUNCH("lora_prepass_kernel", st, lora_prepass_kernel<8>, grid, dim3(256), 0, st, P, ldp, Mi, Ki, R, ldr, r, s, OUT, r_pad); break;
+hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                           const float* qmean, int64_t d_out, int64_t d_in, bool transposed,
+                           uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
+                           const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
+                           int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
+                           int64_t acols, hipStream_t st) {
+    PrologueArgs a;
+    a.codes = codes; a.qconst = qconst; a.qscale = qscale; a.qmean = qmean;
+    a.d_out = d_out; a.d_in = d_in; a.transposed = transposed ? 1 : 0; a.what = what;
+    a.P = P; a.ldp = ldp; a.M = static_cast<int>(M); a.K = static_cast<int>(K);
+    a.R = R; a.ldr = ldr; a.r = r; a.s = s; a.OUT = OUT; a.r_pad = r_pad;
+    a.adapt_mode = adapt_mode; a.asrc = asrc; a.adst = adst; a.arows = arows; a.acols = acols;
+    a.n_pre = static_cast<int>((M + 31) / 32);
+    const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
+    a.n_adapt = static_cast<int>(adapt_elems == 0 ? 0 : std::min<int64_t>(64, (adapt_elems + 255) / 256));
+    const int64_t n = d_out * d_in;
+    a.n_deq = static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64) : (n + kDeqPerWG - 1) / kDeqPerWG);
+    const int NT = r_pad / 32;
+    const size_t lds_pre = static_cast<size_t>(2) * NT * 64 * sizeof(f32x16);
+    const size_t lds_deq = 64 + static_cast<size_t>(64) * kTP * sizeof(uint16_t);
+    const size_t lds = std::max(lds_pre, lds_deq);
+    const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
+    const NF4Tables& tab = tables();
+    switch (NT) {
+        case 2: QN_LAUNCH("prologue_kernel", st, prologue_kernel<2>, grid, dim3(256), lds, st, a, tab); break;
+        case 4: QN_LAUNCH("prologue_kernel", st, prologue_kernel<4>, grid, dim3(256), lds, st, a, tab); break;
+        case 6: QN_LAUNCH("prologue_kernel", st, prologue_kernel<6>, grid, dim3(256), lds, st, a, tab); break;
+        case 8: QN_LAUNCH("prologue_kernel", st, prologue_kernel<8>, grid, dim3(256), lds, st, a, tab); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -439,14 +661,6 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st) {
     const int64_t total = cols * ld_dst;
     QN_LAUNCH("transpose_pad_kernel", st, transpose_pad_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
-                       src, rows, cols, dst, ld_dst);
-    return hipGetLastError();
-}
-
-hipError_t launch_pad_cols(const uint16_t* src, int64_t rows, int64_t cols,
-                           uint16_t* dst, int64_t ld_dst, hipStream_t st) {
-    const int64_t total = rows * ld_dst;
-    QN_LAUNCH("pad_cols_kernel", st, pad_cols_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
                        src, rows, cols, dst, ld_dst);
     return hipGetLastError();
 }

@@ -42,9 +42,6 @@ hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
                            hipStream_t st);
 hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                                const float* qmean, int64_t n, uint16_t* out, hipStream_t st);
-hipError_t launch_dequant_transposed(const uint8_t* codes, const int8_t* qconst,
-                                     const float* qscale, const float* qmean, int64_t d_out,
-                                     int64_t d_in, uint16_t* outT, hipStream_t st);
 
 // ---- gemm.hip ----
 // C[M,N] = bf16( P[M,K1] Q[N,K1]^T + P2[M,K2] Q2[N,K2]^T ), all row-major, K contiguous.
@@ -53,16 +50,20 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
                           int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
                           hipStream_t st);
-// OUT[M, r_pad] = bf16( s * P[M,K] R[r,K]^T ), zero in columns r..r_pad-1; K % 64 == 0.
-hipError_t launch_lora_prepass(const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
-                               const uint16_t* R, int64_t ldr, int r, float s,
-                               uint16_t* OUT, int r_pad, hipStream_t st);
+// One launch before the GEMM of a linear call: LoRA pre-pass
+//   OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T) (zero in columns r..r_pad-1, K % 64 == 0),
+// an adapter layout job (adapt_mode 1: B [arows, acols] -> [arows, r_pad] zero-padded;
+// 2: A [arows, acols] -> A^T [acols, r_pad] zero-padded; 0: none), and the double
+// dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed).
+hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                           const float* qmean, int64_t d_out, int64_t d_in, bool transposed,
+                           uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
+                           const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
+                           int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
+                           int64_t acols, hipStream_t st);
 // dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);
-// dst[i, j] = j < cols ? src[i, j] : 0, for i < rows, j < ld_dst.
-hipError_t launch_pad_cols(const uint16_t* src, int64_t rows, int64_t cols,
-                           uint16_t* dst, int64_t ld_dst, hipStream_t st);
 // y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes.
 hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                            const float* qmean, int64_t d_out, int64_t d_in,

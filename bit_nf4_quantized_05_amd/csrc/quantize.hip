@@ -19,11 +19,12 @@
 //   mean_finalize  - one workgroup: adds the per-workgroup limb sums, divides by n_b
 //                    with integer long division and rounds once to float32 -> mu.
 //   dq_encode      - one workgroup per group of 256 constants: centre, absmax, INT8.
-//   dequant_rows / dequant_transposed - double dequantisation to bf16, row-major or
-//                    transposed through an LDS tile (for the input-gradient GEMM).
+//   dequant_rows   - double dequantisation to bf16 (the standalone entry point; the
+//                    linear calls dequantise inside their prologue launch).
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "nf4_device.h"
 
 namespace qn {
 namespace {
@@ -115,74 +116,90 @@ void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
 
 // ---------------------------------------------------------------------------
 // mu = RoundNearestEven_f32( (sum_j a_j) / n_b ), exact.
-// The sum is an integer S in units of 2^-149 held as 32-bit limbs.
+// The sum is an integer S in units of 2^-149 held as 32-bit limbs. Each thread
+// adds whole per-workgroup records (10 limbs), the 256 threads are reduced in LDS,
+// then one thread carries, divides by n_b and rounds. Every limb array below is
+// indexed by compile-time constants only (fully unrolled), so it stays in registers.
 // ---------------------------------------------------------------------------
-__device__ inline bool bit_of(const uint32_t* q, int k) { return (q[k >> 5] >> (k & 31)) & 1u; }
-
-__device__ inline bool any_below(const uint32_t* q, int k) {   // any of bits [0, k)
-    for (int w = 0; w < (k >> 5); ++w)
-        if (q[w]) return true;
-    const int r = k & 31;
-    return r ? (q[k >> 5] & ((1u << r) - 1u)) != 0u : false;
-}
-
 __global__ __launch_bounds__(kThreads)
 void mean_finalize(const unsigned long long* __restrict__ limb_part, int parts, int64_t n_b,
                    float* __restrict__ qmean) {
-    __shared__ unsigned long long s_sum[kThreads];
+    __shared__ unsigned long long s_sum[kLimbs][kThreads];
     const int tid = threadIdx.x;
-    constexpr int kSlices = kThreads / kLimbs;   // 25
-    unsigned long long acc = 0ull;
-    if (tid < kSlices * kLimbs) {
-        const int limb = tid % kLimbs;
-        for (int g = tid / kLimbs; g < parts; g += kSlices) acc += limb_part[static_cast<int64_t>(g) * kLimbs + limb];
+    unsigned long long acc[kLimbs];
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) acc[L] = 0ull;
+    for (int g = tid; g < parts; g += kThreads) {
+        const unsigned long long* rec = limb_part + static_cast<int64_t>(g) * kLimbs;
+#pragma unroll
+        for (int L = 0; L < kLimbs; ++L) acc[L] += rec[L];
     }
-    s_sum[tid] = acc;
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) s_sum[L][tid] = acc[L];
     __syncthreads();
+    for (int h = kThreads / 2; h >= 1; h >>= 1) {
+        if (tid < h) {
+#pragma unroll
+            for (int L = 0; L < kLimbs; ++L) s_sum[L][tid] += s_sum[L][tid + h];
+        }
+        __syncthreads();
+    }
     if (tid != 0) return;
 
-    // normalise to 32-bit limbs (the total of each limb column is < n_b * 2^32 < 2^64)
+    // carry-normalise to 32-bit limbs (each column total is < n_b * 2^32 < 2^64)
     constexpr int kQ = kLimbs + 1;
     uint32_t N[kQ];
     unsigned long long carry = 0ull;
+#pragma unroll
     for (int L = 0; L < kLimbs; ++L) {
-        unsigned long long col = 0ull;
-        for (int sl = 0; sl < kSlices; ++sl) col += s_sum[sl * kLimbs + L];
+        const unsigned long long col = s_sum[L][0];
         const unsigned long long low = (col & 0xFFFFFFFFull) + (carry & 0xFFFFFFFFull);
         N[L] = static_cast<uint32_t>(low);
         carry = (col >> 32) + (carry >> 32) + (low >> 32);
     }
     N[kLimbs] = static_cast<uint32_t>(carry);
 
-    // long division by n_b (< 2^32)
+    // Q = floor(S / n_b), rem = S mod n_b (n_b < 2^32)
     const unsigned long long d = static_cast<unsigned long long>(n_b);
     uint32_t Q[kQ];
     unsigned long long rem = 0ull;
+#pragma unroll
     for (int L = kQ - 1; L >= 0; --L) {
         const unsigned long long cur = (rem << 32) | N[L];
         Q[L] = static_cast<uint32_t>(cur / d);
         rem = cur % d;
     }
-    int len = 0;   // bit length of Q
-    for (int L = kQ - 1; L >= 0; --L)
-        if (Q[L]) { len = 32 * L + (32 - __clz(Q[L])); break; }
-
+    // 96-bit window of Q holding its top limb, and whether anything lies below it
+    int top = -1;
+#pragma unroll
+    for (int L = 0; L < kQ; ++L)
+        if (Q[L]) top = L;
+    uint32_t w2 = 0, w1 = 0, w0 = 0;
+    bool below = false;
+#pragma unroll
+    for (int L = 0; L < kQ; ++L) {
+        if (L == top) w2 = Q[L];
+        else if (L == top - 1) w1 = Q[L];
+        else if (L == top - 2) w0 = Q[L];
+        else if (L < top - 2 && Q[L] != 0u) below = true;
+    }
     uint32_t bits;
+    const int len = top < 0 ? 0 : 32 * top + (32 - __clz(w2));   // bit length of Q
     if (len >= 24) {
-        int shift = len - 24;
-        uint32_t mant = 0;
-        for (int k = 0; k < 24; ++k) mant |= static_cast<uint32_t>(bit_of(Q, shift + k)) << k;
-        bool up;
-        if (shift == 0) {
-            up = (2ull * rem > d) || (2ull * rem == d && (mant & 1u));
-        } else {
-            const bool guard = bit_of(Q, shift - 1);
-            const bool sticky = any_below(Q, shift - 1) || rem != 0ull;
-            up = guard && (sticky || (mant & 1u));
+        // left-align the window: bit (len-1) of Q moves to bit 95
+        const int lz = __clz(w2);
+        const unsigned long long hi = ((static_cast<unsigned long long>(w2) << 32) | w1) << lz |
+                                      (lz ? (static_cast<unsigned long long>(w0) >> (32 - lz)) : 0ull);
+        const uint32_t lo32 = lz ? (w0 << lz) : w0;   // remaining low bits of the window
+        uint32_t mant = static_cast<uint32_t>(hi >> 40);               // top 24 bits
+        const bool guard = (hi >> 39) & 1ull;
+        const bool sticky = (hi & ((1ull << 39) - 1ull)) != 0ull || lo32 != 0u || below || rem != 0ull;
+        int shift = len - 24;                                            // value = mant * 2^(shift-149)
+        if (guard && (sticky || (mant & 1u))) {
+            if (++mant == (1u << 24)) { mant >>= 1; ++shift; }
         }
-        if (up && ++mant == (1u << 24)) { mant >>= 1; ++shift; }
         bits = (static_cast<uint32_t>(shift + 1) << 23) | (mant & 0x7FFFFFu);
-    } else {   // below 2^-126: fixed 2^-149 grid
+    } else {   // below 2^-126: fixed 2^-149 grid, Q fits in one limb
         uint32_t mant = Q[0];
         if ((2ull * rem > d) || (2ull * rem == d && (mant & 1u))) ++mant;
         bits = mant;
@@ -222,20 +239,6 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const float* __res
     if (tid == 0) qscale[blockIdx.x] = b;
 }
 
-// a_hat = mu + b * (q / 127): separate float32 division, multiply and add.
-__device__ __forceinline__ float block_constant(int8_t q, float b, float mu) {
-    const float rhat = static_cast<float>(q) / static_cast<float>(kInt8Step);
-    const float prod = b * rhat;
-    return mu + prod;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo);    // round to nearest even (v_cvt_pk_bf16_f32)
-    const __bf16 b = static_cast<__bf16>(hi);
-    return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-
 // ---------------------------------------------------------------------------
 // Dequantisation, row-major: one thread per 8 consecutive weights.
 // ---------------------------------------------------------------------------
@@ -268,56 +271,6 @@ void dequant_rows(const uint32_t* __restrict__ codes32, const int8_t* __restrict
     }
 }
 
-// ---------------------------------------------------------------------------
-// Transposed dequantisation: W_hat^T [d_in, d_out] through a 64x64 LDS tile.
-// d_in % 64 == 0, so each tile row is exactly one block.
-// ---------------------------------------------------------------------------
-constexpr int kTP = 64 + 8;   // LDS pitch in bf16 (keeps 16-byte rows aligned)
-
-__global__ __launch_bounds__(kThreads)
-void dequant_transposed(const uint8_t* __restrict__ codes, const int8_t* __restrict__ qconst,
-                        const float* __restrict__ qscale, const float* __restrict__ qmean,
-                        int64_t d_out, int64_t d_in, uint16_t* __restrict__ outT, NF4Tables tab) {
-    __shared__ float s_code[16];
-    __shared__ uint16_t tile[64 * kTP];
-    const int tid = threadIdx.x;
-    if (tid < 16) s_code[tid] = tab.code[tid];
-    __syncthreads();
-    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int64_t o0 = static_cast<int64_t>(blockIdx.y) * 64;
-    const int ol = tid >> 2;             // local row (output column of W_hat^T)
-    const int q4 = tid & 3;              // which 16 of the 64 columns
-    const int64_t o = o0 + ol;
-    if (o < d_out) {
-        const int64_t e0 = o * d_in + i0 + q4 * 16;
-        const int64_t blk = e0 >> 6;
-        const float ahat = block_constant(qconst[blk], qscale[blk / kGroup], qmean[0]);
-        const uint2 cw = *reinterpret_cast<const uint2*>(codes + (e0 >> 1));
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t word = e < 8 ? cw.x : cw.y;
-            const float w = s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat;
-            tile[(q4 * 16 + e) * kTP + ol] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(w));
-        }
-    }
-    __syncthreads();
-    // row il of the output tile = 64 consecutive o values
-    const int il = tid >> 2;
-    const int seg = (tid & 3) * 16;
-    const int64_t i = i0 + il;
-    const int64_t oc = o0 + seg;
-    if (oc < d_out) {
-        const uint4* src = reinterpret_cast<const uint4*>(&tile[il * kTP + seg]);
-        uint4* dst = reinterpret_cast<uint4*>(outT + i * d_out + oc);
-        if (oc + 16 <= d_out) {
-            dst[0] = src[0];
-            dst[1] = src[1];
-        } else {
-            for (int e = 0; e < 16 && oc + e < d_out; ++e) outT[i * d_out + oc + e] = tile[il * kTP + seg + e];
-        }
-    }
-}
-
 }  // namespace
 
 int quant_grid(int64_t n_b) {
@@ -345,15 +298,6 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const
     const int64_t grid = (threads + kThreads - 1) / kThreads;
     QN_LAUNCH("dequant_rows", st, dequant_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st,
                        reinterpret_cast<const uint32_t*>(codes), qconst, qscale, qmean, n, out, tables());
-    return hipGetLastError();
-}
-
-hipError_t launch_dequant_transposed(const uint8_t* codes, const int8_t* qconst,
-                                     const float* qscale, const float* qmean, int64_t d_out,
-                                     int64_t d_in, uint16_t* outT, hipStream_t st) {
-    dim3 grid(static_cast<unsigned>(d_in / 64), static_cast<unsigned>((d_out + 63) / 64));
-    QN_LAUNCH("dequant_transposed", st, dequant_transposed, grid, dim3(kThreads), 0, st, codes, qconst, qscale,
-                       qmean, d_out, d_in, outT, tables());
     return hipGetLastError();
 }
 
