@@ -55,7 +55,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
 // Main NT GEMM
 // ---------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int kGT = 256;                       // threads
 constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (1024)
 constexpr int kGroupM = 4;                     // tile rows per raster group
 
@@ -99,12 +98,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // The "memory" clobber keeps the compiler from moving memory accesses across it.
 #define QN_BARRIER() asm volatile("s_barrier" ::: "memory")
 
-__global__ __launch_bounds__(kGT, 1)
-void gemm_nt_kernel(GemmArgs g) {
+// WM x WN waves; each wave owns a (256/WM) x (256/WN) sub-tile of 32x32 MFMA tiles.
+template <int WM, int WN>
+__device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
+    constexpr int NW = WM * WN;                 // waves
+    constexpr int NT = 64 * NW;                 // threads
+    constexpr int TM = BM / WM / 32;            // m sub-tiles per wave
+    constexpr int TN = BN / WN / 32;            // n sub-tiles per wave
+    constexpr int SEG = BM / NW / 16;           // 16-row load segments per wave and operand
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int M = g.M, N = g.N;
 
     // ---- tile assignment: contiguous logical ranges per XCD, grouped raster
@@ -125,16 +130,16 @@ void gemm_nt_kernel(GemmArgs g) {
     // consecutive rows cover all banks once, and 16 lanes reading one logical chunk
     // of 16 consecutive rows hit 16 distinct 4-bank groups. One load fills a 1 KB
     // segment = 16 rows: lane i lands at row i/4, position i%4, so it fetches chunk
-    // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ (i/16) (rows of a segment start at a
-    // multiple of 16). Wave w fills rows 64w .. 64w+63 of both operand tiles; the
-    // per-lane byte offsets are fixed for the whole K loop, the K position goes in
-    // the scalar offset.
+    // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ (i/16) (segments start at multiples of 16
+    // rows). Wave w fills rows 16*SEG*w .. of both operand tiles; the per-lane byte
+    // offsets are fixed for the whole K loop, the K position goes in the scalar offset.
     const uint32_t kc16 = static_cast<uint32_t>((lane & 3) ^ (lane >> 4)) * 16u;
-    uint32_t voP[4], voQ[4], voP2[4], voQ2[4];
+    uint32_t voP[SEG], voQ[SEG], voP2[SEG], voQ2[SEG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t rp = static_cast<uint32_t>(min(m0 + 64 * wave + 16 * j + (lane >> 2), M - 1));
-        const uint32_t rq = static_cast<uint32_t>(min(n0 + 64 * wave + 16 * j + (lane >> 2), N - 1));
+    for (int j = 0; j < SEG; ++j) {
+        const int rr = 16 * SEG * wave + 16 * j + (lane >> 2);
+        const uint32_t rp = static_cast<uint32_t>(min(m0 + rr, M - 1));
+        const uint32_t rq = static_cast<uint32_t>(min(n0 + rr, N - 1));
         voP[j] = rp * static_cast<uint32_t>(g.ldp * 2) + kc16;
         voQ[j] = rq * static_cast<uint32_t>(g.ldq * 2) + kc16;
         voP2[j] = rp * static_cast<uint32_t>(g.ldp2 * 2) + kc16;
@@ -145,54 +150,55 @@ void gemm_nt_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t rsP2 = make_rsrc(g.P2, g.bytesP2);
     const __amdgpu_buffer_rsrc_t rsQ2 = make_rsrc(g.Q2, g.bytesQ2);
     const int KT = g.kt1 + g.kt2;
+    constexpr int kLoadsPerStep = 2 * SEG;      // per wave
 
 #define QN_ISSUE(KTV, ST)                                                                         \
     {                                                                                             \
         const int kk_ = (KTV);                                                                    \
-        uint4* sp_ = (ST) + wave * 256;                                                           \
+        uint4* sp_ = (ST) + wave * (64 * SEG);                                                    \
         uint4* sq_ = sp_ + kChunks;                                                               \
         if (kk_ < g.kt1) {                                                                        \
             const int so_ = kk_ * (BK * 2);                                                       \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+            _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)(sp_ + 64 * j), 16, voP[j], so_, 0, 0); \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(sq_ + 64 * j), 16, voQ[j], so_, 0, 0); \
             }                                                                                     \
         } else {                                                                                  \
             const int so_ = (kk_ - g.kt1) * (BK * 2);                                             \
-            _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+            _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP2, (lds_ptr_t)(sp_ + 64 * j), 16, voP2[j], so_, 0, 0); \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ2, (lds_ptr_t)(sq_ + 64 * j), 16, voQ2[j], so_, 0, 0); \
             }                                                                                     \
         }                                                                                         \
     }
 
-    // ---- fragments: 16-row x 32-K reads per k16 sub-step kk (0, 1)
+    // ---- fragments: 32-row x 16-K reads per k16 sub-step kk (0, 1)
     const uint32_t frow = lane & 31;
     const uint32_t fsw = (frow >> 2) & 3;      // (row >> 2) & 3 of this lane's fragment rows
-    const uint32_t prow = (wm * 128 + frow) * 4;
-    const uint32_t qrow = kChunks + (wn * 128 + frow) * 4;
+    const uint32_t prow = (wm * (TM * 32) + frow) * 4;
+    const uint32_t qrow = kChunks + (wn * (TN * 32) + frow) * 4;
     const uint32_t ch0 = (0 + (lane >> 5)) ^ fsw;
     const uint32_t ch1 = (2 + (lane >> 5)) ^ fsw;
-    // f[0..3] = Q fragments (n sub-tiles), f[4..7] = P fragments (m sub-tiles), read in
-    // the order the MFMAs below consume them
+    // F[0..TN) = Q fragments (n sub-tiles), F[TN..TN+TM) = P fragments (m sub-tiles),
+    // read in the order the MFMAs below consume them
 #define QN_FRAGS(ST, CH, F)                                             \
     {                                                                   \
         F[0] = (ST)[qrow + (CH)];                                       \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) F[4 + i] = (ST)[prow + i * 128 + (CH)]; \
-        _Pragma("unroll") for (int i = 1; i < 4; ++i) F[i] = (ST)[qrow + i * 128 + (CH)];     \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) F[TN + i] = (ST)[prow + i * 128 + (CH)]; \
+        _Pragma("unroll") for (int i = 1; i < TN; ++i) F[i] = (ST)[qrow + i * 128 + (CH)];      \
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[TN][TM];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < TN; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
 #define QN_MFMAS(F)                                                            \
-    _Pragma("unroll") for (int a = 0; a < 4; ++a)                              \
-        _Pragma("unroll") for (int b = 0; b < 4; ++b)                          \
-            acc[a][b] = mfma32(F[a], F[4 + b], acc[a][b]);
+    _Pragma("unroll") for (int a = 0; a < TN; ++a)                             \
+        _Pragma("unroll") for (int b = 0; b < TM; ++b)                         \
+            acc[a][b] = mfma32(F[a], F[TN + b], acc[a][b]);
 
-    uint4 fa[8], fb[8];
+    uint4 fa[TM + TN], fb[TM + TN];
     // Invariant at the top of step k: stages k and k+1 are complete and certified by
     // a barrier, the kk = 0 fragments of step k are in fa, the loads of steps k+2 and
     // k+3 may still be in flight. Stage (k+4)%5 was last read in step k-1, before its
@@ -203,11 +209,13 @@ void gemm_nt_kernel(GemmArgs g) {
         if (k_ + 4 < KT) QN_ISSUE(k_ + 4, FAR)                                 \
         QN_FRAGS(CUR, ch1, fb)                                                 \
         QN_MFMAS(fa)                                                           \
-        QN_INTERLEAVE_DS_MFMA(8);                                              \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
         if (k_ + 1 < KT) QN_FRAGS(NXT, ch0, fa)                                \
         QN_MFMAS(fb)                                                           \
-        QN_INTERLEAVE_DS_MFMA(8);                                              \
-        if (k_ + 4 < KT) { QN_WAIT_VM(16); } else if (k_ + 3 < KT) { QN_WAIT_VM(8); } else { QN_WAIT_VM(0); } \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+        if (k_ + 4 < KT) { QN_WAIT_VM(2 * kLoadsPerStep); }                    \
+        else if (k_ + 3 < KT) { QN_WAIT_VM(kLoadsPerStep); }                   \
+        else { QN_WAIT_VM(0); }                                                \
         QN_BARRIER();                                                          \
     }
 
@@ -215,7 +223,7 @@ void gemm_nt_kernel(GemmArgs g) {
     if (KT > 1) QN_ISSUE(1, g_st1)
     if (KT > 2) QN_ISSUE(2, g_st2)
     if (KT > 3) QN_ISSUE(3, g_st3)
-    if (KT > 3) { QN_WAIT_VM(16); } else if (KT > 2) { QN_WAIT_VM(8); } else { QN_WAIT_VM(0); }
+    if (KT > 3) { QN_WAIT_VM(2 * kLoadsPerStep); } else if (KT > 2) { QN_WAIT_VM(kLoadsPerStep); } else { QN_WAIT_VM(0); }
     QN_BARRIER();
     QN_FRAGS(g_st0, ch0, fa)
 
@@ -241,18 +249,19 @@ void gemm_nt_kernel(GemmArgs g) {
     // 64q .. 64q+63 in stage q (q = 0..3), 16-byte chunk j of row r at position
     // j ^ (r & 31) (two-pass, conflict-free 8-byte writes, conflict-free 16-byte
     // reads); then each row leaves as 512 contiguous bytes, 16 B per lane.
-    // The lane holds C[m][n..n+3] for m = tile row frow + 32 b + 128 wm and
-    // n = 8 gq + 4 (lane >> 5) + 32 a + 128 wn.
+    // The lane holds C[m][n..n+3] for m = tile row frow + 32 b + 32 TM wm and
+    // n = 8 gq + 4 (lane >> 5) + 32 a + 32 TN wn.
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int rl = wm * 128 + b * 32 + static_cast<int>(frow);
-        uint4* arr = (b < 2) ? (wm ? g_st2 : g_st0) : (wm ? g_st3 : g_st1);
+    for (int b = 0; b < TM; ++b) {
+        const int rl = wm * (TM * 32) + b * 32 + static_cast<int>(frow);
+        const int q = rl >> 6;
+        uint4* arr = q == 0 ? g_st0 : (q == 1 ? g_st1 : (q == 2 ? g_st2 : g_st3));
         char* rowp = reinterpret_cast<char*>(arr) + (rl & 63) * 512;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int nl = wn * 128 + a * 32 + 8 * gq + 4 * (lane >> 5);
+                const int nl = wn * (TN * 32) + a * 32 + 8 * gq + 4 * (lane >> 5);
                 uint2 o;
                 o.x = pack_bf16x2(acc[a][b][4 * gq + 0], acc[a][b][4 * gq + 1]);
                 o.y = pack_bf16x2(acc[a][b][4 * gq + 2], acc[a][b][4 * gq + 3]);
@@ -262,16 +271,28 @@ void gemm_nt_kernel(GemmArgs g) {
     }
     __syncthreads();
     const int cj = tid & 31;                     // 16-byte chunk of the row
+    constexpr int kRowsPerPass = NT / 32;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const int r = i * 8 + (tid >> 5);
-        const uint4* arr = i < 8 ? g_st0 : (i < 16 ? g_st1 : (i < 24 ? g_st2 : g_st3));
+    for (int i = 0; i < BM / kRowsPerPass; ++i) {
+        const int r = i * kRowsPerPass + (tid >> 5);
+        const int q = r >> 6;
+        const uint4* arr = q == 0 ? g_st0 : (q == 1 ? g_st1 : (q == 2 ? g_st2 : g_st3));
         const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(arr) + (r & 63) * 512 +
                                                         ((cj ^ (r & 31)) << 4));
         const int m = m0 + r;
         const int n = n0 + cj * 8;
         if (m < M && n < N) *reinterpret_cast<uint4*>(g.C + static_cast<int64_t>(m) * g.ldc + n) = v;
     }
+}
+
+#ifndef QN_GEMM_WAVES_N
+#define QN_GEMM_WAVES_N 4
+#endif
+constexpr int kGemmWM = 2, kGemmWN = QN_GEMM_WAVES_N;
+
+__global__ __launch_bounds__(64 * kGemmWM * kGemmWN, 1)
+void gemm_nt_kernel(GemmArgs g) {
+    gemm_nt_body<kGemmWM, kGemmWN>(g);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,7 +641,8 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.bytesQ = static_cast<uint32_t>(2 * ldq * N);
     g.bytesP2 = static_cast<uint32_t>(2 * ldp2 * M);
     g.bytesQ2 = static_cast<uint32_t>(2 * ldq2 * N);
-    QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(kGT), 0, st, g);
+    QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(64 * kGemmWM * kGemmWN), 0,
+              st, g);
     return hipGetLastError();
 }
 
