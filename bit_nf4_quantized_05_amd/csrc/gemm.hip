@@ -10,15 +10,17 @@
 //     dX      : P = dY, Q = W_hat^T,  P2 = s (dY B),    Q2 = A^T
 // so it costs r extra K (1.6 % of the flops at r = 64, K = 4096).
 //
-// gemm_nt: 256x256 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
-// 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 accumulators (fp32, in AGPRs).
-// K-steps of 32 go through five LDS stages (5 x 32 KB) filled by buffer_load ... lds
-// four steps ahead, so each step's barrier only certifies data that landed long
-// before, and the next step's first fragments are read before the barrier; rows of
-// 64 B are stored with their 16-byte chunks XOR-swizzled by ((row >> 2) & 3), which
-// makes the 32-row fragment reads (ds_read_b128) free of bank conflicts on the
-// 64-bank LDS. Tiles are handed to the 8 XCDs in contiguous ranges so each XCD's L2
-// sees a compact block of P and Q panels.
+// gemm_nt: 256x256 output tile per workgroup, 8 waves (two per SIMD, so one wave's
+// MFMAs cover the other's waits) in a 2x4 grid, each wave a 128x64 sub-tile of 4x2
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32). K-steps of 64 are double-buffered
+// in LDS (2 x 64 KB) and filled by buffer_load ... lds (direct to LDS, no staging
+// registers): a tile row is then 128 B, one whole cache line per row and load, which
+// halves the L2 requests per byte compared with 64-byte rows. Rows are stored with
+// their 16-byte chunks XOR-swizzled by ((row >> 1) & 7), which makes the 32-row
+// fragment reads (ds_read_b128) free of bank conflicts on the 64-bank LDS. The stage
+// barrier sits before the last k16 sub-step, so the next stage's first fragments are
+// read under the last MFMAs. Tiles are handed to the 8 XCDs in contiguous ranges so
+// each XCD's L2 sees a compact block of P and Q panels.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -54,18 +56,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
 // ---------------------------------------------------------------------------
 // Main NT GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (1024)
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (2048)
 constexpr int kGroupM = 4;                     // tile rows per raster group
 
-// Five LDS stages (the whole 160 KB) as distinct objects, so the compiler can tell
-// that reads of one stage do not depend on in-flight direct-to-LDS loads into
-// another. Each holds [P tile | Q tile] = 2 x 1024 chunks = 32 KB.
+// Two LDS stages as distinct objects, so the compiler can tell that reads of one
+// stage do not depend on in-flight direct-to-LDS loads into the other. Each holds
+// [P tile | Q tile] = 2 x 2048 chunks = 64 KB.
 __shared__ uint4 g_st0[2 * kChunks];
 __shared__ uint4 g_st1[2 * kChunks];
-__shared__ uint4 g_st2[2 * kChunks];
-__shared__ uint4 g_st3[2 * kChunks];
-__shared__ uint4 g_st4[2 * kChunks];
 
 // Scheduling hints: interleave `n` groups of (1 LDS read, 2 MFMA).
 #define QN_INTERLEAVE_DS_MFMA(n)                                  \
@@ -105,7 +104,7 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     constexpr int NT = 64 * NW;                 // threads
     constexpr int TM = BM / WM / 32;            // m sub-tiles per wave
     constexpr int TN = BN / WN / 32;            // n sub-tiles per wave
-    constexpr int SEG = BM / NW / 16;           // 16-row load segments per wave and operand
+    constexpr int SEG = BM / NW / 8;            // 8-row load segments per wave and operand
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -124,20 +123,23 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     const int tn = (logical % gsize) / gm;
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // ---- global -> LDS with buffer_load ... lds (16 B per lane).
-    // A tile row is 32 bf16 = 64 B = 4 chunks of 16 B; chunk c of tile row `row` is
-    // stored at position c ^ ((row >> 2) & 3). The LDS has 64 banks of 4 B, so four
-    // consecutive rows cover all banks once, and 16 lanes reading one logical chunk
-    // of 16 consecutive rows hit 16 distinct 4-bank groups. One load fills a 1 KB
-    // segment = 16 rows: lane i lands at row i/4, position i%4, so it fetches chunk
-    // (i%4) ^ ((row >> 2) & 3) = (i%4) ^ (i/16) (segments start at multiples of 16
-    // rows). Wave w fills rows 16*SEG*w .. of both operand tiles; the per-lane byte
-    // offsets are fixed for the whole K loop, the K position goes in the scalar offset.
-    const uint32_t kc16 = static_cast<uint32_t>((lane & 3) ^ (lane >> 4)) * 16u;
+    // ---- global -> LDS with buffer_load ... lds (16 B per lane). A tile row is 64
+    // bf16 = 128 B = 8 chunks; chunk c of tile row r is stored at c ^ ((r >> 1) & 7).
+    // The LDS has 64 banks of 4 B, so two consecutive rows cover all banks once, and
+    // 16 lanes reading one logical chunk of 16 consecutive rows hit 16 distinct 4-bank
+    // groups. One load fills a 1 KB segment = 8 rows: lane i lands at row i/8,
+    // position i%8, so it fetches chunk (i%8) ^ ((r >> 1) & 7). Wave w fills rows
+    // 8*SEG*w .. of both operand tiles; the per-lane byte offsets are fixed for the
+    // whole K loop, the K position goes in the scalar offset.
+    // 128-B rows, chunk c of row r at c ^ ((r >> 1) & 7); segment j = 8 rows starting
+    // at 8 (SEG w + j): (r >> 1) & 7 = 4 ((SEG w + j) & 1) + i/16 for lane i.
+    const uint32_t kcE = static_cast<uint32_t>((lane & 7) ^ (lane >> 4)) * 16u;
+    const uint32_t kcO = static_cast<uint32_t>((lane & 7) ^ (4 | (lane >> 4))) * 16u;
     uint32_t voP[SEG], voQ[SEG], voP2[SEG], voQ2[SEG];
 #pragma unroll
     for (int j = 0; j < SEG; ++j) {
-        const int rr = 16 * SEG * wave + 16 * j + (lane >> 2);
+        const int rr = 8 * SEG * wave + 8 * j + (lane >> 3);
+        const uint32_t kc16 = (((SEG * wave + j) & 1) ? kcO : kcE);
         const uint32_t rp = static_cast<uint32_t>(min(m0 + rr, M - 1));
         const uint32_t rq = static_cast<uint32_t>(min(n0 + rr, N - 1));
         voP[j] = rp * static_cast<uint32_t>(g.ldp * 2) + kc16;
@@ -172,20 +174,19 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
         }                                                                                         \
     }
 
-    // ---- fragments: 32-row x 16-K reads per k16 sub-step kk (0, 1)
+    // ---- fragments: 32-row x 16-K reads per k16 sub-step kk (0..3)
     const uint32_t frow = lane & 31;
-    const uint32_t fsw = (frow >> 2) & 3;      // (row >> 2) & 3 of this lane's fragment rows
-    const uint32_t prow = (wm * (TM * 32) + frow) * 4;
-    const uint32_t qrow = kChunks + (wn * (TN * 32) + frow) * 4;
-    const uint32_t ch0 = (0 + (lane >> 5)) ^ fsw;
-    const uint32_t ch1 = (2 + (lane >> 5)) ^ fsw;
-    // F[0..TN) = Q fragments (n sub-tiles), F[TN..TN+TM) = P fragments (m sub-tiles),
-    // read in the order the MFMAs below consume them
+    const uint32_t fsw = (frow >> 1) & 7;
+    const uint32_t prow = (wm * (TM * 32) + frow) * 8;
+    const uint32_t qrow = kChunks + (wn * (TN * 32) + frow) * 8;
+    uint32_t chs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) chs[kk] = (2 * kk + (lane >> 5)) ^ fsw;
 #define QN_FRAGS(ST, CH, F)                                             \
     {                                                                   \
         F[0] = (ST)[qrow + (CH)];                                       \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) F[TN + i] = (ST)[prow + i * 128 + (CH)]; \
-        _Pragma("unroll") for (int i = 1; i < TN; ++i) F[i] = (ST)[qrow + i * 128 + (CH)];      \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) F[TN + i] = (ST)[prow + i * 256 + (CH)]; \
+        _Pragma("unroll") for (int i = 1; i < TN; ++i) F[i] = (ST)[qrow + i * 256 + (CH)];      \
     }
 
     f32x16 acc[TN][TM];
@@ -199,46 +200,41 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
             acc[a][b] = mfma32(F[a], F[TN + b], acc[a][b]);
 
     uint4 fa[TM + TN], fb[TM + TN];
-    // Invariant at the top of step k: stages k and k+1 are complete and certified by
-    // a barrier, the kk = 0 fragments of step k are in fa, the loads of steps k+2 and
-    // k+3 may still be in flight. Stage (k+4)%5 was last read in step k-1, before its
-    // barrier, so step k refills it with step k+4.
-#define QN_STEP(KTV, CUR, NXT, FAR)                                            \
+    // One K-step on stage CUR (its kk = 0 fragments already in fa) while NXT receives
+    // step k+1; NXT last held step k-1, whose reads all finished before the previous
+    // step's barrier. Before the last sub-step every wave waits for its own loads and
+    // the barrier certifies NXT complete, so NXT's first fragments are read under the
+    // last MFMAs; CUR's reads are all done by then, so the next step may refill it.
+#define QN_STEP(KTV, CUR, NXT)                                                 \
     {                                                                          \
         const int k_ = (KTV);                                                  \
-        if (k_ + 4 < KT) QN_ISSUE(k_ + 4, FAR)                                 \
-        QN_FRAGS(CUR, ch1, fb)                                                 \
+        if (k_ + 1 < KT) QN_ISSUE(k_ + 1, NXT)                                 \
+        QN_FRAGS(CUR, chs[1], fb)                                              \
         QN_MFMAS(fa)                                                           \
         QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
-        if (k_ + 1 < KT) QN_FRAGS(NXT, ch0, fa)                                \
+        QN_FRAGS(CUR, chs[2], fa)                                              \
         QN_MFMAS(fb)                                                           \
         QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
-        if (k_ + 4 < KT) { QN_WAIT_VM(2 * kLoadsPerStep); }                    \
-        else if (k_ + 3 < KT) { QN_WAIT_VM(kLoadsPerStep); }                   \
-        else { QN_WAIT_VM(0); }                                                \
+        QN_FRAGS(CUR, chs[3], fb)                                              \
+        QN_MFMAS(fa)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+        __builtin_amdgcn_s_waitcnt(0);                                         \
         QN_BARRIER();                                                          \
+        if (k_ + 1 < KT) QN_FRAGS(NXT, chs[0], fa)                             \
+        QN_MFMAS(fb)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
     }
 
     QN_ISSUE(0, g_st0)
-    if (KT > 1) QN_ISSUE(1, g_st1)
-    if (KT > 2) QN_ISSUE(2, g_st2)
-    if (KT > 3) QN_ISSUE(3, g_st3)
-    if (KT > 3) { QN_WAIT_VM(2 * kLoadsPerStep); } else if (KT > 2) { QN_WAIT_VM(kLoadsPerStep); } else { QN_WAIT_VM(0); }
+    QN_WAIT_VM(0);
     QN_BARRIER();
-    QN_FRAGS(g_st0, ch0, fa)
-
+    QN_FRAGS(g_st0, chs[0], fa)
     int kt = 0;
-    for (; kt + 5 <= KT; kt += 5) {
-        QN_STEP(kt, g_st0, g_st1, g_st4)
-        QN_STEP(kt + 1, g_st1, g_st2, g_st0)
-        QN_STEP(kt + 2, g_st2, g_st3, g_st1)
-        QN_STEP(kt + 3, g_st3, g_st4, g_st2)
-        QN_STEP(kt + 4, g_st4, g_st0, g_st3)
+    for (; kt + 2 <= KT; kt += 2) {
+        QN_STEP(kt, g_st0, g_st1)
+        QN_STEP(kt + 1, g_st1, g_st0)
     }
-    if (kt < KT) QN_STEP(kt, g_st0, g_st1, g_st4)
-    if (kt + 1 < KT) QN_STEP(kt + 1, g_st1, g_st2, g_st0)
-    if (kt + 2 < KT) QN_STEP(kt + 2, g_st2, g_st3, g_st1)
-    if (kt + 3 < KT) QN_STEP(kt + 3, g_st3, g_st4, g_st2)
+    if (kt < KT) QN_STEP(kt, g_st0, g_st1)
 #undef QN_STEP
 #undef QN_MFMAS
 #undef QN_FRAGS
@@ -246,7 +242,7 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 
     // ---- epilogue. Every wave is past the last barrier, so the LDS stages are free
     // and no load is in flight. The bf16 C tile (256 rows x 512 B) goes to LDS: rows
-    // 64q .. 64q+63 in stage q (q = 0..3), 16-byte chunk j of row r at position
+    // 128q .. 128q+127 in stage q (q = 0, 1), 16-byte chunk j of row r at position
     // j ^ (r & 31) (two-pass, conflict-free 8-byte writes, conflict-free 16-byte
     // reads); then each row leaves as 512 contiguous bytes, 16 B per lane.
     // The lane holds C[m][n..n+3] for m = tile row frow + 32 b + 32 TM wm and
@@ -254,9 +250,8 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
         const int rl = wm * (TM * 32) + b * 32 + static_cast<int>(frow);
-        const int q = rl >> 6;
-        uint4* arr = q == 0 ? g_st0 : (q == 1 ? g_st1 : (q == 2 ? g_st2 : g_st3));
-        char* rowp = reinterpret_cast<char*>(arr) + (rl & 63) * 512;
+        uint4* arr = (rl >> 7) ? g_st1 : g_st0;
+        char* rowp = reinterpret_cast<char*>(arr) + (rl & 127) * 512;
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
 #pragma unroll
@@ -275,9 +270,8 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 #pragma unroll
     for (int i = 0; i < BM / kRowsPerPass; ++i) {
         const int r = i * kRowsPerPass + (tid >> 5);
-        const int q = r >> 6;
-        const uint4* arr = q == 0 ? g_st0 : (q == 1 ? g_st1 : (q == 2 ? g_st2 : g_st3));
-        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(arr) + (r & 63) * 512 +
+        const uint4* arr = (r >> 7) ? g_st1 : g_st0;
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(arr) + (r & 127) * 512 +
                                                         ((cj ^ (r & 31)) << 4));
         const int m = m0 + r;
         const int n = n0 + cj * 8;
