@@ -317,8 +317,11 @@ constexpr int kDeqIters = 4;                     // 8-weight groups per thread p
 constexpr int kDeqPerWG = 256 * 8 * kDeqIters;   // weights per row-major dequant workgroup
 constexpr int kTP = 64 + 8;                      // LDS pitch (bf16) of the transpose tile
 
+// NT = ceil(r / 32) rank tiles are computed; columns NT*32 .. r_pad-1 are written as
+// zeros. Chunks of 64 K of X and (for NT <= 2) of R are prefetched one chunk ahead.
 template <int NT>
 __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* lds) {
+    constexpr bool kPrefR = NT <= 2;
     f32x16* red = reinterpret_cast<f32x16*>(lds);      // [2][NT][64]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -341,20 +344,58 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* 
         rok[t] = rr < a.r;
         rrow[t] = a.R + static_cast<int64_t>(rok[t] ? rr : 0) * a.ldr + ksub;
     }
-    for (int k = kbeg; k < kend; k += 64) {
-        uint4 pf[4];
+    // X chunks (64 K each) are loaded kDepth chunks ahead into a ring of registers;
+    // R chunks (for NT <= 2) one chunk ahead. Rows of R at or beyond r are not loaded
+    // (they contribute zeros).
+    constexpr int kDepth = 4;
+    uint4 px[kDepth][4];
+    uint4 ra[kPrefR ? NT : 1][4], rb[kPrefR ? NT : 1][4];
+#define QN_XLOAD(K0, PF)                                                                       \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u) PF[u] = *reinterpret_cast<const uint4*>(prow + (K0) + 16 * u);
+#define QN_RLOAD(K0, RF)                                                                       \
+    if constexpr (kPrefR) {                                                                    \
+        _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
+            _Pragma("unroll") for (int u = 0; u < 4; ++u)                                      \
+                RF[t % (kPrefR ? NT : 1)][u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) : uint4{0, 0, 0, 0}; \
+    }
+#define QN_PCOMP(K0, PF, RF)                                                                   \
+    {                                                                                          \
+        if constexpr (kPrefR) {                                                                \
+            _Pragma("unroll") for (int u = 0; u < 4; ++u)                                      \
+                _Pragma("unroll") for (int t = 0; t < NT; ++t) acc[t] = mfma32(RF[t % (kPrefR ? NT : 1)][u], PF[u], acc[t]); \
+        } else {                                                                               \
+            _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                   \
+                uint4 rf[4];                                                                   \
+                _Pragma("unroll") for (int u = 0; u < 4; ++u)                                  \
+                    rf[u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) : uint4{0, 0, 0, 0}; \
+                _Pragma("unroll") for (int u = 0; u < 4; ++u) acc[t] = mfma32(rf[u], PF[u], acc[t]); \
+            }                                                                                  \
+        }                                                                                      \
+    }
+    // chunk c (0-based from kbeg) lives in px[c % kDepth]; R alternates ra / rb
 #pragma unroll
-        for (int u = 0; u < 4; ++u) pf[u] = *reinterpret_cast<const uint4*>(prow + k + 16 * u);
+    for (int d = 0; d < kDepth - 1; ++d)
+        if (kbeg + 64 * d < kend) QN_XLOAD(kbeg + 64 * d, px[d])
+    if (kbeg < kend) QN_RLOAD(kbeg, ra)
+    for (int k = kbeg; k < kend; k += 64 * kDepth) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                uint4 rf = *reinterpret_cast<const uint4*>(rrow[t] + k + 16 * u);
-                if (!rok[t]) rf = uint4{0, 0, 0, 0};
-                acc[t] = mfma32(rf, pf[u], acc[t]);
+        for (int d = 0; d < kDepth; ++d) {
+            const int kc = k + 64 * d;
+            if (kc < kend) {
+                if (kc + 64 * (kDepth - 1) < kend) QN_XLOAD(kc + 64 * (kDepth - 1), px[(d + kDepth - 1) % kDepth])
+                if (d % 2 == 0) {
+                    if (kc + 64 < kend) QN_RLOAD(kc + 64, rb)
+                    QN_PCOMP(kc, px[d], ra)
+                } else {
+                    if (kc + 64 < kend) QN_RLOAD(kc + 64, ra)
+                    QN_PCOMP(kc, px[d], rb)
+                }
             }
         }
     }
+#undef QN_XLOAD
+#undef QN_RLOAD
+#undef QN_PCOMP
     // sum the four K-quarters: waves 2,3 -> 0,1, then 1 -> 0
     if (wave >= 2)
 #pragma unroll
@@ -371,20 +412,22 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* 
     if (wave != 0) return;
     const int m = m0 + (lane & 31);
     if (m >= a.M) return;
+    uint16_t* orow = a.OUT + static_cast<int64_t>(m) * a.r_pad;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const f32x16 v = acc[t] + red[t * 64 + lane];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
-            if (n < a.r_pad) {
-                uint2 o;
-                o.x = pack_bf16x2(a.s * v[4 * gq + 0], a.s * v[4 * gq + 1]);
-                o.y = pack_bf16x2(a.s * v[4 * gq + 2], a.s * v[4 * gq + 3]);
-                *reinterpret_cast<uint2*>(a.OUT + static_cast<int64_t>(m) * a.r_pad + n) = o;
-            }
+            uint2 o;
+            o.x = pack_bf16x2(a.s * v[4 * gq + 0], a.s * v[4 * gq + 1]);
+            o.y = pack_bf16x2(a.s * v[4 * gq + 2], a.s * v[4 * gq + 3]);
+            *reinterpret_cast<uint2*>(orow + n) = o;
         }
     }
+    // zero padding columns NT*32 .. r_pad-1 (lanes 0..31 own this row, 4 bf16 per store)
+    for (int n = NT * 32 + 4 * (lane >> 5); n < a.r_pad; n += 8)
+        *reinterpret_cast<uint2*>(orow + n) = uint2{0u, 0u};
 }
 
 // Adapter layouts; destination is [rows, r_pad] (pad) or [acols, r_pad] (transpose).
@@ -657,17 +700,18 @@ hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const flo
     a.n_adapt = static_cast<int>(adapt_elems == 0 ? 0 : std::min<int64_t>(64, (adapt_elems + 255) / 256));
     const int64_t n = d_out * d_in;
     a.n_deq = static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64) : (n + kDeqPerWG - 1) / kDeqPerWG);
-    const int NT = r_pad / 32;
+    const int NT = (r + 31) / 32;
     const size_t lds_pre = static_cast<size_t>(2) * NT * 64 * sizeof(f32x16);
     const size_t lds_deq = 64 + static_cast<size_t>(64) * kTP * sizeof(uint16_t);
     const size_t lds = std::max(lds_pre, lds_deq);
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
     const NF4Tables& tab = tables();
     switch (NT) {
-        case 2: QN_LAUNCH("prologue_kernel", st, prologue_kernel<2>, grid, dim3(256), lds, st, a, tab); break;
-        case 4: QN_LAUNCH("prologue_kernel", st, prologue_kernel<4>, grid, dim3(256), lds, st, a, tab); break;
-        case 6: QN_LAUNCH("prologue_kernel", st, prologue_kernel<6>, grid, dim3(256), lds, st, a, tab); break;
-        case 8: QN_LAUNCH("prologue_kernel", st, prologue_kernel<8>, grid, dim3(256), lds, st, a, tab); break;
+#define QN_PRO_CASE(T) \
+        case T: QN_LAUNCH("prologue_kernel", st, prologue_kernel<T>, grid, dim3(256), lds, st, a, tab); break;
+        QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
+        QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
+#undef QN_PRO_CASE
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
