@@ -70,7 +70,7 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.lora = off;   off += align_up(2 * d_seq * w.r_pad, 256);                     // s(XA^T) or s(dY B)
     w.adapt = off;  off += align_up(2 * (d_out > d_in ? d_out : d_in) * w.r_pad, 256);  // B padded or A^T padded
     w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T
-    w.t = off;      off += align_up(4 * static_cast<int64_t>(r), 256);              // fp32 A x (GEMV)
+    w.t = off;      off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);  // GEMV: partial A x
     w.bytes = off;
     return w;
 }

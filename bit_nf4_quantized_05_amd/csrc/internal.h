@@ -64,10 +64,11 @@ hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const flo
 // dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);
-// y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes.
+// y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes;
+// ws_part holds at most d_in/64 x r floats of partial A x sums.
 hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                            const float* qmean, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
-                           const uint16_t* x, uint16_t* y, float* ws_t, hipStream_t st);
+                           const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st);
 
 }  // namespace qn

@@ -39,6 +39,9 @@ def test_version_and_sizes():
     assert qn.nf4_sizes(28672, 8192) == (28672 * 8192 // 2, 3670016, 14336)
     assert qn.quantize_workspace_bytes(4096, 4096) >= 262144 * 4
     assert qn.linear_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 4096 * 4096
+    # d_seq = 1: the forward streams the codes, but the input gradient still runs the
+    # dequantise + GEMM path, so one workspace size must cover both
+    assert qn.linear_workspace_bytes(4096, 4096, 1, 16) >= 2 * 4096 * 4096 + 4 * 64 * 16
     assert qn.quantize_workspace_bytes(0, 5) == 0
     assert qn.linear_workspace_bytes(64, 64, 1, 0) == 0
 

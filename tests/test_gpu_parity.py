@@ -165,6 +165,8 @@ LINEAR_SMALL = [
     WL.custom("long_k", 256, 2048, 96, 16, s=2.0),
     WL.custom("gemv_small", 192, 320, 1, 8, s=2.0),
     WL.custom("gemv_r64", 512, 1024, 1, 64, s=1.0),
+    WL.custom("gemv_ragged", 320, 4160, 1, 3, s=2.0),       # 3 column chunks, the last 64 wide
+    WL.custom("gemv_wide", 128, 11008, 1, 256, s=0.5),      # 6 column chunks, r = 256
 ]
 
 
