@@ -12,13 +12,16 @@
 // division), so the results are bit-identical to any faithful implementation.
 //
 // Kernels:
-//   quant_blocks   - HBM-streaming pass over W: per 64-block absmax (8-lane DPP max),
-//                    codes by a 32-cell threshold table in LDS, packed nibbles, the
-//                    block constants, and an exact per-workgroup sum of the
-//                    constants as 32-bit-limb integers (order-free).
-//   mean_finalize  - one workgroup: adds the per-workgroup limb sums, divides by n_b
-//                    with integer long division and rounds once to float32 -> mu.
-//   dq_encode      - one workgroup per group of 256 constants: centre, absmax, INT8.
+//   quant_blocks   - HBM-streaming pass over W (16 waves per workgroup, each with the
+//                    next tile's loads in flight while it codes the current one): per
+//                    64-block absmax (8-lane DPP max), codes by a 32-cell threshold
+//                    table in LDS, packed nibbles, the block constants, and an exact
+//                    per-workgroup sum of the constants as 32-bit-limb integers.
+//   dq_encode      - each workgroup first forms mu itself: it adds the per-workgroup
+//                    limb sums (integers, so the order is free and every workgroup gets
+//                    the same bits), divides by n_b with integer long division and rounds
+//                    once to float32; then, for its kDqGroups groups of 256 constants:
+//                    centre, absmax, INT8.
 //   dequant_rows   - double dequantisation to bf16 (the standalone entry point; the
 //                    linear calls dequantise inside their prologue launch).
 #include <hip/hip_runtime.h>
@@ -47,9 +50,28 @@ __device__ __forceinline__ uint32_t max8(uint32_t v) {
 // ---------------------------------------------------------------------------
 // Level 1. A wave handles a tile of 8 blocks (512 floats): lane l owns floats
 // [8l, 8l+8) of the tile, so 8 lanes share a block and each lane emits one
-// 32-bit word of codes.
+// 32-bit word of codes. Tiles are strided over the grid; a wave issues the loads of
+// its next tile before coding the current one.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads)
+constexpr int kQuantThreads = 1024;
+
+struct Tile8 { float v[8]; };
+
+__device__ __forceinline__ Tile8 load_tile8(const float* __restrict__ W, int64_t n, int64_t e0) {
+    Tile8 t;
+    if (e0 + 8 <= n) {
+        const float4 lo = *reinterpret_cast<const float4*>(W + e0);
+        const float4 hi = *reinterpret_cast<const float4*>(W + e0 + 4);
+        t.v[0] = lo.x; t.v[1] = lo.y; t.v[2] = lo.z; t.v[3] = lo.w;
+        t.v[4] = hi.x; t.v[5] = hi.y; t.v[6] = hi.z; t.v[7] = hi.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t.v[e] = (e0 + e < n) ? W[e0 + e] : 0.0f;
+    }
+    return t;
+}
+
+__global__ __launch_bounds__(kQuantThreads)
 void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
                   uint32_t* __restrict__ codes32, float* __restrict__ absmax,
                   unsigned long long* __restrict__ limb_part, NF4Tables tab) {
@@ -64,32 +86,27 @@ void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
     if (tid < kLimbs) s_limb[tid] = 0ull;
     __syncthreads();
 
+    constexpr int kWaves = kQuantThreads / 64;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t n_tiles = (n_b + 7) >> 3;
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * 4;
-    for (int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wave; t < n_tiles; t += stride) {
-        const int64_t e0 = t * 512 + lane * 8;
-        float v[8];
-        if (e0 + 8 <= n) {
-            const float4 lo = *reinterpret_cast<const float4*>(W + e0);
-            const float4 hi = *reinterpret_cast<const float4*>(W + e0 + 4);
-            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (e0 + e < n) ? W[e0 + e] : 0.0f;
-        }
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWaves;
+    int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
+    Tile8 cur;
+    if (t < n_tiles) cur = load_tile8(W, n, t * 512 + lane * 8);
+    for (; t < n_tiles; t += stride) {
+        Tile8 nxt;
+        if (t + stride < n_tiles) nxt = load_tile8(W, n, (t + stride) * 512 + lane * 8);
         uint32_t m = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+        for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(cur.v[e]) & 0x7FFFFFFFu);
         m = max8(m);                         // exact absmax bits of the block
         const float a = __uint_as_float(m);
 
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = (m == 0) ? 0.0f : v[e] / a;       // IEEE division, |x| <= 1
+            const float x = (m == 0) ? 0.0f : cur.v[e] / a;   // IEEE division, |x| <= 1
             const int cell = min(max(static_cast<int>((x + 1.0f) * 16.0f), 0), kCells - 1);
             const uint32_t c = s_base[cell] + (x > s_thr[cell] ? 1u : 0u);
             packed |= c << (4 * e);
@@ -109,50 +126,27 @@ void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
                 if (wide >> 32) atomicAdd(&s_limb[li + 1], wide >> 32);
             }
         }
+        cur = nxt;
     }
     __syncthreads();
-    if (tid < kLimbs) limb_part[static_cast<int64_t>(blockIdx.x) * kLimbs + tid] = s_limb[tid];
+    // limb-major: limb L of workgroup g at limb_part[L * gridDim.x + g]
+    if (tid < kLimbs) limb_part[static_cast<int64_t>(tid) * gridDim.x + blockIdx.x] = s_limb[tid];
 }
 
 // ---------------------------------------------------------------------------
-// mu = RoundNearestEven_f32( (sum_j a_j) / n_b ), exact.
-// The sum is an integer S in units of 2^-149 held as 32-bit limbs. Each thread
-// adds whole per-workgroup records (10 limbs), the 256 threads are reduced in LDS,
-// then one thread carries, divides by n_b and rounds. Every limb array below is
+// mu = RoundNearestEven_f32( (sum_j a_j) / n_b ), exact. The sum is an integer S
+// in units of 2^-149 given as per-limb column totals colsum[L] (limb L weighs
+// 2^(32 L)); each column total is < n_b * 2^32 < 2^64. Every limb array below is
 // indexed by compile-time constants only (fully unrolled), so it stays in registers.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads)
-void mean_finalize(const unsigned long long* __restrict__ limb_part, int parts, int64_t n_b,
-                   float* __restrict__ qmean) {
-    __shared__ unsigned long long s_sum[kLimbs][kThreads];
-    const int tid = threadIdx.x;
-    unsigned long long acc[kLimbs];
-#pragma unroll
-    for (int L = 0; L < kLimbs; ++L) acc[L] = 0ull;
-    for (int g = tid; g < parts; g += kThreads) {
-        const unsigned long long* rec = limb_part + static_cast<int64_t>(g) * kLimbs;
-#pragma unroll
-        for (int L = 0; L < kLimbs; ++L) acc[L] += rec[L];
-    }
-#pragma unroll
-    for (int L = 0; L < kLimbs; ++L) s_sum[L][tid] = acc[L];
-    __syncthreads();
-    for (int h = kThreads / 2; h >= 1; h >>= 1) {
-        if (tid < h) {
-#pragma unroll
-            for (int L = 0; L < kLimbs; ++L) s_sum[L][tid] += s_sum[L][tid + h];
-        }
-        __syncthreads();
-    }
-    if (tid != 0) return;
-
+__device__ __forceinline__ float mean_from_limbs(const unsigned long long* colsum, int64_t n_b) {
     // carry-normalise to 32-bit limbs (each column total is < n_b * 2^32 < 2^64)
     constexpr int kQ = kLimbs + 1;
     uint32_t N[kQ];
     unsigned long long carry = 0ull;
 #pragma unroll
     for (int L = 0; L < kLimbs; ++L) {
-        const unsigned long long col = s_sum[L][0];
+        const unsigned long long col = colsum[L];
         const unsigned long long low = (col & 0xFFFFFFFFull) + (carry & 0xFFFFFFFFull);
         N[L] = static_cast<uint32_t>(low);
         carry = (col >> 32) + (carry >> 32) + (low >> 32);
@@ -204,29 +198,61 @@ void mean_finalize(const unsigned long long* __restrict__ limb_part, int parts, 
         if ((2ull * rem > d) || (2ull * rem == d && (mant & 1u))) ++mant;
         bits = mant;
     }
-    qmean[0] = __uint_as_float(bits);
+    return __uint_as_float(bits);
 }
 
+
 // ---------------------------------------------------------------------------
-// Level 2: one workgroup per group of 256 block constants.
+// Level 2. A workgroup of 1024 threads forms mu (waves 0..9 add one limb column
+// each over the quant_blocks workgroups), then encodes kDqGroups groups of 256
+// block constants, one per 4 waves.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads)
-void dq_encode(const float* __restrict__ absmax, int64_t n_b, const float* __restrict__ qmean,
-               int8_t* __restrict__ qconst, float* __restrict__ qscale) {
-    __shared__ uint32_t s_max[kThreads / 64];
+constexpr int kDqThreads = 1024;
+constexpr int kDqGroups = kDqThreads / kGroup;
+
+__global__ __launch_bounds__(kDqThreads)
+void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned long long* __restrict__ limb_part,
+               int parts, float* __restrict__ qmean, int8_t* __restrict__ qconst, float* __restrict__ qscale) {
+    __shared__ unsigned long long s_col[kLimbs];
+    __shared__ float s_mu;
+    __shared__ uint32_t s_max[kDqThreads / 64];
     const int tid = threadIdx.x;
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * kGroup + tid;
-    const float mu = qmean[0];
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kDqThreads + tid;
     const bool valid = j < n_b;
-    const float d = valid ? absmax[j] - mu : 0.0f;
+    const float a = valid ? absmax[j] : 0.0f;
+    if (wave < kLimbs) {
+        unsigned long long acc = 0ull;
+        for (int g = lane; g < parts; g += 64) acc += limb_part[static_cast<int64_t>(wave) * parts + g];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc & 0xFFFFFFFFull), off));
+            const uint32_t hi = static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc >> 32), off));
+            acc += (static_cast<unsigned long long>(hi) << 32) | lo;
+        }
+        if (lane == 0) s_col[wave] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long col[kLimbs];
+#pragma unroll
+        for (int L = 0; L < kLimbs; ++L) col[L] = s_col[L];
+        s_mu = mean_from_limbs(col, n_b);
+        if (blockIdx.x == 0) qmean[0] = s_mu;
+    }
+    __syncthreads();
+    const float mu = s_mu;
+    const float d = valid ? a - mu : 0.0f;
     uint32_t m = __float_as_uint(d) & 0x7FFFFFFFu;
     m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
     m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16)));
     m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 8)));
     m = max8(m);
-    if ((tid & 63) == 0) s_max[tid >> 6] = m;
+    if (lane == 0) s_max[wave] = m;
     __syncthreads();
-    const uint32_t mb = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+    const int g0 = (wave >> 2) << 2;             // the 4 waves of this thread's group
+    const uint32_t mb = max(max(s_max[g0], s_max[g0 + 1]), max(s_max[g0 + 2], s_max[g0 + 3]));
     const float b = __uint_as_float(mb);
     if (valid) {
         int8_t q = 0;
@@ -236,7 +262,8 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const float* __res
         }
         qconst[j] = q;
     }
-    if (tid == 0) qscale[blockIdx.x] = b;
+    const int64_t grp = static_cast<int64_t>(blockIdx.x) * kDqGroups + (wave >> 2);
+    if ((tid & (kGroup - 1)) == 0 && grp * kGroup < n_b) qscale[grp] = b;
 }
 
 // ---------------------------------------------------------------------------
@@ -274,9 +301,10 @@ void dequant_rows(const uint32_t* __restrict__ codes32, const int8_t* __restrict
 }  // namespace
 
 int quant_grid(int64_t n_b) {
+    // one 16-wave workgroup per CU, fewer for small inputs (one tile per wave at least)
     const int64_t tiles = (n_b + 7) / 8;
-    const int64_t want = (tiles + 3) / 4;
-    return static_cast<int>(want < 1024 ? (want < 1 ? 1 : want) : 1024);
+    const int64_t want = (tiles + 15) / 16;
+    return static_cast<int>(want < 256 ? (want < 1 ? 1 : want) : 256);
 }
 
 hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
@@ -284,11 +312,11 @@ hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
                            float* ws_absmax, unsigned long long* ws_limbs, int grid,
                            hipStream_t st) {
     const NF4Tables& tab = tables();
-    QN_LAUNCH("quant_blocks", st, quant_blocks, dim3(grid), dim3(kThreads), 0, st, W, n, n_b,
-                       reinterpret_cast<uint32_t*>(codes), ws_absmax, ws_limbs, tab);
-    QN_LAUNCH("mean_finalize", st, mean_finalize, dim3(1), dim3(kThreads), 0, st, ws_limbs, grid, n_b, qmean);
-    QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(n_g)), dim3(kThreads), 0, st,
-                       ws_absmax, n_b, qmean, qconst, qscale);
+    QN_LAUNCH("quant_blocks", st, quant_blocks, dim3(grid), dim3(kQuantThreads), 0, st, W, n, n_b,
+              reinterpret_cast<uint32_t*>(codes), ws_absmax, ws_limbs, tab);
+    const int64_t dq_grid = (n_g + kDqGroups - 1) / kDqGroups;
+    QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(dq_grid)), dim3(kDqThreads), 0, st,
+              ws_absmax, n_b, ws_limbs, grid, qmean, qconst, qscale);
     return hipGetLastError();
 }
 
