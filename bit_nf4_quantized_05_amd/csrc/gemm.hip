@@ -313,26 +313,38 @@ struct PrologueArgs {
     int n_pre, n_adapt, n_deq;
 };
 
-constexpr int kDeqIters = 4;                     // 8-weight groups per thread per workgroup
-constexpr int kDeqPerWG = 256 * 8 * kDeqIters;   // weights per row-major dequant workgroup
+constexpr int kDeqPerWG = 8192;                  // weights per row-major dequant workgroup (128 blocks)
 constexpr int kTP = 64 + 8;                      // LDS pitch (bf16) of the transpose tile
 
+// Three LDS ring slots of the pre-pass, as distinct objects (each 4 waves x 32 rows x
+// 128 B) so the compiler can tell that reading one does not depend on direct-to-LDS
+// loads into another. The other prologue jobs use them as scratch.
+__shared__ uint4 g_pre0[4 * 256];
+__shared__ uint4 g_pre1[4 * 256];
+__shared__ uint4 g_pre2[4 * 256];
+
 // NT = ceil(r / 32) rank tiles are computed; columns NT*32 .. r_pad-1 are written as
-// zeros. Chunks of 64 K of X and (for NT <= 2) of R are prefetched one chunk ahead.
+// zeros. The 4 waves take K-quarters; each streams its quarter in chunks of 32 rows
+// x 64 K of X through a ring of 3 LDS slots, two chunks ahead: a chunk is loaded
+// by 4 direct-to-LDS loads of 8 whole 128-byte rows each (coalesced), with the
+// 16-byte pieces of row r XOR-swizzled by ((r >> 1) & 7) so the MFMA fragment
+// reads (32 rows, one piece each) are free of bank conflicts. For NT <= 2 the
+// matching chunk of R is fetched into registers with the chunk of X (vector loads
+// complete in issue order, so both must run equally far ahead); for NT > 2 (rank
+// >= 96) R fragments are loaded at their use.
 template <int NT>
-__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* lds) {
+__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b) {
     constexpr bool kPrefR = NT <= 2;
-    f32x16* red = reinterpret_cast<f32x16*>(lds);      // [2][NT][64]
+    constexpr int kRS = kPrefR ? NT : 1;               // R tiles held per ring slot
+    constexpr int kLoads = 4 + (kPrefR ? 4 * NT : 0);  // vector loads per chunk
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int m0 = b * 32;
-    const int64_t rowm = min(m0 + (lane & 31), a.M - 1);
     const int nchunk = a.K / 64;                       // whole 64-wide K chunks, split over 4 waves
     const int kbeg = (wave * nchunk / 4) * 64;
     const int kend = ((wave + 1) * nchunk / 4) * 64;
     const int ksub = 8 * (lane >> 5);
-    const uint16_t* prow = a.P + rowm * a.ldp + ksub;
     f32x16 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
@@ -344,78 +356,92 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* 
         rok[t] = rr < a.r;
         rrow[t] = a.R + static_cast<int64_t>(rok[t] ? rr : 0) * a.ldr + ksub;
     }
-    // X chunks (64 K each) are loaded kDepth chunks ahead into a ring of registers;
-    // R chunks (for NT <= 2) one chunk ahead. Rows of R at or beyond r are not loaded
-    // (they contribute zeros).
-    constexpr int kDepth = 4;
-    uint4 px[kDepth][4];
-    uint4 ra[kPrefR ? NT : 1][4], rb[kPrefR ? NT : 1][4];
-#define QN_XLOAD(K0, PF)                                                                       \
-    _Pragma("unroll") for (int u = 0; u < 4; ++u) PF[u] = *reinterpret_cast<const uint4*>(prow + (K0) + 16 * u);
-#define QN_RLOAD(K0, RF)                                                                       \
-    if constexpr (kPrefR) {                                                                    \
-        _Pragma("unroll") for (int t = 0; t < NT; ++t)                                         \
-            _Pragma("unroll") for (int u = 0; u < 4; ++u)                                      \
-                RF[t % (kPrefR ? NT : 1)][u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) : uint4{0, 0, 0, 0}; \
+    // DMA source of lane i in load u: row 8u + i/8 of the chunk, piece (i%8) ^ swz
+    const uint16_t* xsrc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int r = 8 * u + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        xsrc[u] = a.P + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.ldp + 8 * c;
     }
-#define QN_PCOMP(K0, PF, RF)                                                                   \
+    // fragment of sub-step u: row lane%32, piece (2u + lane/32) ^ ((row >> 1) & 7)
+    const int frow = lane & 31;
+    int fpos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fpos[u] = frow * 8 + ((2 * u + (lane >> 5)) ^ ((frow >> 1) & 7));
+    uint4 pr[3][kRS][4];
+#define QN_CLOAD(K0, SL, S)                                                                    \
     {                                                                                          \
+        uint4* sl_ = (SL) + wave * 256;                                                        \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u)                                          \
+            __builtin_amdgcn_global_load_lds((global_ptr)(xsrc[u] + (K0)), (lds_ptr)(sl_ + 64 * u), 16, 0, 0); \
+        if constexpr (kPrefR) {                                                                \
+            _Pragma("unroll") for (int t = 0; t < kRS; ++t)                                    \
+                _Pragma("unroll") for (int u = 0; u < 4; ++u)                                  \
+                    pr[S][t][u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) \
+                                         : uint4{0, 0, 0, 0};                                  \
+        }                                                                                      \
+    }
+#define QN_PCOMP(K0, SL, S)                                                                    \
+    {                                                                                          \
+        const uint4* sl_ = (SL) + wave * 256;                                                  \
+        uint4 xf[4];                                                                           \
+        _Pragma("unroll") for (int u = 0; u < 4; ++u) xf[u] = sl_[fpos[u]];                    \
         if constexpr (kPrefR) {                                                                \
             _Pragma("unroll") for (int u = 0; u < 4; ++u)                                      \
-                _Pragma("unroll") for (int t = 0; t < NT; ++t) acc[t] = mfma32(RF[t % (kPrefR ? NT : 1)][u], PF[u], acc[t]); \
+                _Pragma("unroll") for (int t = 0; t < NT; ++t)                                 \
+                    acc[t] = mfma32(pr[S][t % kRS][u], xf[u], acc[t]);                         \
         } else {                                                                               \
             _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                   \
                 uint4 rf[4];                                                                   \
                 _Pragma("unroll") for (int u = 0; u < 4; ++u)                                  \
                     rf[u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) : uint4{0, 0, 0, 0}; \
-                _Pragma("unroll") for (int u = 0; u < 4; ++u) acc[t] = mfma32(rf[u], PF[u], acc[t]); \
+                _Pragma("unroll") for (int u = 0; u < 4; ++u) acc[t] = mfma32(rf[u], xf[u], acc[t]); \
             }                                                                                  \
         }                                                                                      \
     }
-    // chunk c (0-based from kbeg) lives in px[c % kDepth]; R alternates ra / rb
-#pragma unroll
-    for (int d = 0; d < kDepth - 1; ++d)
-        if (kbeg + 64 * d < kend) QN_XLOAD(kbeg + 64 * d, px[d])
-    if (kbeg < kend) QN_RLOAD(kbeg, ra)
-    for (int k = kbeg; k < kend; k += 64 * kDepth) {
-#pragma unroll
-        for (int d = 0; d < kDepth; ++d) {
-            const int kc = k + 64 * d;
-            if (kc < kend) {
-                if (kc + 64 * (kDepth - 1) < kend) QN_XLOAD(kc + 64 * (kDepth - 1), px[(d + kDepth - 1) % kDepth])
-                if (d % 2 == 0) {
-                    if (kc + 64 < kend) QN_RLOAD(kc + 64, rb)
-                    QN_PCOMP(kc, px[d], ra)
-                } else {
-                    if (kc + 64 < kend) QN_RLOAD(kc + 64, ra)
-                    QN_PCOMP(kc, px[d], rb)
-                }
-            }
-        }
+    // chunk kc: wait until its loads are done (those of the up to two later chunks may
+    // still be in flight), compute, then refill its slot with chunk kc + 3
+#define QN_PSTEP(KC, SL, S)                                                                    \
+    if ((KC) < kend) {                                                                         \
+        if ((KC) + 128 < kend) { QN_WAIT_VM(2 * kLoads); }                                    \
+        else if ((KC) + 64 < kend) { QN_WAIT_VM(kLoads); }                                    \
+        else { QN_WAIT_VM(0); }                                                                \
+        QN_PCOMP(KC, SL, S)                                                                    \
+        if ((KC) + 192 < kend) QN_CLOAD((KC) + 192, SL, S)                                     \
     }
-#undef QN_XLOAD
-#undef QN_RLOAD
+    if (kbeg < kend) QN_CLOAD(kbeg, g_pre0, 0)
+    if (kbeg + 64 < kend) QN_CLOAD(kbeg + 64, g_pre1, 1)
+    if (kbeg + 128 < kend) QN_CLOAD(kbeg + 128, g_pre2, 2)
+    for (int k = kbeg; k < kend; k += 192) {
+        QN_PSTEP(k, g_pre0, 0)
+        QN_PSTEP(k + 64, g_pre1, 1)
+        QN_PSTEP(k + 128, g_pre2, 2)
+    }
+#undef QN_PSTEP
+#undef QN_CLOAD
 #undef QN_PCOMP
-    // sum the four K-quarters: waves 2,3 -> 0,1, then 1 -> 0
-    if (wave >= 2)
+    // sum the four K-quarters, one rank tile at a time through g_pre0 (every load
+    // has landed: each wave's last step waited for all of its loads)
+    f32x16* red = reinterpret_cast<f32x16*>(g_pre0);   // [2][64]
 #pragma unroll
-        for (int t = 0; t < NT; ++t) red[((wave - 2) * NT + t) * 64 + lane] = acc[t];
-    __syncthreads();
-    if (wave < 2)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] += red[(wave * NT + t) * 64 + lane];
-    __syncthreads();
-    if (wave == 1)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) red[t * 64 + lane] = acc[t];
-    __syncthreads();
+    for (int t = 0; t < NT; ++t) {
+        __syncthreads();
+        if (wave >= 2) red[(wave - 2) * 64 + lane] = acc[t];
+        __syncthreads();
+        if (wave < 2) acc[t] += red[wave * 64 + lane];
+        __syncthreads();
+        if (wave == 1) red[lane] = acc[t];
+        __syncthreads();
+        if (wave == 0) acc[t] += red[lane];
+    }
     if (wave != 0) return;
     const int m = m0 + (lane & 31);
     if (m >= a.M) return;
     uint16_t* orow = a.OUT + static_cast<int64_t>(m) * a.r_pad;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const f32x16 v = acc[t] + red[t * 64 + lane];
+        const f32x16 v = acc[t];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
@@ -431,73 +457,91 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, char* 
 }
 
 // Adapter layouts; destination is [rows, r_pad] (pad) or [acols, r_pad] (transpose).
+// Thread t of the job writes 16-byte destination chunk t (8 entries of one row), so
+// every load it needs is independent and issued at once (one memory round trip).
 __device__ __forceinline__ void adapt_job(const PrologueArgs& a, int b) {
-    const int64_t total = (a.adapt_mode == 1 ? a.arows : a.acols) * a.r_pad;
-    for (int64_t idx = static_cast<int64_t>(b) * 256 + threadIdx.x; idx < total;
-         idx += static_cast<int64_t>(a.n_adapt) * 256) {
-        const int64_t i = idx / a.r_pad, j = idx % a.r_pad;
-        uint16_t v = 0;
-        if (a.adapt_mode == 1) {
-            if (j < a.acols) v = a.asrc[i * a.acols + j];          // B [arows, acols=r] -> [arows, r_pad]
-        } else {
-            if (j < a.arows) v = a.asrc[j * a.acols + i];          // A [arows=r, acols] -> A^T [acols, r_pad]
+    const int cpr = a.r_pad / 8;                                   // chunks per destination row
+    const int64_t rows = a.adapt_mode == 1 ? a.arows : a.acols;
+    const int64_t c = static_cast<int64_t>(b) * 256 + threadIdx.x;
+    if (c >= rows * cpr) return;
+    const int64_t i = c / cpr;
+    const int j0 = static_cast<int>(c % cpr) * 8;
+    uint16_t v[8];
+    if (a.adapt_mode == 1) {                                       // B [arows, r] -> [arows, r_pad]
+        if (j0 + 8 <= a.acols && (a.acols & 7) == 0) {
+            const uint4 w = *reinterpret_cast<const uint4*>(a.asrc + i * a.acols + j0);
+            *reinterpret_cast<uint4*>(a.adst + c * 8) = w;
+            return;
         }
-        a.adst[idx] = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = j0 + e < a.acols ? a.asrc[i * a.acols + j0 + e] : uint16_t{0};
+    } else {                                                       // A [r, acols] -> A^T [acols, r_pad]
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = j0 + e < a.arows ? a.asrc[static_cast<int64_t>(j0 + e) * a.acols + i] : uint16_t{0};
     }
+    *reinterpret_cast<uint4*>(a.adst + c * 8) =
+        uint4{v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16),
+              v[4] | (static_cast<uint32_t>(v[5]) << 16), v[6] | (static_cast<uint32_t>(v[7]) << 16)};
 }
 
-__device__ __forceinline__ void dequant_rows_job(const PrologueArgs& a, int b, const float* s_code) {
+// Row-major dequantisation of kDeqPerWG = 8192 weights (128 blocks): threads 0..127
+// form a_hat of one block each into LDS (the constants are loaded once per block,
+// not per weight); thread t takes the 8-weight code words t + 256 q (q = 0..3), so
+// every load and 16-byte store of a wave is contiguous.
+__device__ __forceinline__ void dequant_rows_job(const PrologueArgs& a, int b, const float* s_code,
+                                                 float* s_ahat) {
+    constexpr int kWords = kDeqPerWG / 8 / 256;  // code words per thread
+    const int tid = threadIdx.x;
     const int64_t n = a.d_out * a.d_in;           // multiple of 64 on this path
-    const float mu = a.qmean[0];
+    const int64_t w0 = static_cast<int64_t>(b) * kDeqPerWG;
     const uint32_t* codes32 = reinterpret_cast<const uint32_t*>(a.codes);
-    int64_t t[kDeqIters];
-    uint32_t word[kDeqIters];
-    int8_t q[kDeqIters];
-    float bs[kDeqIters];
+    // code words first (the a_hat loads below are waited for before these)
+    uint32_t cw[kWords];
 #pragma unroll
-    for (int it = 0; it < kDeqIters; ++it) {
-        t[it] = static_cast<int64_t>(b) * (kDeqPerWG / 8) + it * 256 + threadIdx.x;
-        const bool ok = t[it] * 8 < n;
-        const int64_t blk = ok ? t[it] >> 3 : 0;
-        word[it] = ok ? codes32[t[it]] : 0u;
-        q[it] = a.qconst[blk];
-        bs[it] = a.qscale[blk / kGroup];
+    for (int q = 0; q < kWords; ++q) cw[q] = codes32[min(w0 + 8 * (tid + 256 * q), n - 8) / 8];
+    if (tid < kDeqPerWG / 64) {
+        const int64_t blk = min(w0 / 64 + tid, n / 64 - 1);
+        s_ahat[tid] = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
     }
+    __syncthreads();
 #pragma unroll
-    for (int it = 0; it < kDeqIters; ++it) {
-        if (t[it] * 8 >= n) break;
-        const float ahat = block_constant(q[it], bs[it], mu);
+    for (int q = 0; q < kWords; ++q) {
+        const int t = tid + 256 * q;
+        const int64_t e0 = w0 + 8 * t;
+        if (e0 >= n) break;
+        const float ahat = s_ahat[t >> 3];
         float w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] = s_code[(word[it] >> (4 * e)) & 0xFu] * ahat;
-        uint4 o;
-        o.x = pack_bf16x2(w[0], w[1]);
-        o.y = pack_bf16x2(w[2], w[3]);
-        o.z = pack_bf16x2(w[4], w[5]);
-        o.w = pack_bf16x2(w[6], w[7]);
-        *reinterpret_cast<uint4*>(a.what + t[it] * 8) = o;
+        for (int e = 0; e < 8; ++e) w[e] = s_code[(cw[q] >> (4 * e)) & 0xFu] * ahat;
+        *reinterpret_cast<uint4*>(a.what + e0) = uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                                                      pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
     }
 }
 
+// Transposed dequantisation of a 64 (o) x 64 (i) tile: each row o of the tile is one
+// 64-block, whose a_hat threads 0..63 form into LDS; thread (o, q4) dequantises 16
+// weights into the LDS tile, which is written out transposed as W_hat^T rows.
 __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, int b, const float* s_code,
-                                                       uint16_t* tile) {
+                                                       float* s_ahat, uint16_t* tile) {
     const int tid = threadIdx.x;
     const int tiles_i = static_cast<int>(a.d_in / 64);
     const int64_t i0 = static_cast<int64_t>(b % tiles_i) * 64;
     const int64_t o0 = static_cast<int64_t>(b / tiles_i) * 64;
     const int ol = tid >> 2;             // local row o (becomes the output column)
     const int q4 = tid & 3;              // which 16 of the 64 columns
-    const int64_t o = o0 + ol;
-    if (o < a.d_out) {
-        const int64_t e0 = o * a.d_in + i0 + q4 * 16;
-        const int64_t blk = e0 >> 6;
-        const float ahat = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
-        const uint2 cw = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
+    const int64_t o = min(o0 + ol, a.d_out - 1);
+    const int64_t e0 = o * a.d_in + i0 + q4 * 16;
+    const uint2 cw = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
+    if (tid < 64) {
+        const int64_t blk = (min(o0 + tid, a.d_out - 1) * a.d_in + i0) >> 6;
+        s_ahat[tid] = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
+    }
+    __syncthreads();
+    const float ahat = s_ahat[ol];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t word = e < 8 ? cw.x : cw.y;
-            tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
-        }
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t word = e < 8 ? cw.x : cw.y;
+        tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
     }
     __syncthreads();
     const int il = tid >> 2;
@@ -515,24 +559,24 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
 template <int NT>
 __global__ __launch_bounds__(256)
 void prologue_kernel(PrologueArgs a, NF4Tables tab) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char* lds = reinterpret_cast<char*>(g_pre1);          // 16 KB of scratch for the other jobs
     const int b = blockIdx.x;
     if (b < a.n_pre) {
-        prepass_job<NT>(a, b, lds);
+        prepass_job<NT>(a, b);
         return;
     }
     if (b < a.n_pre + a.n_adapt) {
         adapt_job(a, b - a.n_pre);
         return;
     }
-    float* s_code = reinterpret_cast<float*>(lds);
+    float* s_code = reinterpret_cast<float*>(lds);             // 16 floats
+    float* s_ahat = reinterpret_cast<float*>(lds + 64);        // up to 128 floats
     if (threadIdx.x < 16) s_code[threadIdx.x] = tab.code[threadIdx.x];
-    __syncthreads();
     const int bd = b - a.n_pre - a.n_adapt;
     if (a.transposed)
-        dequant_transposed_job(a, bd, s_code, reinterpret_cast<uint16_t*>(lds + 64));
+        dequant_transposed_job(a, bd, s_code, s_ahat, reinterpret_cast<uint16_t*>(lds + 64 + 512));
     else
-        dequant_rows_job(a, bd, s_code);
+        dequant_rows_job(a, bd, s_code, s_ahat);
 }
 
 // ---------------------------------------------------------------------------
@@ -864,18 +908,16 @@ hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const flo
     a.adapt_mode = adapt_mode; a.asrc = asrc; a.adst = adst; a.arows = arows; a.acols = acols;
     a.n_pre = static_cast<int>((M + 31) / 32);
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
-    a.n_adapt = static_cast<int>(adapt_elems == 0 ? 0 : std::min<int64_t>(64, (adapt_elems + 255) / 256));
+    a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
     a.n_deq = static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64) : (n + kDeqPerWG - 1) / kDeqPerWG);
     const int NT = (r + 31) / 32;
-    const size_t lds_pre = static_cast<size_t>(2) * NT * 64 * sizeof(f32x16);
-    const size_t lds_deq = 64 + static_cast<size_t>(64) * kTP * sizeof(uint16_t);
-    const size_t lds = std::max(lds_pre, lds_deq);
+    static_assert(64 + 512 + 64 * kTP * sizeof(uint16_t) <= sizeof(g_pre1), "dequant scratch fits a ring slot");
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
     const NF4Tables& tab = tables();
     switch (NT) {
 #define QN_PRO_CASE(T) \
-        case T: QN_LAUNCH("prologue_kernel", st, prologue_kernel<T>, grid, dim3(256), lds, st, a, tab); break;
+        case T: QN_LAUNCH("prologue_kernel", st, prologue_kernel<T>, grid, dim3(256), 0, st, a, tab); break;
         QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
         QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
 #undef QN_PRO_CASE
