@@ -313,3 +313,19 @@ def linear_bwd_x(w_hat: np.ndarray, a: np.ndarray, b: np.ndarray, s: float, dy: 
     W, A, B, dY = _f64(w_hat), _f64(a), _f64(b), _f64(dy)
     s = float(np.float32(s))
     return dY @ W + s * ((dY @ B) @ A)
+
+
+def lora_grads(a: np.ndarray, b: np.ndarray, s: float, x: np.ndarray, dy: np.ndarray):
+    """Gradients of the adapter factors, (dA [r, d_in], dB [d_out, r]) in float64.
+
+    Only A and B are trained; the frozen quantised weight gets no update
+    [P2 card 1; P1 LoRA]. For the loss gradient dY = dL/dY of the forward
+    Y = X W_hat^T + s (X A^T) B^T (torch layout, one token per row):
+        dB = s dY^T (X A^T),   dA = s (dY B)^T X.
+    Neither depends on W_hat. Inputs are bf16 bits: a [r, d_in], b [d_out, r],
+    x [d_seq, d_in], dy [d_seq, d_out]."""
+    A, B, X, dY = _f64(a), _f64(b), _f64(x), _f64(dy)
+    s = float(np.float32(s))
+    dB = s * (dY.T @ (X @ A.T))
+    dA = s * ((dY @ B).T @ X)
+    return dA, dB
