@@ -1,6 +1,6 @@
 """QLoRA NF4 linear layer for MI355X (gfx950): NF4 + double quantisation,
-double dequantisation, fused forward and input gradient, as hand-written HIP
-kernels behind the C ABI in include/qlora_nf4.h."""
+double dequantisation, fused forward, input gradient and adapter gradients, as
+hand-written HIP kernels behind the C ABI in include/qlora_nf4.h."""
 from ._lib import (  # noqa: F401
     NF4Weight,
     QLoRAError,
@@ -10,6 +10,8 @@ from ._lib import (  # noqa: F401
     linear_bwd_x,
     linear_fwd,
     linear_workspace_bytes,
+    lora_grads,
+    lora_grads_workspace_bytes,
     nf4_sizes,
     profile_enable,
     profile_read,

@@ -36,6 +36,9 @@ SIGNATURES = {
                                   _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_float,
                                     _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "qlora_lora_grads_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "qlora_lora_grads": (_c_int, [_c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
+                                  _c_vp, _c_i64, _c_vp]),
     "qn_profile_enable": (_c_int, [_c_int]),
     "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
 }
@@ -194,6 +197,36 @@ def linear_bwd_x(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, dY: t
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """qlora_linear_bwd_x: dX [d_seq, d_in] = dY W_hat + s (dY B) A."""
     return _linear("qlora_linear_bwd_x", q, A, B, s, dY, q.d_out, q.d_in, out, workspace)
+
+
+def lora_grads_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
+    return lib().qlora_lora_grads_workspace_bytes(d_out, d_in, d_seq, r)
+
+
+def lora_grads(A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor, dY: torch.Tensor,
+               dA: torch.Tensor | None = None, dB: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None):
+    """qlora_lora_grads: (dA [r, d_in], dB [d_out, r]) float32 adapter gradients."""
+    dev = A.device
+    r, d_in = A.shape
+    d_out = B.shape[0]
+    _need(A, torch.bfloat16, (r, d_in), "A", dev)
+    _need(B, torch.bfloat16, (d_out, r), "B", dev)
+    if X.dim() != 2 or dY.dim() != 2 or X.shape[0] != dY.shape[0]:
+        raise ValueError("X [d_seq, d_in] and dY [d_seq, d_out] must share d_seq")
+    d_seq = X.shape[0]
+    _need(X, torch.bfloat16, (d_seq, d_in), "X", dev)
+    _need(dY, torch.bfloat16, (d_seq, d_out), "dY", dev)
+    ga = dA if dA is not None else torch.empty(r, d_in, dtype=torch.float32, device=dev)
+    gb = dB if dB is not None else torch.empty(d_out, r, dtype=torch.float32, device=dev)
+    _need(ga, torch.float32, (r, d_in), "dA", dev)
+    _need(gb, torch.float32, (d_out, r), "dB", dev)
+    need = lora_grads_workspace_bytes(d_out, d_in, d_seq, r)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib().qlora_lora_grads(_ptr(A), _ptr(B), r, float(s), _ptr(X), _ptr(dY), d_out, d_in, d_seq,
+                                _ptr(ga), _ptr(gb), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "qlora_lora_grads")
+    return ga, gb
 
 
 def profile_enable(on: bool = True) -> None:

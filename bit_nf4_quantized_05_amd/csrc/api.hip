@@ -301,4 +301,66 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
     return 0;
 }
 
+// ---- adapter gradients ----------------------------------------------------
+namespace {
+struct GradWs {
+    int64_t tp, up, bt, part, bytes;
+    int r_pad;
+};
+
+GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    GradWs w{};
+    w.r_pad = static_cast<int>(align_up(r, 64));
+    int64_t off = 0;
+    w.tp = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // T' = bf16(s X A^T)
+    w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
+    w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
+    w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
+int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
+    return grad_ws(d_out, d_in, d_seq, r).bytes;
+}
+
+int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X,
+                     const uint16_t* dY, int64_t d_out, int64_t d_in, int64_t d_seq, float* dA, float* dB,
+                     void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!A || !B || !X || !dY || !dA || !dB || !workspace) return fail(-1, "null pointer argument");
+    if (d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1");
+    if (r < 1 || r > 256) return fail(-1, "r must be in [1, 256]");
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(X, 16) || !aligned(dY, 16) || !aligned(dA, 16) ||
+        !aligned(dB, 16) || !aligned(workspace, 256))
+        return fail(-1, "misaligned pointer (16 B for arrays, 256 B for the workspace)");
+    if (d_in % 64 != 0 || d_out % 64 != 0) return fail(-2, "d_in and d_out must be multiples of 64");
+    if (d_in > INT32_MAX || d_out > INT32_MAX || d_seq > INT32_MAX) return fail(-2, "dimension too large");
+    if (2 * d_seq * (d_out > d_in ? d_out : d_in) >= (int64_t{1} << 32)) return fail(-2, "an operand reaches 4 GiB");
+    const GradWs gw = grad_ws(d_out, d_in, d_seq, r);
+    if (workspace_bytes < gw.bytes) return fail(-3, "workspace too small");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* tp = reinterpret_cast<uint16_t*>(ws + gw.tp);
+    uint16_t* up = reinterpret_cast<uint16_t*>(ws + gw.up);
+    uint16_t* bt = reinterpret_cast<uint16_t*>(ws + gw.bt);
+    float* part = reinterpret_cast<float*>(ws + gw.part);
+    hipError_t e;
+    // T' = bf16(s X A^T): the forward's pre-pass, without the dequantisation
+    if ((e = qn::launch_prologue(nullptr, nullptr, nullptr, nullptr, d_out, d_in, false, nullptr, X, d_in, d_seq,
+                                 d_in, A, d_in, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) != hipSuccess)
+        return hip_fail(e, "qlora_lora_grads (X A^T)");
+    // U' = bf16(s dY B): the input gradient's pre-pass on B^T
+    if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
+        return hip_fail(e, "qlora_lora_grads (B^T)");
+    if ((e = qn::launch_prologue(nullptr, nullptr, nullptr, nullptr, d_out, d_in, false, nullptr, dY, d_out,
+                                 d_seq, d_out, bt, d_out, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) !=
+        hipSuccess)
+        return hip_fail(e, "qlora_lora_grads (dY B)");
+    if ((e = qn::launch_lora_grads(X, dY, tp, up, d_out, d_in, d_seq, r, gw.r_pad, part, dA, dB, st)) != hipSuccess)
+        return hip_fail(e, "qlora_lora_grads (reduction)");
+    return 0;
+}
+
 }  // extern "C"

@@ -910,7 +910,9 @@ hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const flo
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
     a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
-    a.n_deq = static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64) : (n + kDeqPerWG - 1) / kDeqPerWG);
+    a.n_deq = what == nullptr ? 0   // pre-pass (and adapter layout) only
+                              : static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64)
+                                                            : (n + kDeqPerWG - 1) / kDeqPerWG);
     const int NT = (r + 31) / 32;
     static_assert(64 + 512 + 64 * kTP * sizeof(uint16_t) <= sizeof(g_pre1), "dequant scratch fits a ring slot");
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));

@@ -54,7 +54,8 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
 //   OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T) (zero in columns r..r_pad-1, K % 64 == 0),
 // an adapter layout job (adapt_mode 1: B [arows, acols] -> [arows, r_pad] zero-padded;
 // 2: A [arows, acols] -> A^T [acols, r_pad] zero-padded; 0: none), and the double
-// dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed).
+// dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed; none if
+// what is null).
 hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                            const float* qmean, int64_t d_out, int64_t d_in, bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
@@ -70,5 +71,16 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const flo
                            const float* qmean, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st);
+
+// ---- lora_grads.hip ----
+// Column-sum partials of out[n, j] = sum_m P[m, n] T[m, j] for the two adapter
+// gradients, then their fixed-order sum:
+//   dB [d_out, r] = dY^T T'   (P = dY, T = T' = bf16(s X A^T))
+//   dA [r, d_in]  = U'^T X     (P = X,  T = U' = bf16(s dY B))
+// T' and U' are [d_seq, r_pad] bf16. part must hold lora_grads_partials(...) floats.
+int64_t lora_grads_partials(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+hipError_t launch_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* Tp, const uint16_t* Up,
+                             int64_t d_out, int64_t d_in, int64_t d_seq, int r, int r_pad,
+                             float* part, float* dA, float* dB, hipStream_t st);
 
 }  // namespace qn

@@ -138,6 +138,29 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
                        const uint16_t* dY, int64_t d_seq, uint16_t* dX,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Workspace bytes qlora_lora_grads needs (0 on bad sizes). */
+int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+
+/*
+ * qlora_lora_grads - gradients of the trainable adapter factors.
+ *   [P2 card 1: the 4-bit weight is frozen, gradients go to the LoRA adapters only;
+ *    P1 LoRA: y = W0 x + s B(A x); the formulas are the derivatives of that forward
+ *    with respect to A and B]
+ *   With T = X A^T and U = dY B ([d_seq, r]):
+ *     dA [r, d_in]  = s U^T X,     dB [d_out, r] = s dY^T T,
+ *   computed from the bf16 operands U' = bf16(s U) and T' = bf16(s T) (the same ones
+ *   the forward and input-gradient GEMMs consume), float32 accumulation, float32
+ *   outputs (overwritten). The quantised weight is not needed.
+ *   A [r, d_in], B [d_out, r], X [d_seq, d_in], dY [d_seq, d_out] bf16 (device);
+ *   dA, dB float32 (device).
+ *   Same shape rules as qlora_linear_fwd (d_in, d_out multiples of 64, 1 <= r <= 256,
+ *   d_seq >= 1). The result is deterministic (fixed summation order).
+ */
+int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s,
+                     const uint16_t* X, const uint16_t* dY, int64_t d_out, int64_t d_in,
+                     int64_t d_seq, float* dA, float* dB,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
 /*
  * Kernel timing, off by default. While enabled, the library brackets every kernel
  * it launches with a pair of HIP events recorded on that kernel's stream, so the

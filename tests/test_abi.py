@@ -82,6 +82,24 @@ def test_argument_validation_without_device_work():
     args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, 16, None, FAKE, 1 << 30, None]
     assert lib.qlora_linear_fwd(*args) == -1
     assert lib.nf4_double_dequant(FAKE, FAKE, FAKE, FAKE, 64, 64, None, None) == -1
+    # adapter gradients: A, B, r, s, X, dY, d_out, d_in, d_seq, dA, dB, ws, ws_bytes, stream
+    g = [FAKE, FAKE, 8, 2.0, FAKE, FAKE, 64, 64, 16, FAKE, FAKE, FAKE, 1 << 30, None]
+    g[0] = None
+    assert lib.qlora_lora_grads(*g) == -1                      # null pointer
+    g[0] = FAKE
+    g[7] = 96
+    assert lib.qlora_lora_grads(*g) == -2                      # d_in % 64 != 0
+    g[7] = 64
+    g[2] = 0
+    assert lib.qlora_lora_grads(*g) == -1                      # r < 1
+    g[2] = 8
+    g[9] = FAKE + 8
+    assert lib.qlora_lora_grads(*g) == -1                      # misaligned dA
+    g[9] = FAKE
+    g[12] = 16
+    assert lib.qlora_lora_grads(*g) == -3                      # workspace too small
+    assert lib.qlora_lora_grads_workspace_bytes(64, 64, 16, 0) == 0
+    assert lib.qlora_lora_grads_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 2 * 4096 * 64
 
 
 def test_codebook_null_pointer():
