@@ -45,7 +45,47 @@ def parse():
     ap.add_argument("--decode-iters", type=int, default=256)
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the prefill workload the CPU oracle runs (0 = skip the CPU baseline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run three plain 512 MiB device copies (the reference for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "gemm_nt_kernel_4096x4096x4160_traffic.md")
+GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_nf4_quantized_05_amd", "csrc",
+                           "gemm_nt.hip")
+
+
+def measured_traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None when the
+    GEMM source has changed since the counters were taken (the summary records the
+    SHA-256 of gemm_nt.hip it was measured with)."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src_hash = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not t or h.group(1) != src_hash:
+        return None
+    return int(t.group(1))
+
+
+def copy_calibration():
+    """Three plain copies of 512 MiB: each reads and writes exactly 2^29 bytes."""
+    import torch
+    n = 512 * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def decode_bytes(cfg) -> int:
@@ -91,6 +131,9 @@ def cpu_baseline(cfg, dcfg, tokens: int) -> dict:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
@@ -179,7 +222,7 @@ def main():
     achieved = gemm_flops / (g_ms / g_n * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "gemm_nt_kernel", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None}
+                "traffic": measured_traffic()}
 
     # ---- decode (d_seq = 1) over rotated layer copies
     log(f"[bench] decode: {args.decode_iters} calls over {len(copies)} copies")
@@ -208,6 +251,34 @@ def main():
                            "unit": "GB/s", "frac": round(nbytes / (kern_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                            "traffic": None}}
 
+    # ---- adapter gradients (dA, dB) of the same layer, outside the timed step
+    log(f"[bench] adapter gradients: {args.steps} calls")
+    gws = torch.empty(qn.lora_grads_workspace_bytes(cfg.d_out, cfg.d_in, cfg.d_seq, cfg.r), dtype=torch.uint8,
+                      device=dev)
+    gA = torch.empty(cfg.r, cfg.d_in, dtype=torch.float32, device=dev)
+    gB = torch.empty(cfg.d_out, cfg.r, dtype=torch.float32, device=dev)
+    for _ in range(2):
+        qn.lora_grads(A, B, cfg.s, X, dY, dA=gA, dB=gB, workspace=gws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        qn.lora_grads(A, B, cfg.s, X, dY, dA=gA, dB=gB, workspace=gws)
+    torch.cuda.synchronize()
+    g_elapsed = (time.perf_counter() - t0) / args.steps
+    qn.profile_enable(True)
+    for _ in range(args.steps):
+        qn.lora_grads(A, B, cfg.s, X, dY, dA=gA, dB=gB, workspace=gws)
+    torch.cuda.synchronize()
+    gprof = qn.profile_read()
+    qn.profile_enable(False)
+    # algorithmic bytes: one read of X and dY, A and B, the fp32 gradients written
+    g_bytes = 2 * cfg.d_seq * (cfg.d_in + cfg.d_out) + 2 * 2 * cfg.r * (cfg.d_in + cfg.d_out) + \
+        4 * cfg.r * (cfg.d_in + cfg.d_out)
+    lora_grads = {"metric": "adapter gradients dA, dB (effective GB/s)",
+                  "value": round(g_bytes / g_elapsed / 1e9, 1), "unit": "GB/s", "bytes_per_call": g_bytes,
+                  "call_us": round(1e6 * g_elapsed, 2),
+                  "kernel_us": {k: round(1e3 * ms / n, 2) for k, (n, ms) in sorted(gprof.items())}}
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -227,6 +298,7 @@ def main():
                    "decode_copies": len(copies)},
         "roofline": roofline,
         "decode": decode,
+        "lora_grads": lora_grads,
         "kernels": kernels,
         "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
     }

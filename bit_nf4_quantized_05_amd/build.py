@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlora_nf4.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm.hip", "lora_grads.hip", "tables.cpp"]
+SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "prologue.hip", "gemv.hip", "lora_grads.hip", "tables.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -40,7 +40,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]

@@ -1,6 +1,7 @@
 // extern "C" entry points of libqlora_nf4: argument checks, workspace layout and
-// kernel sequencing. Every step of the layer runs in the kernels of quantize.hip
-// and gemm.hip; this file does no arithmetic on the data.
+// kernel sequencing. Every step of the layer runs in the kernels of quantize.hip,
+// prologue.hip, gemm_nt.hip, gemv.hip and lora_grads.hip; this file does no
+// arithmetic on the data.
 #include <hip/hip_runtime.h>
 
 #include <atomic>

@@ -1,0 +1,292 @@
+// BF16 MFMA contractions of the QLoRA linear layer on gfx950.
+//
+// Forward (whoami-wesleyyou.top "LoRA": Y = W0 X + s B (A X)) and input gradient
+// (learn.ifs.name deck card 1: gradients flow through the dequantised BF16 weights)
+// are both written as an "NT" product of two K-contiguous operands,
+//     C[M, N] = P[M, K] Q[N, K]^T  (+ P2[M, K2] Q2[N, K2]^T),
+// with M = tokens. The rank-r LoRA branch is the second term, folded in as extra
+// K-steps of the same accumulators:
+//     forward : P = X,  Q = W_hat,    P2 = s (X A^T),   Q2 = B
+//     dX      : P = dY, Q = W_hat^T,  P2 = s (dY B),    Q2 = A^T
+// so it costs r extra K (1.6 % of the flops at r = 64, K = 4096).
+//
+// gemm_nt: 256x256 output tile per workgroup, 8 waves (two per SIMD, so one wave's
+// MFMAs cover the other's waits) in a 2x4 grid, each wave a 128x64 sub-tile of 4x2
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32). K-steps of 64 are double-buffered
+// in LDS (2 x 64 KB) and filled by buffer_load ... lds (direct to LDS, no staging
+// registers): a tile row is then 128 B, one whole cache line per row and load, which
+// halves the L2 requests per byte compared with 64-byte rows. Rows are stored with
+// their 16-byte chunks XOR-swizzled by ((row >> 1) & 7), which makes the 32-row
+// fragment reads (ds_read_b128) free of bank conflicts on the 64-bank LDS. The stage
+// barrier sits before the last k16 sub-step, so the next stage's first fragments are
+// read under the last MFMAs. Tiles are handed to the 8 XCDs in contiguous ranges so
+// each XCD's L2 sees a compact block of P and Q panels.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "mfma_device.h"
+#include "nf4_device.h"
+
+#include <algorithm>
+
+namespace qn {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Main NT GEMM
+// ---------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (2048)
+constexpr int kGroupM = 4;                     // tile rows per raster group
+
+// Two LDS stages as distinct objects, so the compiler can tell that reads of one
+// stage do not depend on in-flight direct-to-LDS loads into the other. Each holds
+// [P tile | Q tile] = 2 x 2048 chunks = 64 KB.
+__shared__ uint4 g_st0[2 * kChunks];
+__shared__ uint4 g_st1[2 * kChunks];
+
+// Scheduling hints: interleave `n` groups of (1 LDS read, 2 MFMA).
+#define QN_INTERLEAVE_DS_MFMA(n)                                  \
+    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {          \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        \
+    }
+
+struct GemmArgs {
+    const uint16_t* P; int64_t ldp;
+    const uint16_t* Q; int64_t ldq; int kt1;
+    const uint16_t* P2; int64_t ldp2;
+    const uint16_t* Q2; int64_t ldq2; int kt2;
+    uint16_t* C; int64_t ldc; int M, N, tiles_m, tiles_n;
+    uint32_t bytesP, bytesQ, bytesP2, bytesQ2;   // buffer extents for the load descriptors
+};
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+// Workgroup barrier without the memory fence __syncthreads() adds (which would wait
+// for every in-flight load, including the stages fetched ahead). The loads a barrier
+// certifies are waited for explicitly with QN_WAIT_VM before it; LDS has no cache.
+// The "memory" clobber keeps the compiler from moving memory accesses across it.
+#define QN_BARRIER() asm volatile("s_barrier" ::: "memory")
+
+// WM x WN waves; each wave owns a (256/WM) x (256/WN) sub-tile of 32x32 MFMA tiles.
+template <int WM, int WN>
+__device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
+    constexpr int NW = WM * WN;                 // waves
+    constexpr int NT = 64 * NW;                 // threads
+    constexpr int TM = BM / WM / 32;            // m sub-tiles per wave
+    constexpr int TN = BN / WN / 32;            // n sub-tiles per wave
+    constexpr int SEG = BM / NW / 8;            // 8-row load segments per wave and operand
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int M = g.M, N = g.N;
+
+    // ---- tile assignment: contiguous logical ranges per XCD, grouped raster
+    const int T = g.tiles_m * g.tiles_n;
+    const int w = blockIdx.x;
+    const int logical = (T % 8 == 0) ? (w & 7) * (T >> 3) + (w >> 3) : w;
+    const int gsize = kGroupM * g.tiles_n;
+    const int grp = logical / gsize;
+    const int first_m = grp * kGroupM;
+    const int gm = min(g.tiles_m - first_m, kGroupM);
+    const int tm = first_m + (logical % gsize) % gm;
+    const int tn = (logical % gsize) / gm;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- global -> LDS with buffer_load ... lds (16 B per lane). A tile row is 64
+    // bf16 = 128 B = 8 chunks; chunk c of tile row r is stored at c ^ ((r >> 1) & 7).
+    // The LDS has 64 banks of 4 B, so two consecutive rows cover all banks once, and
+    // 16 lanes reading one logical chunk of 16 consecutive rows hit 16 distinct 4-bank
+    // groups. One load fills a 1 KB segment = 8 rows: lane i lands at row i/8,
+    // position i%8, so it fetches chunk (i%8) ^ ((r >> 1) & 7). Wave w fills rows
+    // 8*SEG*w .. of both operand tiles; the per-lane byte offsets are fixed for the
+    // whole K loop, the K position goes in the scalar offset.
+    // 128-B rows, chunk c of row r at c ^ ((r >> 1) & 7); segment j = 8 rows starting
+    // at 8 (SEG w + j): (r >> 1) & 7 = 4 ((SEG w + j) & 1) + i/16 for lane i.
+    const uint32_t kcE = static_cast<uint32_t>((lane & 7) ^ (lane >> 4)) * 16u;
+    const uint32_t kcO = static_cast<uint32_t>((lane & 7) ^ (4 | (lane >> 4))) * 16u;
+    uint32_t voP[SEG], voQ[SEG], voP2[SEG], voQ2[SEG];
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        const int rr = 8 * SEG * wave + 8 * j + (lane >> 3);
+        const uint32_t kc16 = (((SEG * wave + j) & 1) ? kcO : kcE);
+        const uint32_t rp = static_cast<uint32_t>(min(m0 + rr, M - 1));
+        const uint32_t rq = static_cast<uint32_t>(min(n0 + rr, N - 1));
+        voP[j] = rp * static_cast<uint32_t>(g.ldp * 2) + kc16;
+        voQ[j] = rq * static_cast<uint32_t>(g.ldq * 2) + kc16;
+        voP2[j] = rp * static_cast<uint32_t>(g.ldp2 * 2) + kc16;
+        voQ2[j] = rq * static_cast<uint32_t>(g.ldq2 * 2) + kc16;
+    }
+    const __amdgpu_buffer_rsrc_t rsP = make_rsrc(g.P, g.bytesP);
+    const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(g.Q, g.bytesQ);
+    const __amdgpu_buffer_rsrc_t rsP2 = make_rsrc(g.P2, g.bytesP2);
+    const __amdgpu_buffer_rsrc_t rsQ2 = make_rsrc(g.Q2, g.bytesQ2);
+    const int KT = g.kt1 + g.kt2;
+    constexpr int kLoadsPerStep = 2 * SEG;      // per wave
+
+#define QN_ISSUE(KTV, ST)                                                                         \
+    {                                                                                             \
+        const int kk_ = (KTV);                                                                    \
+        uint4* sp_ = (ST) + wave * (64 * SEG);                                                    \
+        uint4* sq_ = sp_ + kChunks;                                                               \
+        if (kk_ < g.kt1) {                                                                        \
+            const int so_ = kk_ * (BK * 2);                                                       \
+            _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)(sp_ + 64 * j), 16, voP[j], so_, 0, 0); \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(sq_ + 64 * j), 16, voQ[j], so_, 0, 0); \
+            }                                                                                     \
+        } else {                                                                                  \
+            const int so_ = (kk_ - g.kt1) * (BK * 2);                                             \
+            _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP2, (lds_ptr_t)(sp_ + 64 * j), 16, voP2[j], so_, 0, 0); \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ2, (lds_ptr_t)(sq_ + 64 * j), 16, voQ2[j], so_, 0, 0); \
+            }                                                                                     \
+        }                                                                                         \
+    }
+
+    // ---- fragments: 32-row x 16-K reads per k16 sub-step kk (0..3)
+    const uint32_t frow = lane & 31;
+    const uint32_t fsw = (frow >> 1) & 7;
+    const uint32_t prow = (wm * (TM * 32) + frow) * 8;
+    const uint32_t qrow = kChunks + (wn * (TN * 32) + frow) * 8;
+    uint32_t chs[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) chs[kk] = (2 * kk + (lane >> 5)) ^ fsw;
+#define QN_FRAGS(ST, CH, F)                                             \
+    {                                                                   \
+        F[0] = (ST)[qrow + (CH)];                                       \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) F[TN + i] = (ST)[prow + i * 256 + (CH)]; \
+        _Pragma("unroll") for (int i = 1; i < TN; ++i) F[i] = (ST)[qrow + i * 256 + (CH)];      \
+    }
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b) acc[a][b] = f32x16{};
+#define QN_MFMAS(F)                                                            \
+    _Pragma("unroll") for (int a = 0; a < TN; ++a)                             \
+        _Pragma("unroll") for (int b = 0; b < TM; ++b)                         \
+            acc[a][b] = mfma32(F[a], F[TN + b], acc[a][b]);
+
+    uint4 fa[TM + TN], fb[TM + TN];
+    // One K-step on stage CUR (its kk = 0 fragments already in fa) while NXT receives
+    // step k+1; NXT last held step k-1, whose reads all finished before the previous
+    // step's barrier. Before the last sub-step every wave waits for its own loads and
+    // the barrier certifies NXT complete, so NXT's first fragments are read under the
+    // last MFMAs; CUR's reads are all done by then, so the next step may refill it.
+#define QN_STEP(KTV, CUR, NXT)                                                 \
+    {                                                                          \
+        const int k_ = (KTV);                                                  \
+        if (k_ + 1 < KT) QN_ISSUE(k_ + 1, NXT)                                 \
+        QN_FRAGS(CUR, chs[1], fb)                                              \
+        QN_MFMAS(fa)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+        QN_FRAGS(CUR, chs[2], fa)                                              \
+        QN_MFMAS(fb)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+        QN_FRAGS(CUR, chs[3], fb)                                              \
+        QN_MFMAS(fa)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+        __builtin_amdgcn_s_waitcnt(0);                                         \
+        QN_BARRIER();                                                          \
+        if (k_ + 1 < KT) QN_FRAGS(NXT, chs[0], fa)                             \
+        QN_MFMAS(fb)                                                           \
+        QN_INTERLEAVE_DS_MFMA((TM + TN));                                      \
+    }
+
+    QN_ISSUE(0, g_st0)
+    QN_WAIT_VM(0);
+    QN_BARRIER();
+    QN_FRAGS(g_st0, chs[0], fa)
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+        QN_STEP(kt, g_st0, g_st1)
+        QN_STEP(kt + 1, g_st1, g_st0)
+    }
+    if (kt < KT) QN_STEP(kt, g_st0, g_st1)
+#undef QN_STEP
+#undef QN_MFMAS
+#undef QN_FRAGS
+#undef QN_ISSUE
+
+    // ---- epilogue. Every wave is past the last barrier, so the LDS stages are free
+    // and no load is in flight. The bf16 C tile (256 rows x 512 B) goes to LDS: rows
+    // 128q .. 128q+127 in stage q (q = 0, 1), 16-byte chunk j of row r at position
+    // j ^ (r & 31) (two-pass, conflict-free 8-byte writes, conflict-free 16-byte
+    // reads); then each row leaves as 512 contiguous bytes, 16 B per lane.
+    // The lane holds C[m][n..n+3] for m = tile row frow + 32 b + 32 TM wm and
+    // n = 8 gq + 4 (lane >> 5) + 32 a + 32 TN wn.
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+        const int rl = wm * (TM * 32) + b * 32 + static_cast<int>(frow);
+        uint4* arr = (rl >> 7) ? g_st1 : g_st0;
+        char* rowp = reinterpret_cast<char*>(arr) + (rl & 127) * 512;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int nl = wn * (TN * 32) + a * 32 + 8 * gq + 4 * (lane >> 5);
+                uint2 o;
+                o.x = pack_bf16x2(acc[a][b][4 * gq + 0], acc[a][b][4 * gq + 1]);
+                o.y = pack_bf16x2(acc[a][b][4 * gq + 2], acc[a][b][4 * gq + 3]);
+                *reinterpret_cast<uint2*>(rowp + (((nl >> 3) ^ (rl & 31)) << 4) + ((nl & 7) << 1)) = o;
+            }
+        }
+    }
+    __syncthreads();
+    const int cj = tid & 31;                     // 16-byte chunk of the row
+    constexpr int kRowsPerPass = NT / 32;
+#pragma unroll
+    for (int i = 0; i < BM / kRowsPerPass; ++i) {
+        const int r = i * kRowsPerPass + (tid >> 5);
+        const uint4* arr = (r >> 7) ? g_st1 : g_st0;
+        const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(arr) + (r & 127) * 512 +
+                                                        ((cj ^ (r & 31)) << 4));
+        const int m = m0 + r;
+        const int n = n0 + cj * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(g.C + static_cast<int64_t>(m) * g.ldc + n) = v;
+    }
+}
+
+#ifndef QN_GEMM_WAVES_N
+#define QN_GEMM_WAVES_N 4
+#endif
+constexpr int kGemmWM = 2, kGemmWN = QN_GEMM_WAVES_N;
+
+__global__ __launch_bounds__(64 * kGemmWM * kGemmWN, 1)
+void gemm_nt_kernel(GemmArgs g) {
+    gemm_nt_body<kGemmWM, kGemmWN>(g);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
+                          const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
+                          int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                          hipStream_t st) {
+    GemmArgs g;
+    g.tiles_m = static_cast<int>((M + BM - 1) / BM);
+    g.tiles_n = static_cast<int>((N + BN - 1) / BN);
+    if (P2 == nullptr) { P2 = P; Q2 = Q; ldp2 = ldp; ldq2 = ldq; K2 = 0; }
+    g.P = P; g.ldp = ldp; g.Q = Q; g.ldq = ldq; g.kt1 = static_cast<int>(K1 / BK);
+    g.P2 = P2; g.ldp2 = ldp2; g.Q2 = Q2; g.ldq2 = ldq2; g.kt2 = static_cast<int>(K2 / BK);
+    g.C = C; g.ldc = ldc; g.M = static_cast<int>(M); g.N = static_cast<int>(N);
+    // every operand is < 4 GiB (checked by the caller): the extents fit 32 bits
+    g.bytesP = static_cast<uint32_t>(2 * ldp * M);
+    g.bytesQ = static_cast<uint32_t>(2 * ldq * N);
+    g.bytesP2 = static_cast<uint32_t>(2 * ldp2 * M);
+    g.bytesQ2 = static_cast<uint32_t>(2 * ldq2 * N);
+    QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(64 * kGemmWM * kGemmWN), 0,
+              st, g);
+    return hipGetLastError();
+}
+
+}  // namespace qn

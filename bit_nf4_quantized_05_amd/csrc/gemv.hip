@@ -1,0 +1,321 @@
+// d_seq = 1 forward (decode) of the QLoRA linear layer on gfx950: a streaming GEMV
+// over the packed NF4 codes with the rank-r LoRA term.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "mfma_device.h"
+#include "nf4_device.h"
+
+#include <algorithm>
+
+namespace qn {
+namespace {
+
+// ---------------------------------------------------------------------------
+// d_seq = 1 (decode), two launches:
+//   lora_ax_partial: the 64-column blocks of x are split into nparts contiguous
+//     slices (nparts * r <= 1024); workgroup w writes, for every rank row j, the dot
+//     product of A[j] and x over slice w to part[w][j] (fixed summation order).
+//   gemv_nf4: streams the packed codes once and adds B (s A x), summing the slice
+//     partials in a fixed order: y = W_hat x + B (s A x). Deterministic.
+// ---------------------------------------------------------------------------
+constexpr int kAxMaxParts = 16;
+
+__global__ __launch_bounds__(256)
+void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint16_t* __restrict__ x,
+                            int r, int blocks_per_part, float* __restrict__ part) {
+    __shared__ float red[256];
+    const int tid = threadIdx.x;
+    const int groups = 256 / r;                   // threads per rank row
+    const int nb64 = d_in / 64;
+    const int b_lo = blockIdx.x * blocks_per_part;
+    const int b_hi = min(b_lo + blocks_per_part, nb64);
+    float acc = 0.0f;
+    if (tid < groups * r) {
+        const int j = tid % r;
+        for (int b = b_lo + tid / r; b < b_hi; b += groups) {
+            const uint4* ar = reinterpret_cast<const uint4*>(A + static_cast<int64_t>(j) * d_in + b * 64);
+            const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * 64);
+            uint4 av[8], xv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { av[e] = ar[e]; xv[e] = xr[e]; }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                const uint32_t xw[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                          __builtin_bit_cast(bf16x2, xw[q]), acc, false);
+            }
+        }
+    }
+    red[tid] = acc;
+    __syncthreads();
+    if (tid < r) {
+        float t = 0.0f;
+        for (int g = 0; g < groups; ++g) t += red[g * r + tid];
+        part[static_cast<int64_t>(blockIdx.x) * r + tid] = t;
+    }
+}
+
+// gemv_nf4: a workgroup of 16 waves takes 16 consecutive rows, one per wave (four
+// waves per SIMD hide each other's latencies). A row is walked in segments of 4096
+// weights = 64 blocks; in a segment, lane l of a wave owns block l's constant and
+// two chunks of 2048 weights, in each the weights [32 l, 32 l + 32) = 16 code bytes
+// (one 16-byte load; the wave reads 1 KB contiguous), half of block 32 h + l/2.
+// The vector-memory address unit takes about as long for a 1-byte load as for a
+// 16-byte one, so everything but the codes is loaded once per workgroup with wide
+// loads by one wave each and passed through LDS: the x segment (waves 0..7), the
+// 16 rows' 8-bit constants (wave 8, when the rows' 64-block runs are 16-byte
+// aligned; else each wave loads its own), their group scales (wave 9), the A x
+// slice partials (waves 10..13) and the 16 rows of B (wave 14). Every wave issues
+// the loads it must wait for before its code loads, so that wait never covers the
+// codes, and the next segment's loads go out before the current one is computed.
+// A lane forms a_hat of block l and hands it to the two lanes owning the block's
+// halves by a cross-lane read. Each code byte (two weights) is looked up as a pair
+// of bf16 code values and dotted with the bf16 x pair (v_dot2_f32_bf16); a_hat
+// multiplies each half-block partial once (the constant factors out of the sum
+// over its block). The lookup table is replicated kLutCopies times with copy c in
+// bank c, so a half-wave never collides, and the x chunks are XOR-swizzled so the
+// 16-byte reads of 16 lanes hit 16 distinct bank groups. s (A x) is formed before
+// the weight loop, so each wave finishes on its own.
+constexpr int kGvWaves = 16;
+constexpr int kGvSeg = 4096;
+constexpr int kLutCopies = 32;
+
+struct GvRowSeg {
+    uint4 cw[2];            // code words of the two chunks
+    int8_t qv;              // constant of block l (only when each wave loads its own)
+    float sv;               // its group scale (idem)
+};
+
+struct GvStage {            // per-workgroup staging loads of one segment
+    uint4 v;                // x (waves 0..7) or constants (wave 8)
+    float sc;               // group scale (wave 9, lanes < 32)
+};
+
+__device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv, const uint32_t* lut,
+                                                 uint32_t lane_off) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    float part = 0.0f;
+#pragma unroll
+    for (int w4 = 0; w4 < 4; ++w4) {
+        const uint32_t xw[4] = {xv[w4].x, xv[w4].y, xv[w4].z, xv[w4].w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lut[byte * kLutCopies + lane_off]),
+                                                   __builtin_bit_cast(bf16x2, xw[b]), part, false);
+        }
+    }
+    return part;
+}
+
+// position of 16-byte x chunk c of a segment in LDS: lane l = (c >> 2) & 63 reads
+// chunks 4 l .. 4 l + 3; their order is XORed with bits 2..3 of l
+__device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c >> 4) & 3)); }
+
+template <bool kStageQ>
+__global__ __launch_bounds__(1024)
+void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__ qconst,
+                     const float* __restrict__ qscale, const float* __restrict__ qmean,
+                     int d_out, int d_in, const uint16_t* __restrict__ x,
+                     const uint16_t* __restrict__ B, int r, float s, const float* __restrict__ part,
+                     int nparts, uint16_t* __restrict__ y, NF4Tables tab) {
+    __shared__ uint4 lut4[256 * kLutCopies / 4];
+    __shared__ uint4 xs[2][kGvSeg / 8];
+    __shared__ uint4 qcs[2][kGvWaves * 64 / 16];      // row i's 64 constants at bytes 64 i ..
+    __shared__ float qss[2][2 * kGvWaves];            // row i: scales of groups base_i, base_i + 1
+    __shared__ float tvs[1024];
+    __shared__ uint4 bs[kGvWaves * 256 * 2 / 16];     // the 16 rows of B (r <= 256)
+    __shared__ float qlut[256];
+    __shared__ float s_t[256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave-uniform (a scalar), so the per-wave roles below are scalar branches and
+    // no wave waits on loads of a role it does not have
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row0 = blockIdx.x * kGvWaves;
+    const int row = min(row0 + wave, d_out - 1);
+    const int nbpr = d_in / 64;
+    const int upr = d_in / 32;                    // 16-byte code words per row
+    const int nseg = (d_in + kGvSeg - 1) / kGvSeg;
+    const int64_t n_b = static_cast<int64_t>(d_out) * nbpr;
+    const int64_t n_g = (n_b + 255) / 256;
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    const int64_t row_u = static_cast<int64_t>(row) * upr;
+
+    // first block of row i's run in segment S, and the first group it touches
+    auto run0 = [&](int i, int S) { return static_cast<int64_t>(min(row0 + i, d_out - 1)) * nbpr + S * 64; };
+    auto stage_issue = [&](GvStage& g, int S) {
+        if (wave < 8) {
+            const int col = S * kGvSeg + 8 * tid;
+            g.v = x4[min(col, d_in - 8) / 8];
+        } else if (kStageQ && wave == 8) {
+            // row lane/4, bytes 16 (lane%4) .. of its 64-block run (16-byte aligned);
+            // the tail of the last row is clamped into the array (those bytes are unused)
+            const int64_t b = min(run0(lane >> 2, S) + 16 * (lane & 3), n_b - 16);
+            g.v = *reinterpret_cast<const uint4*>(qconst + b);
+        } else if (wave == 9 && lane < 2 * kGvWaves) {
+            g.sc = qscale[min((run0(lane >> 1, S) >> 8) + (lane & 1), n_g - 1)];
+        }
+    };
+    auto stage_store = [&](const GvStage& g, int S) {
+        const int k = S & 1;
+        if (wave < 8) xs[k][gv_xpos(tid)] = S * kGvSeg + 8 * tid < d_in ? g.v : uint4{0, 0, 0, 0};
+        else if (kStageQ && wave == 8) qcs[k][lane] = g.v;
+        else if (wave == 9 && lane < 2 * kGvWaves) qss[k][lane] = g.sc;
+    };
+    auto seg_issue = [&](GvRowSeg& k, int S) {
+        if (!kStageQ) {
+            const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
+            k.qv = qconst[b];
+            k.sv = qscale[b >> 8];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = S * kGvSeg + h * 2048 + lane * 32;
+            k.cw[h] = codes[row_u + (col < d_in ? col / 32 : 0)];
+        }
+    };
+
+    // ---- loads: staged data first, then the codes
+    GvStage st;
+    st.v = uint4{0, 0, 0, 0};
+    st.sc = 0.0f;
+    stage_issue(st, 0);
+    const int nval = nparts * r;                  // <= 1024
+    uint4 tst = uint4{0, 0, 0, 0};
+    if (wave >= 10 && wave < 14)
+        tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nval + 3) / 4 - 1)];
+    const int nbv = 2 * r;                        // 16-byte pieces of the 16 rows of B
+    const uint4* b4 = reinterpret_cast<const uint4*>(B + static_cast<int64_t>(row0) * r);
+    uint4 bst[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bst[i] = uint4{0, 0, 0, 0};
+    if (wave == 14) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (64 * i < nbv) bst[i] = b4[min(lane + 64 * i, nbv - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    GvRowSeg g0, g1;
+    seg_issue(g0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- tables and staged data to LDS; the barriers wait for LDS writes only
+    if (tid < 256) {
+        // code-book values picked from the (scalar) kernel arguments by selects: an
+        // indexed read would be a memory load
+        float lo = tab.code[0], hi = tab.code[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            lo = (tid & 15) == i ? tab.code[i] : lo;
+            hi = (tid >> 4) == i ? tab.code[i] : hi;
+        }
+        const uint32_t v = pack_bf16x2(lo, hi);
+#pragma unroll
+        for (int c = 0; c < kLutCopies / 4; ++c) lut4[tid * (kLutCopies / 4) + c] = uint4{v, v, v, v};
+        qlut[tid] = static_cast<float>(tid - 128) / static_cast<float>(kInt8Step);
+    }
+    stage_store(st, 0);
+    if (wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
+    if (wave == 14) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (lane + 64 * i < nbv) bs[lane + 64 * i] = bst[i];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // s (A x), summed per rank row in slice order
+    if (tid < r) {
+        float t = 0.0f;
+        for (int p = 0; p < nparts; ++p) t += tvs[p * r + tid];
+        s_t[tid] = s * t;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const uint32_t* lut = reinterpret_cast<const uint32_t*>(lut4);
+    const uint32_t lane_off = static_cast<uint32_t>(lane & (kLutCopies - 1));
+    const float mu = qmean[0];
+    float acc = 0.0f;
+    auto compute = [&](const GvRowSeg& k, int S) {
+        const int kb = S & 1;
+        const int64_t b = static_cast<int64_t>(row) * nbpr + S * 64 + lane;
+        const bool bok = S * 64 + lane < nbpr;
+        int q;
+        float sc;
+        if (kStageQ) {
+            q = reinterpret_cast<const int8_t*>(qcs[kb])[wave * 64 + lane];
+            sc = qss[kb][2 * wave + static_cast<int>((b >> 8) - (run0(wave, S) >> 8))];
+        } else {
+            q = k.qv;
+            sc = k.sv;
+        }
+        const float ah = bok ? mu + sc * qlut[q + 128] : 0.0f;
+        const uint4* xb = xs[kb];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a = __shfl(ah, h * 32 + (lane >> 1));
+            uint4 xv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[e] = xb[h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
+            acc += a * gemv_half_block(k.cw[h], xv, lut, lane_off);
+        }
+    };
+    // segment S+1's loads go out before segment S is computed; its staged data is
+    // stored to the other LDS buffers after, behind a barrier
+    auto step = [&](GvRowSeg& cur, GvRowSeg& nxt, int S) {
+        const bool more = S + 1 < nseg;
+        if (more) {
+            stage_issue(st, S + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            seg_issue(nxt, S + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        compute(cur, S);
+        if (more) {
+            stage_store(st, S + 1);
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        }
+    };
+    for (int sg = 0; sg < nseg; sg += 2) {
+        step(g0, g1, sg);
+        if (sg + 1 < nseg) step(g1, g0, sg + 1);
+    }
+
+    // ---- rank-r term of this wave's row, row sum, store
+    const uint16_t* brow = reinterpret_cast<const uint16_t*>(bs) + wave * r;
+    for (int k = lane; k < r; k += 64) acc += bf16_to_f32(brow[k]) * s_t[k];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0 && row0 + wave < d_out) y[row0 + wave] = bf16_bits(acc);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                           const float* qmean, int64_t d_out, int64_t d_in,
+                           const uint16_t* A, const uint16_t* B, int r, float s,
+                           const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st) {
+    // slices of A x: at most 16, and nparts * r <= 1024 partials in all
+    const int nb64 = static_cast<int>(d_in / 64);
+    const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / r}));
+    const int per = (nb64 + want - 1) / want;
+    const int nparts = (nb64 + per - 1) / per;   // <= want
+    QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
+              static_cast<int>(d_in), x, r, per, ws_part);
+    const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
+    if ((d_in / 64) % 16 == 0) {
+        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<true>, grid, dim3(64 * kGvWaves), 0, st,
+                  reinterpret_cast<const uint4*>(codes), qconst, qscale, qmean, static_cast<int>(d_out),
+                  static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
+    } else {
+        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<false>, grid, dim3(64 * kGvWaves), 0, st,
+                  reinterpret_cast<const uint4*>(codes), qconst, qscale, qmean, static_cast<int>(d_out),
+                  static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
+    }
+    return hipGetLastError();
+}
+
+}  // namespace qn

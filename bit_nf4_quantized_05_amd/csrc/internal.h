@@ -43,13 +43,15 @@ hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
 hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                                const float* qmean, int64_t n, uint16_t* out, hipStream_t st);
 
-// ---- gemm.hip ----
+// ---- gemm_nt.hip ----
 // C[M,N] = bf16( P[M,K1] Q[N,K1]^T + P2[M,K2] Q2[N,K2]^T ), all row-major, K contiguous.
 // K1, K2 multiples of 64 (K2 may be 0); N multiple of 4.
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
                           int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
                           hipStream_t st);
+
+// ---- prologue.hip ----
 // One launch before the GEMM of a linear call: LoRA pre-pass
 //   OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T) (zero in columns r..r_pad-1, K % 64 == 0),
 // an adapter layout job (adapt_mode 1: B [arows, acols] -> [arows, r_pad] zero-padded;
@@ -65,6 +67,8 @@ hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const flo
 // dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);
+
+// ---- gemv.hip ----
 // y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes;
 // ws_part holds at most d_in/64 x r floats of partial A x sums.
 hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,

@@ -77,11 +77,16 @@ void lora_grad_partials(GradArgs g) {
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int j = 0; j < J; ++j) acc[c][j] = 0.0f;
+        // the P words of the next token pair are loaded before the current pair is used
+        uint32_t n0w = wm_lo < wm_hi ? pcol[static_cast<int64_t>(wm_lo) * pstride] : 0u;
+        uint32_t n1w = wm_lo + 1 < wm_hi ? pcol[static_cast<int64_t>(wm_lo + 1) * pstride] : 0u;
         for (int m = wm_lo; m < wm_hi; m += 2) {
             const bool two = m + 1 < wm_hi;
             const int m1 = two ? m + 1 : m;
-            const uint32_t p0 = pcol[static_cast<int64_t>(m) * pstride];
-            const uint32_t p1 = two ? pcol[static_cast<int64_t>(m1) * pstride] : 0u;
+            const uint32_t p0 = n0w;
+            const uint32_t p1 = two ? n1w : 0u;
+            n0w = m + 2 < wm_hi ? pcol[static_cast<int64_t>(m + 2) * pstride] : 0u;
+            n1w = m + 3 < wm_hi ? pcol[static_cast<int64_t>(m + 3) * pstride] : 0u;
             const uint32_t pc0 = (p0 & 0xFFFFu) | (p1 << 16);          // (P[m, c0], P[m+1, c0])
             const uint32_t pc1 = (p0 >> 16) | (p1 & 0xFFFF0000u);      // (P[m, c1], P[m+1, c1])
             const uint32_t* t0 = reinterpret_cast<const uint32_t*>(jb.T + static_cast<int64_t>(m) * g.r_pad + j0);
@@ -127,6 +132,7 @@ void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __re
     const int64_t nB = d_out * r;
     if (idx < nB) {                                   // dB[n, j], n = idx / r
         float v = 0.0f;
+#pragma unroll 8
         for (int s = 0; s < SB; ++s) v += partB[static_cast<int64_t>(s) * nB + idx];
         dB[idx] = v;
         return;
@@ -136,6 +142,7 @@ void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __re
     const int64_t j = k / d_in, n = k % d_in;
     const int64_t nA = d_in * r;
     float v = 0.0f;
+#pragma unroll 8
     for (int s = 0; s < SA; ++s) v += partA[static_cast<int64_t>(s) * nA + n * r + j];
     dA[k] = v;
 }
