@@ -59,7 +59,7 @@ QuantWs quant_ws(int64_t n_b) {
 }
 
 struct LinWs {
-    int64_t what, lora, adapt, adapt2, t, bytes;
+    int64_t what, lora, adapt, adapt2, t, part, bytes;
     int r_pad;
 };
 
@@ -72,6 +72,9 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.adapt = off;  off += align_up(2 * (d_out > d_in ? d_out : d_in) * w.r_pad, 256);  // B padded or A^T padded
     w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T
     w.t = off;      off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);  // GEMV: partial A x
+    w.part = off;                                                                // small batch: K-split partials
+    if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
+        off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * (d_out + w.r_pad), 256);
     w.bytes = off;
     return w;
 }
@@ -258,6 +261,15 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
         e = qn::launch_gemv_nf4(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, s, X, Y,
                                 reinterpret_cast<float*>(ws + lw.t), st);
         if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
+        return 0;
+    }
+    if (d_seq <= qn::kSkinnyMaxTokens) {
+        // few tokens: the codes streamed once, A x in the same launch
+        float* part = reinterpret_cast<float*>(ws + lw.part);
+        float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * d_out;
+        if ((e = qn::launch_skinny_nf4(codes, qconst, qscale, qmean, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
+                                       part, part_a, Y, st)) != hipSuccess)
+            return hip_fail(e, "qlora_linear_fwd (small batch)");
         return 0;
     }
     uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);

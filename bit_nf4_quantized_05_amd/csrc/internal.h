@@ -76,6 +76,18 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const flo
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st);
 
+// ---- skinny.hip ----
+// Small-batch forward, 2 <= d_seq <= 64: Y = dequant(W) X + bf16(s X A^T) B^T from the
+// packed codes, A x formed in the same launch. part must hold skinny_splits(d_in) *
+// d_seq * d_out floats, part_a skinny_splits(d_in) * d_seq * r_pad. d_out % 64 == 0,
+// d_in % 64 == 0.
+constexpr int kSkinnyMaxTokens = 64;
+int skinny_splits(int64_t d_in);
+hipError_t launch_skinny_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                             const float* qmean, int64_t d_out, int64_t d_in, const uint16_t* X, int64_t d_seq,
+                             const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
+                             float* part_a, uint16_t* Y, hipStream_t st);
+
 // ---- lora_grads.hip ----
 // Column-sum partials of out[n, j] = sum_m P[m, n] T[m, j] for the two adapter
 // gradients, then their fixed-order sum:

@@ -1,0 +1,290 @@
+// Small-batch forward of the QLoRA linear layer on gfx950 (2 <= d_seq <= 64 tokens).
+//
+// Y = dequant(W) X + s B (A X) (whoami-wesleyyou.top "LoRA"; "1. NF4": the 4-bit
+// weight is dequantised to BF16 for the product) with few tokens: the weight stream
+// (0.516 B per weight) dominates, so the packed codes are read once and dequantised
+// in registers straight into MFMA operands; nothing is written back but Y.
+//
+// skinny_nf4: a workgroup takes 64 rows of W (16 per wave) and K-slices of 8 blocks
+// (512 weights) s = split, split + splits, ...; the splits are summed by the second
+// kernel. ceil(r / 64) more row blocks take the rows of A instead (bf16, loaded as
+// they are), so the same launch also forms the K-split partials of A x. Per slice, the x slice of every token (zero past d_seq) is staged in LDS
+// with its 16-byte chunks XOR-swizzled by the token index, and a_hat of the 64 rows
+// x 8 blocks is formed once into LDS. Per 128-weight pair of blocks, lane l of a wave
+// (row i = l % 16, k-group g = l / 16) loads 16 code bytes = weights [128 p + 32 g,
+// +32) of its row (one 16-byte load; the k order inside the pair is permuted, and the
+// x fragments follow the same permutation), forms bf16(c[code] * a_hat) exactly as the
+// dequantiser does, and feeds v_mfma_f32_16x16x32_bf16 with one 16-token tile of x as
+// the other operand (up to 4 tiles).
+// skinny_reduce: per 16 rows, adds the split partials in order; forms T' = bf16(s A x)
+// from the A x partials (in split order, as the large-batch pre-pass rounds it) and
+// adds the rank-r term T' B^T (both staged in LDS); rounds to bf16.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+#include "nf4_device.h"
+
+#include <algorithm>
+
+namespace qn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSkRows = 64;         // rows of W per workgroup (16 per wave)
+constexpr int kSkBlk = 8;           // 64-weight blocks per K-slice
+constexpr int kSkTok = 64;          // tokens at most
+constexpr int kSkSplits = 8;        // K-split partials at most
+
+struct SkArgs {
+    const uint8_t* codes; const int8_t* qconst; const float* qscale; const float* qmean;
+    int d_out, d_in, d_seq, splits, r, r_pad;
+    const uint16_t* X;              // [d_seq, d_in]
+    const uint16_t* A;              // [r, d_in]
+    float* part;                    // [splits][d_seq][d_out]
+    float* part_a;                  // [splits][d_seq][r_pad]
+};
+
+__device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+template <int TT>   // 16-token tiles
+__global__ __launch_bounds__(256)
+void skinny_nf4(SkArgs a, NF4Tables tab) {
+    __shared__ uint4 xs[kSkTok * kSkBlk * 8];      // [token][64 chunks of 8 weights], swizzled
+    __shared__ float s_code[16 * 64];              // code book, copy per lane (conflict-free lookups)
+    __shared__ float s_ahat[kSkRows * kSkBlk];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int row_blocks = a.d_out / kSkRows;
+    const int all_blocks = row_blocks + (a.r + kSkRows - 1) / kSkRows;
+    const int rb = static_cast<int>(blockIdx.x) % all_blocks;
+    const int sp = static_cast<int>(blockIdx.x) / all_blocks;
+    const bool lora = rb >= row_blocks;            // workgroup-uniform: rows of A
+    const int ra = (rb - row_blocks) * kSkRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 16 + (threadIdx.x & 15);
+    const int nb = a.d_in / 64;
+    const int nslices = (nb + kSkBlk - 1) / kSkBlk;
+    const int i = lane & 15;                       // row within the wave / token within a tile
+    const int g = lane >> 4;                       // k-group
+    const int o = lora ? 0 : rb * kSkRows + wave * 16 + i;
+    const int64_t row_u = static_cast<int64_t>(o) * (a.d_in / 32);   // 16-byte code words per row
+    const uint4* arow = reinterpret_cast<const uint4*>(a.A + static_cast<int64_t>(lora ? min(ra, a.r - 1) : 0) * a.d_in);
+    const bool aok = lora && ra < a.r;
+    const uint4* codes4 = reinterpret_cast<const uint4*>(a.codes);
+    const uint4* x4 = reinterpret_cast<const uint4*>(a.X);
+    const float mu = a.qmean[0];
+    {
+        // code book from the (scalar) kernel arguments by selects
+        for (int e = tid; e < 16 * 64; e += 256) {
+            const int c = e >> 6;
+            float v = tab.code[0];
+#pragma unroll
+            for (int q = 1; q < 16; ++q) v = c == q ? tab.code[q] : v;
+            s_code[e] = v;
+        }
+    }
+    f32x4 acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int sl = sp; sl < nslices; sl += a.splits) {
+        const int b0 = sl * kSkBlk;
+        const int nbk = min(kSkBlk, nb - b0);
+        // staging loads first (x chunks, block constants), then this wave's code words
+        constexpr int kXPer = TT * 16 * kSkBlk * 8 / 256;   // 16-byte x chunks per thread
+        uint4 xv[kXPer];
+#pragma unroll
+        for (int q = 0; q < kXPer; ++q) {
+            const int e = tid + 256 * q;
+            const int tok = e >> 6, c = e & 63;
+            const bool ok = tok < a.d_seq && c < nbk * 8;
+            xv[q] = ok ? x4[(static_cast<int64_t>(tok) * a.d_in + b0 * 64) / 8 + c] : uint4{0, 0, 0, 0};
+        }
+        int8_t qv[2] = {0, 0};
+        float sv[2] = {0.0f, 0.0f};
+        uint4 cw[kSkBlk / 2];
+        uint4 aw[kSkBlk / 2][4];
+        if (!lora) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int e = tid + 256 * q;        // (row e / 8, block e % 8) of the workgroup's rows
+                const int64_t blk = static_cast<int64_t>(rb * kSkRows + (e >> 3)) * nb + b0 + min(e & 7, nbk - 1);
+                qv[q] = a.qconst[blk];
+                sv[q] = a.qscale[blk >> 8];
+            }
+#pragma unroll
+            for (int p = 0; p < kSkBlk / 2; ++p) {
+                const int bl = 2 * p + (g >> 1);     // block of this lane's 32 weights
+                const int word = (b0 + min(bl, nbk - 1)) * 2 + (g & 1);   // clamped into the row
+                cw[p] = codes4[row_u + word];
+            }
+        } else {
+            // the same 32 k of a row of A, as 4 x 8 bf16 (clamped into the row)
+#pragma unroll
+            for (int p = 0; p < kSkBlk / 2; ++p) {
+                const int bl = 2 * p + (g >> 1);
+                const int64_t e0 = static_cast<int64_t>(b0 + min(bl, nbk - 1)) * 64 + 32 * (g & 1);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) aw[p][st] = arow[e0 / 8 + st];
+            }
+        }
+        __syncthreads();                             // the previous slice's readers are done
+#pragma unroll
+        for (int q = 0; q < kXPer; ++q) {
+            const int e = tid + 256 * q;
+            const int tok = e >> 6, c = e & 63;
+            xs[tok * 64 + (c ^ (tok & 15))] = xv[q];
+        }
+        if (!lora) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int e = tid + 256 * q;
+                s_ahat[e] = block_constant(qv[q], sv[q], mu);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < kSkBlk / 2; ++p) {
+            const int bl = 2 * p + (g >> 1);
+            if (2 * p >= nbk) break;                  // uniform: no block of this pair exists
+            const bool bok = bl < nbk;
+            const float ah = !lora && bok ? s_ahat[(wave * 16 + i) * kSkBlk + bl] : 0.0f;
+            const uint32_t words[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                uint4 af;
+                if (lora) {
+                    af = aok && bok ? aw[p][st] : uint4{0, 0, 0, 0};
+                } else {
+                    float w[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = s_code[((words[st] >> (4 * e)) & 0xFu) * 64 + lane] * ah;
+                    af = uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                               pack_bf16x2(w[6], w[7])};
+                }
+                // x chunk of the same 8 weights: 128 p + 32 g + 8 st
+                const int c = 16 * p + 4 * g + st;
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    const int tok = t * 16 + i;
+                    acc[t] = mfma16(af, xs[tok * 64 + (c ^ i)], acc[t]);
+                }
+            }
+        }
+    }
+    // D of a 16x16 tile: lane l holds rows 4 (l / 16) + v of column l % 16
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int tok = t * 16 + i;
+        if (tok < a.d_seq) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (lora) {
+                    const int j = (rb - row_blocks) * kSkRows + wave * 16 + 4 * g + v;
+                    if (j < a.r_pad) a.part_a[(static_cast<int64_t>(sp) * a.d_seq + tok) * a.r_pad + j] = acc[t][v];
+                } else {
+                    const int orow = rb * kSkRows + wave * 16 + 4 * g + v;
+                    a.part[(static_cast<int64_t>(sp) * a.d_seq + tok) * a.d_out + orow] = acc[t][v];
+                }
+            }
+        }
+    }
+}
+
+// Y[t, o] = bf16( sum_split part + sum_j T'[t, j] B[o, j] ) for kRdRows rows o per
+// workgroup, T'[t, j] = bf16(s * sum_split part_a). Thread tid takes the (token, row)
+// pairs tid + 256 q; the rank sums go through LDS in chunks of 64 rank entries (rows
+// of odd pitch, so a row of B and a row of T' fall in different banks).
+constexpr int kRdRows = 16;
+
+__global__ __launch_bounds__(256)
+void skinny_reduce(const float* __restrict__ part, const float* __restrict__ part_a, int splits, float s,
+                   int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y) {
+    constexpr int kJ = 64, kP = kJ + 1;
+    constexpr int kPairs = kSkTok * kRdRows / 256;   // pairs per thread at most
+    __shared__ float s_b[kRdRows * kP];
+    __shared__ float s_t[kSkTok * kP];
+    const int tid = threadIdx.x;
+    const int o0 = static_cast<int>(blockIdx.x) * kRdRows;
+    const int npairs = d_seq * kRdRows;
+    float acc[kPairs];
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+        const int e = tid + 256 * q;
+        float v = 0.0f;
+        if (e < npairs) {
+            const int64_t idx = static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows;
+            for (int sp = 0; sp < splits; ++sp) v += part[static_cast<int64_t>(sp) * d_seq * d_out + idx];
+        }
+        acc[q] = v;
+    }
+    for (int j0 = 0; j0 < r; j0 += kJ) {
+        const int nj = min(kJ, r - j0);
+        __syncthreads();
+        for (int e = tid; e < kRdRows * nj; e += 256) {
+            const int ro = e / nj, j = e % nj;
+            s_b[ro * kP + j] = __uint_as_float(static_cast<uint32_t>(B[static_cast<int64_t>(o0 + ro) * r + j0 + j]) << 16);
+        }
+        for (int e = tid; e < d_seq * nj; e += 256) {
+            const int t = e / nj, j = e % nj;
+            float v = 0.0f;
+            for (int sp = 0; sp < splits; ++sp)
+                v += part_a[(static_cast<int64_t>(sp) * d_seq + t) * r_pad + j0 + j];
+            s_t[t * kP + j] = __uint_as_float(static_cast<uint32_t>(bf16_bits(s * v)) << 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPairs; ++q) {
+            const int e = tid + 256 * q;
+            if (e < npairs) {
+                const int t = e / kRdRows, ro = e % kRdRows;
+                float l = 0.0f;
+                for (int j = 0; j < nj; ++j) l += s_t[t * kP + j] * s_b[ro * kP + j];
+                acc[q] += l;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) {
+        const int e = tid + 256 * q;
+        if (e < npairs) Y[static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows] = bf16_bits(acc[q]);
+    }
+}
+
+}  // namespace
+
+int skinny_splits(int64_t d_in) {
+    const int64_t nslices = (d_in / 64 + kSkBlk - 1) / kSkBlk;
+    return static_cast<int>(std::min<int64_t>(kSkSplits, nslices));
+}
+
+hipError_t launch_skinny_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                             const float* qmean, int64_t d_out, int64_t d_in, const uint16_t* X, int64_t d_seq,
+                             const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
+                             float* part_a, uint16_t* Y, hipStream_t st) {
+    SkArgs a;
+    a.codes = codes; a.qconst = qconst; a.qscale = qscale; a.qmean = qmean;
+    a.d_out = static_cast<int>(d_out); a.d_in = static_cast<int>(d_in); a.d_seq = static_cast<int>(d_seq);
+    a.splits = skinny_splits(d_in);
+    a.r = r; a.r_pad = r_pad;
+    a.X = X; a.A = A; a.part = part; a.part_a = part_a;
+    const int blocks = static_cast<int>(d_out / kSkRows) + (r + kSkRows - 1) / kSkRows;
+    const dim3 grid(static_cast<unsigned>(blocks * a.splits));
+    const NF4Tables& tab = tables();
+    switch ((d_seq + 15) / 16) {
+        case 1: QN_LAUNCH("skinny_nf4", st, skinny_nf4<1>, grid, dim3(256), 0, st, a, tab); break;
+        case 2: QN_LAUNCH("skinny_nf4", st, skinny_nf4<2>, grid, dim3(256), 0, st, a, tab); break;
+        case 3: QN_LAUNCH("skinny_nf4", st, skinny_nf4<3>, grid, dim3(256), 0, st, a, tab); break;
+        case 4: QN_LAUNCH("skinny_nf4", st, skinny_nf4<4>, grid, dim3(256), 0, st, a, tab); break;
+        default: return hipErrorInvalidValue;
+    }
+    QN_LAUNCH("skinny_reduce", st, skinny_reduce, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256), 0, st,
+              part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y);
+    return hipGetLastError();
+}
+
+}  // namespace qn

@@ -176,6 +176,34 @@ def test_linear_fwd_bwd_small(cfg):
     _fwd_bwd_full_check(cfg)
 
 
+# 2 <= d_seq <= 64 runs the small-batch kernel (codes streamed once, dequantised in
+# registers into 16x16x32 MFMAs): 1..4 token tiles, ragged token counts, K-slices
+# that end inside a block pair (d_in 4160: 65 blocks), several K-splits per
+# workgroup (d_in 11008: 22 slices over 8 splits), r up to 256.
+SMALL_BATCH = [
+    WL.custom("sb_2", 128, 256, 2, 8, s=2.0),
+    WL.custom("sb_15", 192, 4160, 15, 3, s=1.0),
+    WL.custom("sb_16", 256, 1024, 16, 16, s=2.0),
+    WL.custom("sb_17", 320, 512, 17, 64, s=0.5),
+    WL.custom("sb_33", 128, 11008, 33, 16, s=2.0, outlier_frac=0.01),
+    WL.custom("sb_48", 64, 2048, 48, 100, s=1.5),
+    WL.custom("sb_64", 512, 768, 64, 256, s=1.0),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_BATCH, ids=[c.name for c in SMALL_BATCH])
+def test_small_batch_forward(cfg):
+    _say(f"[small batch] {cfg.name} d_out={cfg.d_out} d_in={cfg.d_in} d_seq={cfg.d_seq} r={cfg.r}")
+    _fwd_bwd_full_check(cfg, check_bwd=False)
+
+
+def test_small_batch_forward_full_layer():
+    base = WL.CONFIGS["decode"]
+    cfg = WL.custom("decode_64tok", base.d_out, base.d_in, 64, base.r, s=base.s)
+    _say("[small batch] 4096x4096 d_seq=64 r=16")
+    _fwd_bwd_full_check(cfg, check_bwd=False)
+
+
 def test_identity_input_returns_dequantised_weight_exactly():
     cfg = WL.custom("eye", 192, 256, 256, 8)
     w, a, b = _layer(cfg)
