@@ -54,7 +54,7 @@ __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f3
 template <int TT>   // 16-token tiles
 __global__ __launch_bounds__(256)
 void skinny_nf4(SkArgs a, NF4Tables tab) {
-    __shared__ uint4 xs[kSkTok * kSkBlk * 8];      // [token][64 chunks of 8 weights], swizzled
+    __shared__ uint4 xs[TT * 16 * kSkBlk * 8];     // [token][64 chunks of 8 weights], swizzled
     __shared__ float s_code[16 * 64];              // code book, copy per lane (conflict-free lookups)
     __shared__ float s_ahat[kSkRows * kSkBlk];
     const int tid = threadIdx.x;
@@ -91,12 +91,9 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int sl = sp; sl < nslices; sl += a.splits) {
-        const int b0 = sl * kSkBlk;
-        const int nbk = min(kSkBlk, nb - b0);
-        // staging loads first (x chunks, block constants), then this wave's code words
-        constexpr int kXPer = TT * 16 * kSkBlk * 8 / 256;   // 16-byte x chunks per thread
-        uint4 xv[kXPer];
+    constexpr int kXPer = TT * 16 * kSkBlk * 8 / 256;   // 16-byte x chunks per thread
+    // x chunks of the slice (zero past d_seq and past the row), stored after a barrier
+    auto load_x = [&](uint4 (&xv)[kXPer], int b0, int nbk) {
 #pragma unroll
         for (int q = 0; q < kXPer; ++q) {
             const int e = tid + 256 * q;
@@ -104,11 +101,57 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             const bool ok = tok < a.d_seq && c < nbk * 8;
             xv[q] = ok ? x4[(static_cast<int64_t>(tok) * a.d_in + b0 * 64) / 8 + c] : uint4{0, 0, 0, 0};
         }
-        int8_t qv[2] = {0, 0};
-        float sv[2] = {0.0f, 0.0f};
-        uint4 cw[kSkBlk / 2];
-        uint4 aw[kSkBlk / 2][4];
-        if (!lora) {
+    };
+    auto store_x = [&](const uint4 (&xv)[kXPer]) {
+#pragma unroll
+        for (int q = 0; q < kXPer; ++q) {
+            const int e = tid + 256 * q;
+            const int tok = e >> 6, c = e & 63;
+            xs[tok * 64 + (c ^ (tok & 15))] = xv[q];
+        }
+    };
+    // one MFMA per token tile with the 8 weights [128 p + 32 g + 8 st, +8) of row i
+    auto mma = [&](const uint4& af, int p, int st) {
+        const int c = 16 * p + 4 * g + st;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[t] = mfma16(af, xs[(t * 16 + i) * 64 + (c ^ i)], acc[t]);
+    };
+
+    if (lora) {
+        // rows of A (workgroup-uniform branch): the 32 k of a lane as 4 x 8 bf16
+        for (int sl = sp; sl < nslices; sl += a.splits) {
+            const int b0 = sl * kSkBlk;
+            const int nbk = min(kSkBlk, nb - b0);
+            uint4 xv[kXPer];
+            load_x(xv, b0, nbk);
+            uint4 aw[kSkBlk / 2][4];
+#pragma unroll
+            for (int p = 0; p < kSkBlk / 2; ++p) {
+                const int bl = 2 * p + (g >> 1);
+                const int64_t e0 = static_cast<int64_t>(b0 + min(bl, nbk - 1)) * 64 + 32 * (g & 1);   // clamped
+#pragma unroll
+                for (int st = 0; st < 4; ++st) aw[p][st] = arow[e0 / 8 + st];
+            }
+            __syncthreads();                         // the previous slice's readers are done
+            store_x(xv);
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < kSkBlk / 2; ++p) {
+                if (2 * p >= nbk) break;
+                const bool ok = aok && 2 * p + (g >> 1) < nbk;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) mma(ok ? aw[p][st] : uint4{0, 0, 0, 0}, p, st);
+            }
+        }
+    } else {
+        for (int sl = sp; sl < nslices; sl += a.splits) {
+            const int b0 = sl * kSkBlk;
+            const int nbk = min(kSkBlk, nb - b0);
+            // staging loads first (x chunks, block constants), then this wave's code words
+            uint4 xv[kXPer];
+            load_x(xv, b0, nbk);
+            int8_t qv[2];
+            float sv[2];
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int e = tid + 256 * q;        // (row e / 8, block e % 8) of the workgroup's rows
@@ -116,62 +159,32 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
                 qv[q] = a.qconst[blk];
                 sv[q] = a.qscale[blk >> 8];
             }
+            uint4 cw[kSkBlk / 2];
 #pragma unroll
             for (int p = 0; p < kSkBlk / 2; ++p) {
                 const int bl = 2 * p + (g >> 1);     // block of this lane's 32 weights
                 const int word = (b0 + min(bl, nbk - 1)) * 2 + (g & 1);   // clamped into the row
                 cw[p] = codes4[row_u + word];
             }
-        } else {
-            // the same 32 k of a row of A, as 4 x 8 bf16 (clamped into the row)
+            __syncthreads();                         // the previous slice's readers are done
+            store_x(xv);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) s_ahat[tid + 256 * q] = block_constant(qv[q], sv[q], mu);
+            __syncthreads();
 #pragma unroll
             for (int p = 0; p < kSkBlk / 2; ++p) {
                 const int bl = 2 * p + (g >> 1);
-                const int64_t e0 = static_cast<int64_t>(b0 + min(bl, nbk - 1)) * 64 + 32 * (g & 1);
+                if (2 * p >= nbk) break;              // uniform: no block of this pair exists
+                const float ah = bl < nbk ? s_ahat[(wave * 16 + i) * kSkBlk + bl] : 0.0f;
+                const uint32_t words[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
 #pragma unroll
-                for (int st = 0; st < 4; ++st) aw[p][st] = arow[e0 / 8 + st];
-            }
-        }
-        __syncthreads();                             // the previous slice's readers are done
-#pragma unroll
-        for (int q = 0; q < kXPer; ++q) {
-            const int e = tid + 256 * q;
-            const int tok = e >> 6, c = e & 63;
-            xs[tok * 64 + (c ^ (tok & 15))] = xv[q];
-        }
-        if (!lora) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int e = tid + 256 * q;
-                s_ahat[e] = block_constant(qv[q], sv[q], mu);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int p = 0; p < kSkBlk / 2; ++p) {
-            const int bl = 2 * p + (g >> 1);
-            if (2 * p >= nbk) break;                  // uniform: no block of this pair exists
-            const bool bok = bl < nbk;
-            const float ah = !lora && bok ? s_ahat[(wave * 16 + i) * kSkBlk + bl] : 0.0f;
-            const uint32_t words[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                uint4 af;
-                if (lora) {
-                    af = aok && bok ? aw[p][st] : uint4{0, 0, 0, 0};
-                } else {
+                for (int st = 0; st < 4; ++st) {
                     float w[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) w[e] = s_code[((words[st] >> (4 * e)) & 0xFu) * 64 + lane] * ah;
-                    af = uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                               pack_bf16x2(w[6], w[7])};
-                }
-                // x chunk of the same 8 weights: 128 p + 32 g + 8 st
-                const int c = 16 * p + 4 * g + st;
-#pragma unroll
-                for (int t = 0; t < TT; ++t) {
-                    const int tok = t * 16 + i;
-                    acc[t] = mfma16(af, xs[tok * 64 + (c ^ i)], acc[t]);
+                    mma(uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                              pack_bf16x2(w[6], w[7])},
+                        p, st);
                 }
             }
         }
@@ -217,8 +230,14 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
         const int e = tid + 256 * q;
         float v = 0.0f;
         if (e < npairs) {
+            // all split loads issued before the ordered sum
             const int64_t idx = static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows;
-            for (int sp = 0; sp < splits; ++sp) v += part[static_cast<int64_t>(sp) * d_seq * d_out + idx];
+            float pv[kSkSplits];
+#pragma unroll
+            for (int sp = 0; sp < kSkSplits; ++sp)
+                pv[sp] = sp < splits ? part[static_cast<int64_t>(sp) * d_seq * d_out + idx] : 0.0f;
+#pragma unroll
+            for (int sp = 0; sp < kSkSplits; ++sp) v += pv[sp];
         }
         acc[q] = v;
     }
@@ -231,9 +250,13 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
         }
         for (int e = tid; e < d_seq * nj; e += 256) {
             const int t = e / nj, j = e % nj;
+            float pv[kSkSplits];
+#pragma unroll
+            for (int sp = 0; sp < kSkSplits; ++sp)
+                pv[sp] = sp < splits ? part_a[(static_cast<int64_t>(sp) * d_seq + t) * r_pad + j0 + j] : 0.0f;
             float v = 0.0f;
-            for (int sp = 0; sp < splits; ++sp)
-                v += part_a[(static_cast<int64_t>(sp) * d_seq + t) * r_pad + j0 + j];
+#pragma unroll
+            for (int sp = 0; sp < kSkSplits; ++sp) v += pv[sp];
             s_t[t * kP + j] = __uint_as_float(static_cast<uint32_t>(bf16_bits(s * v)) << 16);
         }
         __syncthreads();
