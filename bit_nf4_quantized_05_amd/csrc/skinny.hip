@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
+#include "mfma_device.h"
 #include "nf4_device.h"
 
 #include <algorithm>
@@ -29,7 +30,6 @@
 namespace qn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSkRows = 64;         // rows of W per workgroup (16 per wave)
@@ -49,6 +49,14 @@ struct SkArgs {
 __device__ __forceinline__ f32x4 mfma16(const uint4& a, const uint4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
+}
+
+// one MFMA per token tile: the lane's 8 weights (x chunk c) of row i against token i
+// of each tile
+template <int TT>
+__device__ __forceinline__ void mma(f32x4 (&acc)[TT], const uint4* xs, const uint4& af, int c, int i) {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[t] = mfma16(af, xs[(t * 16 + i) * 64 + (c ^ i)], acc[t]);
 }
 
 template <int TT>   // 16-token tiles
@@ -91,39 +99,29 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    constexpr int kXPer = TT * 16 * kSkBlk * 8 / 256;   // 16-byte x chunks per thread
-    // x chunks of the slice (zero past d_seq and past the row), stored after a barrier
-    auto load_x = [&](uint4 (&xv)[kXPer], int b0, int nbk) {
+    // x of a K-slice into LDS as [token][64 chunks of 8 weights], the chunk index
+    // XOR-swizzled by the token: straight from global memory (no registers), one token
+    // row of 1 KB per wave instruction, lane l writing slot l = chunk l ^ (token % 16).
+    // The addresses are clamped into X: a token past d_seq only feeds an output column
+    // that is never stored, a chunk past the row meets zero weights.
+    constexpr int kXRows = TT * 16 / 4;            // token rows per wave
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto stage_x = [&](int b0, int nbk) {
 #pragma unroll
-        for (int q = 0; q < kXPer; ++q) {
-            const int e = tid + 256 * q;
-            const int tok = e >> 6, c = e & 63;
-            const bool ok = tok < a.d_seq && c < nbk * 8;
-            xv[q] = ok ? x4[(static_cast<int64_t>(tok) * a.d_in + b0 * 64) / 8 + c] : uint4{0, 0, 0, 0};
+        for (int j = 0; j < kXRows; ++j) {
+            const int tok = wv + 4 * j;
+            const int c = min(lane ^ (tok & 15), nbk * 8 - 1);
+            load_lds16(x4 + (static_cast<int64_t>(min(tok, a.d_seq - 1)) * a.d_in + b0 * 64) / 8 + c, xs + tok * 64);
         }
+        __builtin_amdgcn_sched_barrier(0);         // the row loads go out before the loads that follow
     };
-    auto store_x = [&](const uint4 (&xv)[kXPer]) {
-#pragma unroll
-        for (int q = 0; q < kXPer; ++q) {
-            const int e = tid + 256 * q;
-            const int tok = e >> 6, c = e & 63;
-            xs[tok * 64 + (c ^ (tok & 15))] = xv[q];
-        }
-    };
-    // one MFMA per token tile with the 8 weights [128 p + 32 g + 8 st, +8) of row i
-    auto mma = [&](const uint4& af, int p, int st) {
-        const int c = 16 * p + 4 * g + st;
-#pragma unroll
-        for (int t = 0; t < TT; ++t) acc[t] = mfma16(af, xs[(t * 16 + i) * 64 + (c ^ i)], acc[t]);
-    };
-
     if (lora) {
         // rows of A (workgroup-uniform branch): the 32 k of a lane as 4 x 8 bf16
         for (int sl = sp; sl < nslices; sl += a.splits) {
             const int b0 = sl * kSkBlk;
             const int nbk = min(kSkBlk, nb - b0);
-            uint4 xv[kXPer];
-            load_x(xv, b0, nbk);
+            __syncthreads();                         // the previous slice's readers are done
+            stage_x(b0, nbk);
             uint4 aw[kSkBlk / 2][4];
 #pragma unroll
             for (int p = 0; p < kSkBlk / 2; ++p) {
@@ -132,24 +130,23 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 #pragma unroll
                 for (int st = 0; st < 4; ++st) aw[p][st] = arow[e0 / 8 + st];
             }
-            __syncthreads();                         // the previous slice's readers are done
-            store_x(xv);
+            QN_WAIT_VM(kSkBlk * 2);                  // this wave's x rows have landed (A words may be in flight)
             __syncthreads();
 #pragma unroll
             for (int p = 0; p < kSkBlk / 2; ++p) {
                 if (2 * p >= nbk) break;
                 const bool ok = aok && 2 * p + (g >> 1) < nbk;
 #pragma unroll
-                for (int st = 0; st < 4; ++st) mma(ok ? aw[p][st] : uint4{0, 0, 0, 0}, p, st);
+                for (int st = 0; st < 4; ++st) mma<TT>(acc, xs, ok ? aw[p][st] : uint4{0, 0, 0, 0}, 16 * p + 4 * g + st, i);
             }
         }
     } else {
         for (int sl = sp; sl < nslices; sl += a.splits) {
             const int b0 = sl * kSkBlk;
             const int nbk = min(kSkBlk, nb - b0);
-            // staging loads first (x chunks, block constants), then this wave's code words
-            uint4 xv[kXPer];
-            load_x(xv, b0, nbk);
+            // x rows and block constants first, then this wave's code words
+            __syncthreads();                         // the previous slice's readers are done
+            stage_x(b0, nbk);
             int8_t qv[2];
             float sv[2];
 #pragma unroll
@@ -166,8 +163,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
                 const int word = (b0 + min(bl, nbk - 1)) * 2 + (g & 1);   // clamped into the row
                 cw[p] = codes4[row_u + word];
             }
-            __syncthreads();                         // the previous slice's readers are done
-            store_x(xv);
+            QN_WAIT_VM(kSkBlk / 2);                  // x rows and block constants in (code words may not be)
 #pragma unroll
             for (int q = 0; q < 2; ++q) s_ahat[tid + 256 * q] = block_constant(qv[q], sv[q], mu);
             __syncthreads();
@@ -182,9 +178,10 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
                     float w[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) w[e] = s_code[((words[st] >> (4 * e)) & 0xFu) * 64 + lane] * ah;
-                    mma(uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
-                              pack_bf16x2(w[6], w[7])},
-                        p, st);
+                    mma<TT>(acc, xs,
+                            uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                                  pack_bf16x2(w[6], w[7])},
+                            16 * p + 4 * g + st, i);
                 }
             }
         }
