@@ -24,6 +24,11 @@ Readings taken where the pages are silent (each is listed with its reason in
 the design notes): code-book probability offset, nearest-code tie rule, nibble
 order, the mean of the block constants rounded exactly, symmetric INT8 with step
 127 for the second level, and the separate multiply-then-add reconstruction.
+
+Second-level formats: "int8" (the default above); "fp8", the "8-bit floats" of
+[P2 card 4] taken as OCP FP8 E4M3 codes of r * 448 (448 is the largest finite
+E4M3 magnitude, as 127 is for INT8); "none", no second level: the float32 a_j is
+stored per block (the 4.5 bit/param layout of [P1 2. DQ]).
 """
 from __future__ import annotations
 
@@ -35,6 +40,8 @@ import numpy as np
 BLOCK = 64        # weights per first-level block [P1 DQ section; P4 DQ example]
 DQ_GROUP = 256    # first-level constants per second-level block [P2 card 4; P4 DQ example]
 INT8_STEP = 127   # largest INT8 code magnitude (symmetric absmax INT8, [P4 量化原理])
+E4M3_MAX = 448    # largest finite OCP FP8 E4M3 magnitude (1.75 * 2^8)
+DQ_FORMATS = ("int8", "fp8", "none")
 
 
 # --------------------------------------------------------------------------
@@ -185,13 +192,65 @@ def exact_mean_f32(a: np.ndarray) -> np.float32:
     return f32_from_rational(total, a.size << 149)
 
 
-def dq_encode(a: np.ndarray, mu: np.float32, group: int = DQ_GROUP):
-    """INT8 codes of the centred constants, one fp32 scale per group of 256.
+def e4m3_values() -> np.ndarray:
+    """The 256 OCP FP8 E4M3 codes as float64 values, indexed by the code byte.
+
+    Bit 7 is the sign, bits 6..3 the exponent (bias 7), bits 2..0 the mantissa.
+    Exponent field 0 is subnormal: (m / 8) * 2^-6. Otherwise (1 + m / 8) * 2^(e - 7),
+    except that S.1111.111 is NaN (the format has no infinities)."""
+    out = np.empty(256, np.float64)
+    for u in range(256):
+        sign = -1.0 if u & 0x80 else 1.0
+        e, m = (u >> 3) & 0xF, u & 0x7
+        if e == 0xF and m == 0x7:
+            out[u] = np.nan
+        elif e == 0:
+            out[u] = sign * math.ldexp(m, -9)
+        else:
+            out[u] = sign * math.ldexp(8 + m, e - 10)
+    return out
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code (uint8) of each float32 v with |v| <= 448.
+
+    The magnitude goes to the nearest of the 127 finite non-negative values (codes
+    0x00..0x7E, ascending with the code); an exact tie goes to the even code. The
+    sign bit is v's sign bit (-0.0 -> 0x80). The midpoint test 2|v| vs lo + hi is
+    exact in float64 (both sides are sums of at most two short dyadic numbers)."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
+        raise ValueError("e4m3_encode expects |v| <= 448")
+    pos = e4m3_values()[:0x7F]
+    lo = np.clip(np.searchsorted(pos, a, side="right") - 1, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    two_a, mid2 = 2.0 * a, pos[lo] + pos[hi]
+    up = (two_a > mid2) | ((two_a == mid2) & (hi % 2 == 0))
+    code = np.where(up, hi, lo).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 7)
+
+
+def dq_step(qconst: np.ndarray, fmt: str) -> np.ndarray:
+    """r_hat = T[q] in float32: fl32(q / 127) for int8, fl32(e4m3(q) / 448) for fp8."""
+    if fmt == "int8":
+        q = np.asarray(qconst, dtype=np.int8).reshape(-1)
+        return (q.astype(np.float32) / np.float32(INT8_STEP)).astype(np.float32)
+    if fmt == "fp8":
+        u = np.asarray(qconst).reshape(-1).view(np.uint8)
+        val = e4m3_values()[u].astype(np.float32)          # exact: 4 significant bits
+        return (val / np.float32(E4M3_MAX)).astype(np.float32)
+    raise ValueError(fmt)
+
+
+def dq_encode(a: np.ndarray, mu: np.float32, group: int = DQ_GROUP, fmt: str = "int8"):
+    """8-bit codes of the centred constants, one fp32 scale per group of 256.
 
     d_j = fl32(a_j - mu); b_g = max |d_j| over the group (absmax, as for the
-    first level); r_j = fl32(d_j / b_g) in [-1, 1]; q_j = round-half-even of
-    fl32(r_j * 127). A group with b_g = 0 gets q = 0. Returns (q int8 [n_b],
-    b float32 [n_g])."""
+    first level); r_j = fl32(d_j / b_g) in [-1, 1]; then for int8 q_j = round-
+    half-even of fl32(r_j * 127), for fp8 q_j = the nearest E4M3 code of
+    fl32(r_j * 448). A group with b_g = 0 gets q = 0 (+0 in both formats).
+    Returns (q int8 [n_b] (fp8: the code bytes), b float32 [n_g])."""
     a = np.asarray(a, dtype=np.float32).reshape(-1)
     mu = np.float32(mu)
     d = (a - mu).astype(np.float32)
@@ -202,32 +261,52 @@ def dq_encode(a: np.ndarray, mu: np.float32, group: int = DQ_GROUP):
     bj = np.repeat(b, group)[: a.size]
     safe = np.where(bj > 0, bj, np.float32(1.0)).astype(np.float32)
     r = (d / safe).astype(np.float32)
-    q = np.rint((r * np.float32(INT8_STEP)).astype(np.float32))
-    q[bj == 0] = 0
-    return q.astype(np.int8), b
+    if fmt == "int8":
+        q = np.rint((r * np.float32(INT8_STEP)).astype(np.float32))
+        q[bj == 0] = 0
+        return q.astype(np.int8), b
+    if fmt == "fp8":
+        code = e4m3_encode((r * np.float32(E4M3_MAX)).astype(np.float32))
+        code[bj == 0] = 0
+        return code.view(np.int8), b
+    raise ValueError(fmt)
 
 
-def dq_decode(qconst: np.ndarray, qscale: np.ndarray, mu: np.float32, group: int = DQ_GROUP) -> np.ndarray:
-    """a_hat_j = fl32(mu + fl32(b_g * fl32(q_j / 127))), a separate multiply then add."""
-    q = np.asarray(qconst, dtype=np.int8).reshape(-1)
-    b = np.repeat(np.asarray(qscale, dtype=np.float32), group)[: q.size]
-    rhat = (q.astype(np.float32) / np.float32(INT8_STEP)).astype(np.float32)
+def dq_decode(qconst: np.ndarray, qscale: np.ndarray, mu: np.float32, group: int = DQ_GROUP,
+              fmt: str = "int8") -> np.ndarray:
+    """a_hat_j = fl32(mu + fl32(b_g * T[q_j])), a separate multiply then add; with
+    no second level ("none") a_hat_j is the stored a_j itself."""
+    if fmt == "none":
+        return np.asarray(qscale, dtype=np.float32).reshape(-1).copy()
+    rhat = dq_step(qconst, fmt)
+    b = np.repeat(np.asarray(qscale, dtype=np.float32), group)[: rhat.size]
     return (np.float32(mu) + (b * rhat).astype(np.float32)).astype(np.float32)
 
 
-def quantize(w: np.ndarray) -> dict:
-    """Full NF4 + DQ quantisation of a float32 weight matrix.
+def quantize(w: np.ndarray, dq: str = "int8") -> dict:
+    """Full NF4 quantisation of a float32 weight matrix, second level `dq`.
 
-    Returns codes (uint8, 32 bytes per block), qconst (int8 [n_b]),
-    qscale (float32 [n_g]), qmean (float32 [1]) and the first-level absmax
-    (float32 [n_b], not stored by the format, kept for checks)."""
+    Returns codes (uint8, 32 bytes per block), qconst (int8 [n_b]; empty for
+    "none"), qscale (float32 [n_g]; the a_j themselves [n_b] for "none"), qmean
+    (float32 [1]; 0 for "none", where it is not part of the format), the format
+    name and the first-level absmax (float32 [n_b], kept for checks)."""
+    if dq not in DQ_FORMATS:
+        raise ValueError(dq)
     blocks = to_blocks(w)
     a = block_absmax(blocks)
-    mu = exact_mean_f32(a)
-    qconst, qscale = dq_encode(a, mu)
     codes = pack_codes(block_codes(blocks, a))
+    if dq == "none":
+        return {"codes": codes, "qconst": np.zeros(0, np.int8), "qscale": a.copy(),
+                "qmean": np.zeros(1, np.float32), "absmax": a, "dq": dq}
+    mu = exact_mean_f32(a)
+    qconst, qscale = dq_encode(a, mu, fmt=dq)
     return {"codes": codes, "qconst": qconst, "qscale": qscale,
-            "qmean": np.array([mu], np.float32), "absmax": a}
+            "qmean": np.array([mu], np.float32), "absmax": a, "dq": dq}
+
+
+def block_constants(q: dict) -> np.ndarray:
+    """a_hat of every block of a quantize() result."""
+    return dq_decode(q["qconst"], q["qscale"], np.float32(q["qmean"][0]), fmt=q.get("dq", "int8"))
 
 
 def storage_bits_per_param(n: int, double_quant: bool = True) -> float:
@@ -260,10 +339,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def double_dequant(codes: np.ndarray, qconst: np.ndarray, qscale: np.ndarray,
-                   qmean, d_out: int, d_in: int) -> np.ndarray:
+                   qmean, d_out: int, d_in: int, dq: str = "int8") -> np.ndarray:
     """W_hat as bf16 bits [d_out, d_in]: w_hat = bf16(fl32(c[code] * a_hat_j))."""
     n = d_out * d_in
-    ahat = dq_decode(qconst, qscale, np.float32(np.asarray(qmean).reshape(-1)[0]))
+    ahat = dq_decode(qconst, qscale, np.float32(np.asarray(qmean).reshape(-1)[0]), fmt=dq)
     cb = codebook()
     vals = cb[unpack_codes(codes)[: ahat.size * BLOCK]].reshape(-1, BLOCK)
     prod = (vals * ahat[:, None]).astype(np.float32).reshape(-1)[:n]
@@ -275,7 +354,7 @@ def dequant_rows(q: dict, d_in: int, rows: np.ndarray) -> np.ndarray:
     if d_in % BLOCK:
         raise ValueError("row extraction needs whole blocks per row")
     per_row = d_in // BLOCK
-    ahat = dq_decode(q["qconst"], q["qscale"], np.float32(q["qmean"][0]))
+    ahat = block_constants(q)
     cb = codebook()
     out = np.empty((len(rows), d_in), np.uint16)
     codes = q["codes"].reshape(-1, BLOCK // 2)
