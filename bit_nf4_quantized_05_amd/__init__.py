@@ -2,6 +2,7 @@
 double dequantisation, fused forward, input gradient and adapter gradients, as
 hand-written HIP kernels behind the C ABI in include/qlora_nf4.h."""
 from ._lib import (  # noqa: F401
+    DQ_CODES,
     NF4Weight,
     QLoRAError,
     alloc_weight,

@@ -39,9 +39,19 @@ SIGNATURES = {
     "qlora_lora_grads_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
     "qlora_lora_grads": (_c_int, [_c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
                                   _c_vp, _c_i64, _c_vp]),
+    "qn_nf4_sizes_ex": (_c_int, [_c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp]),
+    "nf4_quantize_ex": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "nf4_double_dequant_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "qlora_linear_fwd_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
+                                     _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "qlora_linear_bwd_x_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
+                                       _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qn_profile_enable": (_c_int, [_c_int]),
     "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
 }
+
+# second-level formats: the QN_DQ_* codes of the header
+DQ_CODES = {"int8": 0, "fp8": 1, "none": 2}
 
 _lib = None
 
@@ -92,13 +102,18 @@ def _need(t: torch.Tensor, dtype, shape, name: str, device) -> None:
 
 @dataclass
 class NF4Weight:
-    """An NF4 + double-quantised weight as produced by ``quantize``."""
+    """An NF4 weight with its block constants as produced by ``quantize``.
+
+    dq names the second level: "int8" (default) or "fp8" (qconst holds E4M3 code
+    bytes), both with qscale [n_g] and qmean [1]; or "none", where qscale [n_b]
+    holds the float32 block absmax and qconst, qmean are empty."""
     codes: torch.Tensor    # uint8 [n_b * 32]
-    qconst: torch.Tensor   # int8 [n_b]
-    qscale: torch.Tensor   # float32 [n_g]
-    qmean: torch.Tensor    # float32 [1]
+    qconst: torch.Tensor   # int8 [n_b] (empty for "none")
+    qscale: torch.Tensor   # float32 [n_g] ([n_b] for "none")
+    qmean: torch.Tensor    # float32 [1] (empty for "none")
     d_out: int
     d_in: int
+    dq: str = "int8"
 
     @property
     def device(self) -> torch.device:
@@ -118,11 +133,18 @@ def codebook() -> list:
     return list(buf)
 
 
-def nf4_sizes(d_out: int, d_in: int):
-    cb, nb, ng = _c_i64(), _c_i64(), _c_i64()
-    _check(lib().qn_nf4_sizes(d_out, d_in, ctypes.addressof(cb), ctypes.addressof(nb), ctypes.addressof(ng)),
-           "qn_nf4_sizes")
-    return cb.value, nb.value, ng.value
+def _dq_code(dq: str) -> int:
+    if dq not in DQ_CODES:
+        raise ValueError(f"dq must be one of {sorted(DQ_CODES)}, got {dq!r}")
+    return DQ_CODES[dq]
+
+
+def nf4_sizes(d_out: int, d_in: int, dq: str = "int8"):
+    """(codes bytes, qconst entries, qscale entries) for format dq."""
+    cb, nq, ns = _c_i64(), _c_i64(), _c_i64()
+    _check(lib().qn_nf4_sizes_ex(d_out, d_in, _dq_code(dq), ctypes.addressof(cb), ctypes.addressof(nq),
+                                 ctypes.addressof(ns)), "qn_nf4_sizes_ex")
+    return cb.value, nq.value, ns.value
 
 
 def quantize_workspace_bytes(d_out: int, d_in: int) -> int:
@@ -133,36 +155,39 @@ def linear_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
     return lib().qlora_linear_workspace_bytes(d_out, d_in, d_seq, r)
 
 
-def alloc_weight(d_out: int, d_in: int, device) -> NF4Weight:
-    cb, nb, ng = nf4_sizes(d_out, d_in)
+def alloc_weight(d_out: int, d_in: int, device, dq: str = "int8") -> NF4Weight:
+    cb, nq, ns = nf4_sizes(d_out, d_in, dq)
     return NF4Weight(torch.empty(cb, dtype=torch.uint8, device=device),
-                     torch.empty(nb, dtype=torch.int8, device=device),
-                     torch.empty(ng, dtype=torch.float32, device=device),
-                     torch.empty(1, dtype=torch.float32, device=device), d_out, d_in)
+                     torch.empty(nq, dtype=torch.int8, device=device),
+                     torch.empty(ns, dtype=torch.float32, device=device),
+                     torch.empty(0 if dq == "none" else 1, dtype=torch.float32, device=device), d_out, d_in, dq)
 
 
-def quantize(W: torch.Tensor, out: NF4Weight | None = None, workspace: torch.Tensor | None = None) -> NF4Weight:
-    """nf4_quantize on a float32 [d_out, d_in] CUDA tensor."""
+def quantize(W: torch.Tensor, out: NF4Weight | None = None, workspace: torch.Tensor | None = None,
+             dq: str = "int8") -> NF4Weight:
+    """nf4_quantize_ex on a float32 [d_out, d_in] CUDA tensor, second level dq."""
     if W.dim() != 2:
         raise ValueError("W must be 2-D [d_out, d_in]")
     d_out, d_in = W.shape
     _need(W, torch.float32, (d_out, d_in), "W", W.device)
-    q = out if out is not None else alloc_weight(d_out, d_in, W.device)
+    q = out if out is not None else alloc_weight(d_out, d_in, W.device, dq)
+    if q.dq != dq:
+        raise ValueError(f"out holds format {q.dq!r}, asked for {dq!r}")
     need = quantize_workspace_bytes(d_out, d_in)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=W.device)
-    rc = lib().nf4_quantize(_ptr(W), d_out, d_in, _ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean),
-                            _ptr(ws), ws.numel() * ws.element_size(), _stream(W.device))
-    _check(rc, "nf4_quantize")
+    rc = lib().nf4_quantize_ex(_ptr(W), d_out, d_in, _dq_code(dq), _ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale),
+                               _ptr(q.qmean), _ptr(ws), ws.numel() * ws.element_size(), _stream(W.device))
+    _check(rc, "nf4_quantize_ex")
     return q
 
 
 def double_dequant(q: NF4Weight, out: torch.Tensor | None = None) -> torch.Tensor:
-    """nf4_double_dequant -> bfloat16 [d_out, d_in]."""
+    """nf4_double_dequant_ex -> bfloat16 [d_out, d_in]."""
     o = out if out is not None else torch.empty(q.d_out, q.d_in, dtype=torch.bfloat16, device=q.device)
     _need(o, torch.bfloat16, (q.d_out, q.d_in), "out", q.device)
-    rc = lib().nf4_double_dequant(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
-                                  _ptr(o), _stream(q.device))
-    _check(rc, "nf4_double_dequant")
+    rc = lib().nf4_double_dequant_ex(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
+                                     _dq_code(q.dq), _ptr(o), _stream(q.device))
+    _check(rc, "nf4_double_dequant_ex")
     return o
 
 
@@ -181,7 +206,7 @@ def _linear(fn_name: str, q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: flo
     need = linear_workspace_bytes(q.d_out, q.d_in, d_seq, r)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = getattr(lib(), fn_name)(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
-                                 _ptr(A), _ptr(B), r, float(s), _ptr(inp), d_seq, _ptr(o), _ptr(ws),
+                                 _dq_code(q.dq), _ptr(A), _ptr(B), r, float(s), _ptr(inp), d_seq, _ptr(o), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, fn_name)
     return o
@@ -190,13 +215,13 @@ def _linear(fn_name: str, q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: flo
 def linear_fwd(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """qlora_linear_fwd: Y [d_seq, d_out] = X W_hat^T + s (X A^T) B^T."""
-    return _linear("qlora_linear_fwd", q, A, B, s, X, q.d_in, q.d_out, out, workspace)
+    return _linear("qlora_linear_fwd_ex", q, A, B, s, X, q.d_in, q.d_out, out, workspace)
 
 
 def linear_bwd_x(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, dY: torch.Tensor,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """qlora_linear_bwd_x: dX [d_seq, d_in] = dY W_hat + s (dY B) A."""
-    return _linear("qlora_linear_bwd_x", q, A, B, s, dY, q.d_out, q.d_in, out, workspace)
+    return _linear("qlora_linear_bwd_x_ex", q, A, B, s, dY, q.d_out, q.d_in, out, workspace)
 
 
 def lora_grads_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:

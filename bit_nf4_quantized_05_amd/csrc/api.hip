@@ -1,7 +1,7 @@
 // extern "C" entry points of libqlora_nf4: argument checks, workspace layout and
 // kernel sequencing. Every step of the layer runs in the kernels of quantize.hip,
-// prologue.hip, gemm_nt.hip, gemv.hip and lora_grads.hip; this file does no
-// arithmetic on the data.
+// prologue.hip, gemm_nt.hip, gemv.hip, skinny.hip and lora_grads.hip; this file does
+// no arithmetic on the data.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -44,6 +44,27 @@ bool nf4_counts(int64_t d_out, int64_t d_in, int64_t* n, int64_t* n_b, int64_t* 
     return *n_b <= kMaxBlocks;
 }
 
+// The block-constant arrays of a quantised weight in format dq. Checks pointers and
+// alignment; for QN_DQ_NONE, qconst and qmean are not part of the format (may be
+// null) and readable stand-ins replace them, since kernels load them unconditionally.
+int make_consts(int dq, const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                qn::BlockConsts* bc) {
+    if (dq != QN_DQ_INT8 && dq != QN_DQ_FP8 && dq != QN_DQ_NONE) return fail(-1, "unknown second-level format");
+    if (!codes || !qscale) return fail(-1, "null pointer argument");
+    if (!aligned(qscale, 4)) return fail(-1, "misaligned pointer");
+    if (dq == QN_DQ_NONE) {
+        *bc = qn::BlockConsts{reinterpret_cast<const int8_t*>(codes), qscale, qscale, qn::kDqNone, 0};
+        return 0;
+    }
+    if (!qconst || !qmean) return fail(-1, "null pointer argument");
+    if (!aligned(qmean, 4)) return fail(-1, "misaligned pointer");
+    *bc = qn::BlockConsts{qconst, qscale, qmean, dq == QN_DQ_FP8 ? qn::kDqFp8 : qn::kDqInt8, 8};
+    return 0;
+}
+
+static_assert(QN_DQ_INT8 == qn::kDqInt8 && QN_DQ_FP8 == qn::kDqFp8 && QN_DQ_NONE == qn::kDqNone,
+              "format codes");
+
 struct QuantWs {
     int64_t absmax_off, limbs_off, bytes;
     int grid;
@@ -79,16 +100,16 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     return w;
 }
 
-int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean, int dq,
                  int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r,
                  const uint16_t* in, int64_t d_seq, uint16_t* out, void* ws, int64_t ws_bytes,
-                 LinWs* lw) {
-    if (!codes || !qconst || !qscale || !qmean || !A || !B || !in || !out || !ws)
-        return fail(-1, "null pointer argument");
+                 LinWs* lw, qn::BlockConsts* bc) {
+    if (int rc = make_consts(dq, codes, qconst, qscale, qmean, bc)) return rc;
+    if (!A || !B || !in || !out || !ws) return fail(-1, "null pointer argument");
     if (d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1");
     if (r < 1 || r > 256) return fail(-1, "r must be in [1, 256]");
     if (!aligned(codes, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(in, 16) ||
-        !aligned(out, 16) || !aligned(ws, 256) || !aligned(qscale, 4) || !aligned(qmean, 4))
+        !aligned(out, 16) || !aligned(ws, 256))
         return fail(-1, "misaligned pointer (16 B for arrays, 256 B for the workspace)");
     if (d_in % 64 != 0 || d_out % 64 != 0) return fail(-2, "d_in and d_out must be multiples of 64");
     if (d_in > INT32_MAX || d_out > INT32_MAX || d_seq > INT32_MAX) return fail(-2, "dimension too large");
@@ -149,6 +170,26 @@ void prof_end(void* token, const char* name, hipStream_t st) {
 }
 }  // namespace qn
 
+// workspace of qlora_lora_grads
+namespace {
+struct GradWs {
+    int64_t tp, up, bt, part, bytes;
+    int r_pad;
+};
+
+GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    GradWs w{};
+    w.r_pad = static_cast<int>(align_up(r, 64));
+    int64_t off = 0;
+    w.tp = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // T' = bf16(s X A^T)
+    w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
+    w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
+    w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
+    w.bytes = off;
+    return w;
+}
+}  // namespace
+
 extern "C" {
 
 int qn_profile_enable(int on) {
@@ -203,24 +244,35 @@ int qn_nf4_sizes(int64_t d_out, int64_t d_in, int64_t* codes_bytes, int64_t* n_b
     return 0;
 }
 
+int qn_nf4_sizes_ex(int64_t d_out, int64_t d_in, int dq, int64_t* codes_bytes, int64_t* qconst_entries,
+                    int64_t* qscale_entries) {
+    if (dq != QN_DQ_INT8 && dq != QN_DQ_FP8 && dq != QN_DQ_NONE) return fail(-1, "unknown second-level format");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
+    if (codes_bytes) *codes_bytes = n_b * (qn::kBlock / 2);
+    if (qconst_entries) *qconst_entries = dq == QN_DQ_NONE ? 0 : n_b;
+    if (qscale_entries) *qscale_entries = dq == QN_DQ_NONE ? n_b : n_g;
+    return 0;
+}
+
 int64_t nf4_quantize_workspace_bytes(int64_t d_out, int64_t d_in) {
     int64_t n, n_b, n_g;
     if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return 0;
     return quant_ws(n_b).bytes;
 }
 
-int nf4_quantize(const float* W, int64_t d_out, int64_t d_in, uint8_t* codes, int8_t* qconst,
-                 float* qscale, float* qmean, void* workspace, int64_t workspace_bytes, void* stream) {
-    if (!W || !codes || !qconst || !qscale || !qmean || !workspace) return fail(-1, "null pointer argument");
+int nf4_quantize_ex(const float* W, int64_t d_out, int64_t d_in, int dq, uint8_t* codes, int8_t* qconst,
+                    float* qscale, float* qmean, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!W || !workspace) return fail(-1, "null pointer argument");
+    qn::BlockConsts bc;
+    if (int rc = make_consts(dq, codes, qconst, qscale, qmean, &bc)) return rc;
     int64_t n, n_b, n_g;
     if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
-    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(workspace, 256) || !aligned(qscale, 4) ||
-        !aligned(qmean, 4))
-        return fail(-1, "misaligned pointer");
+    if (!aligned(W, 16) || !aligned(codes, 16) || !aligned(workspace, 256)) return fail(-1, "misaligned pointer");
     const QuantWs w = quant_ws(n_b);
     if (workspace_bytes < w.bytes) return fail(-3, "workspace too small");
     char* ws = static_cast<char*>(workspace);
-    hipError_t e = qn::launch_quantize(W, n, n_b, n_g, codes, qconst, qscale, qmean,
+    hipError_t e = qn::launch_quantize(W, n, n_b, n_g, bc.fmt, codes, qconst, qscale, qmean,
                                        reinterpret_cast<float*>(ws + w.absmax_off),
                                        reinterpret_cast<unsigned long long*>(ws + w.limbs_off), w.grid,
                                        static_cast<hipStream_t>(stream));
@@ -228,17 +280,28 @@ int nf4_quantize(const float* W, int64_t d_out, int64_t d_in, uint8_t* codes, in
     return 0;
 }
 
-int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
-                       int64_t d_out, int64_t d_in, uint16_t* W_bf16, void* stream) {
-    if (!codes || !qconst || !qscale || !qmean || !W_bf16) return fail(-1, "null pointer argument");
+int nf4_quantize(const float* W, int64_t d_out, int64_t d_in, uint8_t* codes, int8_t* qconst,
+                 float* qscale, float* qmean, void* workspace, int64_t workspace_bytes, void* stream) {
+    return nf4_quantize_ex(W, d_out, d_in, QN_DQ_INT8, codes, qconst, qscale, qmean, workspace, workspace_bytes,
+                           stream);
+}
+
+int nf4_double_dequant_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                          int64_t d_out, int64_t d_in, int dq, uint16_t* W_bf16, void* stream) {
+    qn::BlockConsts bc;
+    if (int rc = make_consts(dq, codes, qconst, qscale, qmean, &bc)) return rc;
+    if (!W_bf16) return fail(-1, "null pointer argument");
     int64_t n, n_b, n_g;
     if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-1, "bad weight shape");
-    if (!aligned(codes, 16) || !aligned(W_bf16, 16) || !aligned(qscale, 4) || !aligned(qmean, 4))
-        return fail(-1, "misaligned pointer");
-    hipError_t e = qn::launch_dequant_rows(codes, qconst, qscale, qmean, n, W_bf16,
-                                           static_cast<hipStream_t>(stream));
+    if (!aligned(codes, 16) || !aligned(W_bf16, 16)) return fail(-1, "misaligned pointer");
+    hipError_t e = qn::launch_dequant_rows(codes, bc, n, W_bf16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "nf4_double_dequant");
     return 0;
+}
+
+int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                       int64_t d_out, int64_t d_in, uint16_t* W_bf16, void* stream) {
+    return nf4_double_dequant_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, W_bf16, stream);
 }
 
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
@@ -246,19 +309,20 @@ int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq,
     return linear_ws(d_out, d_in, d_seq, r).bytes;
 }
 
-int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
-                     int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
-                     const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
-                     int64_t workspace_bytes, void* stream) {
+int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                        int64_t d_out, int64_t d_in, int dq, const uint16_t* A, const uint16_t* B, int r, float s,
+                        const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
     LinWs lw;
-    int rc = check_linear(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, X, d_seq, Y, workspace,
-                          workspace_bytes, &lw);
+    qn::BlockConsts bc;
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, X, d_seq, Y, workspace,
+                          workspace_bytes, &lw, &bc);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
     hipError_t e;
     if (d_seq == 1) {
-        e = qn::launch_gemv_nf4(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, s, X, Y,
+        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, Y,
                                 reinterpret_cast<float*>(ws + lw.t), st);
         if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
         return 0;
@@ -267,7 +331,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
         // few tokens: the codes streamed once, A x in the same launch
         float* part = reinterpret_cast<float*>(ws + lw.part);
         float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * d_out;
-        if ((e = qn::launch_skinny_nf4(codes, qconst, qscale, qmean, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
+        if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
                                        part, part_a, Y, st)) != hipSuccess)
             return hip_fail(e, "qlora_linear_fwd (small batch)");
         return 0;
@@ -277,7 +341,7 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
     uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
     const bool pad = r != lw.r_pad;
     // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
-    if ((e = qn::launch_prologue(codes, qconst, qscale, qmean, d_out, d_in, false, what, X, d_in, d_seq, d_in,
+    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
                                  A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
     if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
@@ -286,13 +350,22 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
     return 0;
 }
 
-int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
-                       int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
-                       const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
-                       int64_t workspace_bytes, void* stream) {
+int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                     int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
+                     const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+    return qlora_linear_fwd_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, X, d_seq, Y,
+                               workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                          int64_t d_out, int64_t d_in, int dq, const uint16_t* A, const uint16_t* B, int r,
+                          float s, const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
+                          int64_t workspace_bytes, void* stream) {
     LinWs lw;
-    int rc = check_linear(codes, qconst, qscale, qmean, d_out, d_in, A, B, r, dY, d_seq, dX, workspace,
-                          workspace_bytes, &lw);
+    qn::BlockConsts bc;
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, dY, d_seq, dX, workspace,
+                          workspace_bytes, &lw, &bc);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
@@ -305,7 +378,7 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
     if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (B^T)");
     // dequant W_hat^T + U = s (dY B) + A^T padded to r_pad columns, in one launch
-    if ((e = qn::launch_prologue(codes, qconst, qscale, qmean, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
+    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
                                  bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (prologue)");
     if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
@@ -314,25 +387,15 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
     return 0;
 }
 
-// ---- adapter gradients ----------------------------------------------------
-namespace {
-struct GradWs {
-    int64_t tp, up, bt, part, bytes;
-    int r_pad;
-};
-
-GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
-    GradWs w{};
-    w.r_pad = static_cast<int>(align_up(r, 64));
-    int64_t off = 0;
-    w.tp = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // T' = bf16(s X A^T)
-    w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
-    w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
-    w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
-    w.bytes = off;
-    return w;
+int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                       int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
+                       const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+    return qlora_linear_bwd_x_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, dY, d_seq, dX,
+                                 workspace, workspace_bytes, stream);
 }
-}  // namespace
+
+// ---- adapter gradients ----------------------------------------------------
 
 int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
@@ -361,13 +424,13 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const
     float* part = reinterpret_cast<float*>(ws + gw.part);
     hipError_t e;
     // T' = bf16(s X A^T): the forward's pre-pass, without the dequantisation
-    if ((e = qn::launch_prologue(nullptr, nullptr, nullptr, nullptr, d_out, d_in, false, nullptr, X, d_in, d_seq,
+    if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, X, d_in, d_seq,
                                  d_in, A, d_in, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (X A^T)");
     // U' = bf16(s dY B): the input gradient's pre-pass on B^T
     if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (B^T)");
-    if ((e = qn::launch_prologue(nullptr, nullptr, nullptr, nullptr, d_out, d_in, false, nullptr, dY, d_out,
+    if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, dY, d_out,
                                  d_seq, d_out, bt, d_out, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) !=
         hipSuccess)
         return hip_fail(e, "qlora_lora_grads (dY B)");

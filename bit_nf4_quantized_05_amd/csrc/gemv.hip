@@ -118,8 +118,7 @@ __device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c
 
 template <bool kStageQ>
 __global__ __launch_bounds__(1024)
-void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__ qconst,
-                     const float* __restrict__ qscale, const float* __restrict__ qmean,
+void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                      int d_out, int d_in, const uint16_t* __restrict__ x,
                      const uint16_t* __restrict__ B, int r, float s, const float* __restrict__ part,
                      int nparts, uint16_t* __restrict__ y, NF4Tables tab) {
@@ -156,9 +155,9 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
             // row lane/4, bytes 16 (lane%4) .. of its 64-block run (16-byte aligned);
             // the tail of the last row is clamped into the array (those bytes are unused)
             const int64_t b = min(run0(lane >> 2, S) + 16 * (lane & 3), n_b - 16);
-            g.v = *reinterpret_cast<const uint4*>(qconst + b);
+            g.v = *reinterpret_cast<const uint4*>(bc.q + b);
         } else if (wave == 9 && lane < 2 * kGvWaves) {
-            g.sc = qscale[min((run0(lane >> 1, S) >> 8) + (lane & 1), n_g - 1)];
+            g.sc = bc.scale[min((run0(lane >> 1, S) >> 8) + (lane & 1), n_g - 1)];
         }
     };
     auto stage_store = [&](const GvStage& g, int S) {
@@ -170,8 +169,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
     auto seg_issue = [&](GvRowSeg& k, int S) {
         if (!kStageQ) {
             const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
-            k.qv = qconst[b];
-            k.sv = qscale[b >> 8];
+            k.qv = bc.q[b];
+            k.sv = bc.scale[b >> bc.gshift];
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -217,7 +216,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
         const uint32_t v = pack_bf16x2(lo, hi);
 #pragma unroll
         for (int c = 0; c < kLutCopies / 4; ++c) lut4[tid * (kLutCopies / 4) + c] = uint4{v, v, v, v};
-        qlut[tid] = static_cast<float>(tid - 128) / static_cast<float>(kInt8Step);
+        qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));      // T[q] at q + 128
     }
     stage_store(st, 0);
     if (wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
@@ -237,7 +236,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
 
     const uint32_t* lut = reinterpret_cast<const uint32_t*>(lut4);
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kLutCopies - 1));
-    const float mu = qmean[0];
+    const float mu = bc.mean[0];
     float acc = 0.0f;
     auto compute = [&](const GvRowSeg& k, int S) {
         const int kb = S & 1;
@@ -252,7 +251,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
             q = k.qv;
             sc = k.sv;
         }
-        const float ah = bok ? mu + sc * qlut[q + 128] : 0.0f;
+        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? sc : mu + sc * qlut[q + 128];
         const uint4* xb = xs[kb];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -294,8 +293,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, const int8_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                           const float* qmean, int64_t d_out, int64_t d_in,
+hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st) {
     // slices of A x: at most 16, and nparts * r <= 1024 partials in all
@@ -306,13 +304,15 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const flo
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
     const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
-    if ((d_in / 64) % 16 == 0) {
+    // the staged variant takes each row's constants and group scales per segment,
+    // which needs groups of 256 blocks
+    if ((d_in / 64) % 16 == 0 && bc.gshift == 8) {
         QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<true>, grid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), qconst, qscale, qmean, static_cast<int>(d_out),
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out),
                   static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
     } else {
         QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<false>, grid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), qconst, qscale, qmean, static_cast<int>(d_out),
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out),
                   static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
     }
     return hipGetLastError();

@@ -8,7 +8,24 @@ namespace qn {
 constexpr int kBlock = 64;        // weights per NF4 block
 constexpr int kGroup = 256;       // block constants per double-quantisation group
 constexpr int kInt8Step = 127;    // symmetric INT8 code range [-127, 127]
+constexpr int kE4m3Max = 448;     // largest finite OCP FP8 E4M3 magnitude
 constexpr int kLimbs = 10;        // 32-bit limbs of the exact constant sum (covers 2^320)
+
+// Second-level (block constant) formats, the values of the C ABI's QN_DQ_* codes.
+constexpr int kDqInt8 = 0;        // q = round(r * 127), a_hat = mu + b (q / 127)
+constexpr int kDqFp8 = 1;         // q = E4M3 code of r * 448, a_hat = mu + b (e4m3(q) / 448)
+constexpr int kDqNone = 2;        // no second level: the float32 a_j per block
+
+// Where a kernel finds a_hat_j: from q[j], scale[j >> gshift] and mean[0]. For
+// kDqNone, scale holds a_j (gshift 0) and q, mean point at readable stand-ins whose
+// values are not used, so kernels may load them unconditionally.
+struct BlockConsts {
+    const int8_t* q;
+    const float* scale;
+    const float* mean;
+    int fmt;
+    int gshift;
+};
 constexpr int kCells = 32;        // [-1, 1] split into 32 equal cells for the code search
 
 // Constant tables, built once on the host and passed to kernels by value.
@@ -36,12 +53,13 @@ void prof_end(void* token, const char* name, hipStream_t st);
 
 // ---- quantize.hip ----
 int quant_grid(int64_t n_b);
-hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
+// fmt kDqNone writes the block constants to qscale [n_b] (qconst, qmean untouched).
+hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g, int fmt,
                            uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
                            float* ws_absmax, unsigned long long* ws_limbs, int grid,
                            hipStream_t st);
-hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                               const float* qmean, int64_t n, uint16_t* out, hipStream_t st);
+hipError_t launch_dequant_rows(const uint8_t* codes, const BlockConsts& bc, int64_t n, uint16_t* out,
+                               hipStream_t st);
 
 // ---- gemm_nt.hip ----
 // C[M,N] = bf16( P[M,K1] Q[N,K1]^T + P2[M,K2] Q2[N,K2]^T ), all row-major, K contiguous.
@@ -58,8 +76,8 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
 // 2: A [arows, acols] -> A^T [acols, r_pad] zero-padded; 0: none), and the double
 // dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed; none if
 // what is null).
-hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                           const float* qmean, int64_t d_out, int64_t d_in, bool transposed,
+hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
+                           bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
                            const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
                            int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
@@ -71,8 +89,7 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
 // ---- gemv.hip ----
 // y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes;
 // ws_part holds at most d_in/64 x r floats of partial A x sums.
-hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                           const float* qmean, int64_t d_out, int64_t d_in,
+hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st);
 
@@ -83,8 +100,8 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const int8_t* qconst, const flo
 // d_in % 64 == 0.
 constexpr int kSkinnyMaxTokens = 64;
 int skinny_splits(int64_t d_in);
-hipError_t launch_skinny_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                             const float* qmean, int64_t d_out, int64_t d_in, const uint16_t* X, int64_t d_seq,
+hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
+                             const uint16_t* X, int64_t d_seq,
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
                              float* part_a, uint16_t* Y, hipStream_t st);
 

@@ -6,10 +6,42 @@
 
 namespace qn {
 
-// a_hat = mu + b * (q / 127): separate float32 division, multiply and add.
-__device__ __forceinline__ float block_constant(int8_t q, float b, float mu) {
-    const float rhat = static_cast<float>(q) / static_cast<float>(kInt8Step);
-    const float prod = b * rhat;
+// Value of OCP FP8 E4M3 code byte u (sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; exponent 0 is subnormal, m * 2^-9). Exact in float32.
+__device__ __forceinline__ float e4m3_value(uint32_t u) {
+    const uint32_t e = (u >> 3) & 0xFu, m = u & 0x7u;
+    const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (u & 0x80u) ? -mag : mag;
+}
+
+// Nearest E4M3 code of v, |v| <= 448, ties to the even code; the sign bit is v's.
+// From 2^-6 up the float32 mantissa is rounded to 3 bits (nearest, even; a carry
+// moves into the exponent); below, the value is a multiple of 2^-9 rounded to
+// nearest even.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    uint32_t code;
+    if (mag >= 0x3C800000u) {
+        const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+    } else {
+        code = static_cast<uint32_t>(rintf(__uint_as_float(mag) * 512.0f));
+    }
+    return ((bits >> 24) & 0x80u) | code;
+}
+
+// r_hat = T[q]: q / 127 (INT8) or e4m3(q) / 448 (FP8), one float32 division.
+__device__ __forceinline__ float dq_step(int fmt, int8_t q) {
+    if (fmt == kDqFp8) return e4m3_value(static_cast<uint8_t>(q)) / static_cast<float>(kE4m3Max);
+    return static_cast<float>(q) / static_cast<float>(kInt8Step);
+}
+
+// a_hat = mu + b * r_hat (separate float32 multiply and add); with no second level
+// the stored constant itself.
+__device__ __forceinline__ float block_constant(int fmt, int8_t q, float b, float mu) {
+    if (fmt == kDqNone) return b;
+    const float prod = b * dq_step(fmt, q);
     return mu + prod;
 }
 

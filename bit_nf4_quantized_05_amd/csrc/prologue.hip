@@ -25,7 +25,7 @@ namespace {
 //                         (forward) or W_hat^T through a 64x64 LDS tile (dX).
 // ---------------------------------------------------------------------------
 struct PrologueArgs {
-    const uint8_t* codes; const int8_t* qconst; const float* qscale; const float* qmean;
+    const uint8_t* codes; BlockConsts bc;
     int64_t d_out, d_in;
     int transposed;                 // dequant to W_hat^T [d_in, d_out] instead of W_hat
     uint16_t* what;
@@ -225,7 +225,7 @@ __device__ __forceinline__ void dequant_rows_job(const PrologueArgs& a, int b, c
     for (int q = 0; q < kWords; ++q) cw[q] = codes32[min(w0 + 8 * (tid + 256 * q), n - 8) / 8];
     if (tid < kDeqPerWG / 64) {
         const int64_t blk = min(w0 / 64 + tid, n / 64 - 1);
-        s_ahat[tid] = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
+        s_ahat[tid] = block_constant(a.bc.fmt, a.bc.q[blk], a.bc.scale[blk >> a.bc.gshift], a.bc.mean[0]);
     }
     __syncthreads();
 #pragma unroll
@@ -258,7 +258,7 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
     const uint2 cw = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
     if (tid < 64) {
         const int64_t blk = (min(o0 + tid, a.d_out - 1) * a.d_in + i0) >> 6;
-        s_ahat[tid] = block_constant(a.qconst[blk], a.qscale[blk / kGroup], a.qmean[0]);
+        s_ahat[tid] = block_constant(a.bc.fmt, a.bc.q[blk], a.bc.scale[blk >> a.bc.gshift], a.bc.mean[0]);
     }
     __syncthreads();
     const float ahat = s_ahat[ol];
@@ -316,14 +316,14 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t r
 
 }  // namespace
 
-hipError_t launch_prologue(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                           const float* qmean, int64_t d_out, int64_t d_in, bool transposed,
+hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
+                           bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
                            const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
                            int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
                            int64_t acols, hipStream_t st) {
     PrologueArgs a;
-    a.codes = codes; a.qconst = qconst; a.qscale = qscale; a.qmean = qmean;
+    a.codes = codes; a.bc = bc;
     a.d_out = d_out; a.d_in = d_in; a.transposed = transposed ? 1 : 0; a.what = what;
     a.P = P; a.ldp = ldp; a.M = static_cast<int>(M); a.K = static_cast<int>(K);
     a.R = R; a.ldr = ldr; a.r = r; a.s = s; a.OUT = OUT; a.r_pad = r_pad;

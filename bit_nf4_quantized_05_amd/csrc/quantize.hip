@@ -212,7 +212,8 @@ constexpr int kDqGroups = kDqThreads / kGroup;
 
 __global__ __launch_bounds__(kDqThreads)
 void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned long long* __restrict__ limb_part,
-               int parts, float* __restrict__ qmean, int8_t* __restrict__ qconst, float* __restrict__ qscale) {
+               int parts, int fmt, float* __restrict__ qmean, int8_t* __restrict__ qconst,
+               float* __restrict__ qscale) {
     __shared__ unsigned long long s_col[kLimbs];
     __shared__ float s_mu;
     __shared__ uint32_t s_max[kDqThreads / 64];
@@ -258,7 +259,10 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned lon
         int8_t q = 0;
         if (mb != 0) {
             const float r = d / b;                                  // in [-1, 1]
-            q = static_cast<int8_t>(static_cast<int>(rintf(r * static_cast<float>(kInt8Step))));
+            if (fmt == kDqFp8)
+                q = static_cast<int8_t>(e4m3_encode(r * static_cast<float>(kE4m3Max)));
+            else
+                q = static_cast<int8_t>(static_cast<int>(rintf(r * static_cast<float>(kInt8Step))));
         }
         qconst[j] = q;
     }
@@ -270,8 +274,7 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned lon
 // Dequantisation, row-major: one thread per 8 consecutive weights.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads)
-void dequant_rows(const uint32_t* __restrict__ codes32, const int8_t* __restrict__ qconst,
-                  const float* __restrict__ qscale, const float* __restrict__ qmean, int64_t n,
+void dequant_rows(const uint32_t* __restrict__ codes32, BlockConsts bc, int64_t n,
                   uint16_t* __restrict__ out, NF4Tables tab) {
     __shared__ float s_code[16];
     if (threadIdx.x < 16) s_code[threadIdx.x] = tab.code[threadIdx.x];
@@ -280,7 +283,7 @@ void dequant_rows(const uint32_t* __restrict__ codes32, const int8_t* __restrict
     const int64_t e0 = t * 8;
     if (e0 >= n) return;
     const int64_t blk = t >> 3;
-    const float ahat = block_constant(qconst[blk], qscale[blk / kGroup], qmean[0]);
+    const float ahat = block_constant(bc.fmt, bc.q[blk], bc.scale[blk >> bc.gshift], bc.mean[0]);
     const uint32_t word = codes32[t];
     float w[8];
 #pragma unroll
@@ -307,25 +310,29 @@ int quant_grid(int64_t n_b) {
     return static_cast<int>(want < 256 ? (want < 1 ? 1 : want) : 256);
 }
 
-hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g,
+hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g, int fmt,
                            uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
                            float* ws_absmax, unsigned long long* ws_limbs, int grid,
                            hipStream_t st) {
     const NF4Tables& tab = tables();
+    // with no second level the block constants are the output itself
+    float* absmax = fmt == kDqNone ? qscale : ws_absmax;
     QN_LAUNCH("quant_blocks", st, quant_blocks, dim3(grid), dim3(kQuantThreads), 0, st, W, n, n_b,
-              reinterpret_cast<uint32_t*>(codes), ws_absmax, ws_limbs, tab);
-    const int64_t dq_grid = (n_g + kDqGroups - 1) / kDqGroups;
-    QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(dq_grid)), dim3(kDqThreads), 0, st,
-              ws_absmax, n_b, ws_limbs, grid, qmean, qconst, qscale);
+              reinterpret_cast<uint32_t*>(codes), absmax, ws_limbs, tab);
+    if (fmt != kDqNone) {
+        const int64_t dq_grid = (n_g + kDqGroups - 1) / kDqGroups;
+        QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(dq_grid)), dim3(kDqThreads), 0, st,
+                  ws_absmax, n_b, ws_limbs, grid, fmt, qmean, qconst, qscale);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_dequant_rows(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                               const float* qmean, int64_t n, uint16_t* out, hipStream_t st) {
+hipError_t launch_dequant_rows(const uint8_t* codes, const BlockConsts& bc, int64_t n, uint16_t* out,
+                               hipStream_t st) {
     const int64_t threads = (n + 7) / 8;
     const int64_t grid = (threads + kThreads - 1) / kThreads;
     QN_LAUNCH("dequant_rows", st, dequant_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st,
-                       reinterpret_cast<const uint32_t*>(codes), qconst, qscale, qmean, n, out, tables());
+                       reinterpret_cast<const uint32_t*>(codes), bc, n, out, tables());
     return hipGetLastError();
 }
 

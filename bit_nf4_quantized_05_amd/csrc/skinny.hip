@@ -38,7 +38,7 @@ constexpr int kSkTok = 64;          // tokens at most
 constexpr int kSkSplits = 8;        // K-split partials at most
 
 struct SkArgs {
-    const uint8_t* codes; const int8_t* qconst; const float* qscale; const float* qmean;
+    const uint8_t* codes; BlockConsts bc;
     int d_out, d_in, d_seq, splits, r, r_pad;
     const uint16_t* X;              // [d_seq, d_in]
     const uint16_t* A;              // [r, d_in]
@@ -84,7 +84,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
     const bool aok = lora && ra < a.r;
     const uint4* codes4 = reinterpret_cast<const uint4*>(a.codes);
     const uint4* x4 = reinterpret_cast<const uint4*>(a.X);
-    const float mu = a.qmean[0];
+    const float mu = a.bc.mean[0];
     {
         // code book from the (scalar) kernel arguments by selects
         for (int e = tid; e < 16 * 64; e += 256) {
@@ -153,8 +153,8 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             for (int q = 0; q < 2; ++q) {
                 const int e = tid + 256 * q;        // (row e / 8, block e % 8) of the workgroup's rows
                 const int64_t blk = static_cast<int64_t>(rb * kSkRows + (e >> 3)) * nb + b0 + min(e & 7, nbk - 1);
-                qv[q] = a.qconst[blk];
-                sv[q] = a.qscale[blk >> 8];
+                qv[q] = a.bc.q[blk];
+                sv[q] = a.bc.scale[blk >> a.bc.gshift];
             }
             uint4 cw[kSkBlk / 2];
 #pragma unroll
@@ -165,7 +165,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             }
             QN_WAIT_VM(kSkBlk / 2);                  // x rows and block constants in (code words may not be)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) s_ahat[tid + 256 * q] = block_constant(qv[q], sv[q], mu);
+            for (int q = 0; q < 2; ++q) s_ahat[tid + 256 * q] = block_constant(a.bc.fmt, qv[q], sv[q], mu);
             __syncthreads();
 #pragma unroll
             for (int p = 0; p < kSkBlk / 2; ++p) {
@@ -282,12 +282,12 @@ int skinny_splits(int64_t d_in) {
     return static_cast<int>(std::min<int64_t>(kSkSplits, nslices));
 }
 
-hipError_t launch_skinny_nf4(const uint8_t* codes, const int8_t* qconst, const float* qscale,
-                             const float* qmean, int64_t d_out, int64_t d_in, const uint16_t* X, int64_t d_seq,
+hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
+                             const uint16_t* X, int64_t d_seq,
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
                              float* part_a, uint16_t* Y, hipStream_t st) {
     SkArgs a;
-    a.codes = codes; a.qconst = qconst; a.qscale = qscale; a.qmean = qmean;
+    a.codes = codes; a.bc = bc;
     a.d_out = static_cast<int>(d_out); a.d_in = static_cast<int>(d_in); a.d_seq = static_cast<int>(d_seq);
     a.splits = skinny_splits(d_in);
     a.r = r; a.r_pad = r_pad;

@@ -34,6 +34,8 @@
  *      qconst int8  [n_b]      : 8-bit code of each block's absmax constant.
  *      qscale float [n_g]      : per-group scale b_g of the centred constants.
  *      qmean  float [1]        : mean mu of all block constants.
+ *    That is the default second level (QN_DQ_INT8). The _ex entry points take the
+ *    format `dq` explicitly; see "Second-level formats" below.
  *
  * Return codes: 0 success; -1 invalid argument (null or misaligned pointer,
  * non-positive size, ...); -2 unsupported shape; -3 workspace too small;
@@ -51,6 +53,24 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/*
+ * Second-level formats (the `dq` argument of the _ex entry points). The pages call
+ * for 8-bit constants in blocks of 256 [P2 card 4 "8-bit floats"; P4 Double
+ * Quantization "INT8"] and count 4.5 bit/param without the second level [P1 2. DQ].
+ * In all three, r_j = (a_j - mu) / b_g is one float32 division and
+ * a_hat_j = mu + b_g * T[q_j] one float32 multiply then one add.
+ *   QN_DQ_INT8  qconst_j = round-half-even(r_j * 127) in [-127, 127]; T[q] = q / 127.
+ *   QN_DQ_FP8   qconst_j = the OCP FP8 E4M3 code byte nearest to r_j * 448 (ties to
+ *               the even code; 448 is E4M3's largest finite magnitude);
+ *               T[q] = e4m3_value(q) / 448. Same buffer sizes as QN_DQ_INT8.
+ *   QN_DQ_NONE  no second level: qscale [n_b] holds a_j itself (float32) and
+ *               a_hat_j = a_j; qconst and qmean are not used and may be NULL.
+ * A b_g of 0 gives q = 0 (a_hat = mu) in both 8-bit formats.
+ */
+#define QN_DQ_INT8 0
+#define QN_DQ_FP8 1
+#define QN_DQ_NONE 2
 
 /* Library version, as major*10000 + minor*100 + patch. */
 int qn_version(void);
@@ -71,7 +91,15 @@ int qn_codebook(float* out16);
 int qn_nf4_sizes(int64_t d_out, int64_t d_in, int64_t* codes_bytes,
                  int64_t* n_blocks, int64_t* n_groups);
 
-/* Workspace bytes nf4_quantize needs for a d_out x d_in weight (0 on bad sizes). */
+/* Sizes for second-level format dq: codes bytes (n_b*32), qconst entries (n_b, or 0
+ * for QN_DQ_NONE) and qscale entries (n_g, or n_b for QN_DQ_NONE); qmean is one
+ * float for the 8-bit formats. Host pointers, any may be NULL. Returns 0, or -1 on a
+ * bad size or format. */
+int qn_nf4_sizes_ex(int64_t d_out, int64_t d_in, int dq, int64_t* codes_bytes,
+                    int64_t* qconst_entries, int64_t* qscale_entries);
+
+/* Workspace bytes nf4_quantize(_ex) needs for a d_out x d_in weight, any format
+ * (0 on bad sizes). */
 int64_t nf4_quantize_workspace_bytes(int64_t d_out, int64_t d_in);
 
 /*
@@ -94,6 +122,13 @@ int nf4_quantize(const float* W, int64_t d_out, int64_t d_in,
                  uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
                  void* workspace, int64_t workspace_bytes, void* stream);
 
+/* nf4_quantize with second-level format dq (QN_DQ_INT8 gives nf4_quantize). The
+ * first level and mu are the same in every format; QN_DQ_NONE writes a_j to qscale
+ * [n_b] and leaves qconst and qmean alone (they may be NULL). -1 on an unknown dq. */
+int nf4_quantize_ex(const float* W, int64_t d_out, int64_t d_in, int dq,
+                    uint8_t* codes, int8_t* qconst, float* qscale, float* qmean,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
 /*
  * nf4_double_dequant - constants first, then weights, to BF16.
  *   [P4 QLoRA: doubleDequant; P1 2. DQ a_hat = mu + b r_hat; P1 4-bit -> BF16]
@@ -105,6 +140,12 @@ int nf4_quantize(const float* W, int64_t d_out, int64_t d_in,
 int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                        const float* qmean, int64_t d_out, int64_t d_in,
                        uint16_t* W_bf16, void* stream);
+
+/* nf4_double_dequant for a weight quantised in format dq (a_hat as defined under
+ * "Second-level formats"). */
+int nf4_double_dequant_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                          const float* qmean, int64_t d_out, int64_t d_in, int dq,
+                          uint16_t* W_bf16, void* stream);
 
 /* Workspace bytes qlora_linear_fwd / qlora_linear_bwd_x need (0 on bad sizes). */
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
@@ -125,6 +166,13 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
                      const uint16_t* X, int64_t d_seq, uint16_t* Y,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
+/* qlora_linear_fwd for a weight quantised in format dq. */
+int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                        const float* qmean, int64_t d_out, int64_t d_in, int dq,
+                        const uint16_t* A, const uint16_t* B, int r, float s,
+                        const uint16_t* X, int64_t d_seq, uint16_t* Y,
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
 /*
  * qlora_linear_bwd_x - input gradient dX = dequant(W)^T dY + s A^T (B^T dY).
  *   [P2 card 1: gradients flow through the dequantised weights, only A and B
@@ -137,6 +185,13 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
                        const uint16_t* A, const uint16_t* B, int r, float s,
                        const uint16_t* dY, int64_t d_seq, uint16_t* dX,
                        void* workspace, int64_t workspace_bytes, void* stream);
+
+/* qlora_linear_bwd_x for a weight quantised in format dq. */
+int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                          const float* qmean, int64_t d_out, int64_t d_in, int dq,
+                          const uint16_t* A, const uint16_t* B, int r, float s,
+                          const uint16_t* dY, int64_t d_seq, uint16_t* dX,
+                          void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes qlora_lora_grads needs (0 on bad sizes). */
 int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);

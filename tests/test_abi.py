@@ -102,6 +102,35 @@ def test_argument_validation_without_device_work():
     assert lib.qlora_lora_grads_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 2 * 4096 * 64
 
 
+def test_second_level_formats_sizes_and_validation():
+    assert qn.nf4_sizes(256, 256, "fp8") == (32768, 1024, 4)
+    assert qn.nf4_sizes(256, 256, "none") == (32768, 0, 1024)     # a_j per block, no qconst
+    assert qn.nf4_sizes(3, 50, "none") == (3 * 32, 0, 3)
+    with pytest.raises(ValueError):
+        qn.nf4_sizes(256, 256, "fp4")
+    lib = _lib.lib()
+    cb = ctypes.c_int64()
+    assert lib.qn_nf4_sizes_ex(256, 256, 3, ctypes.addressof(cb), None, None) == -1
+    # unknown format -> -1 on every entry point
+    assert lib.nf4_quantize_ex(FAKE, 4, 64, 7, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+    assert lib.nf4_double_dequant_ex(FAKE, FAKE, FAKE, FAKE, 4, 64, -1, FAKE, None) == -1
+    assert lib.qlora_linear_fwd_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
+                                   1 << 30, None) == -1
+    assert lib.qlora_linear_bwd_x_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
+                                     1 << 30, None) == -1
+    # the 8-bit formats need qconst and qmean; "none" does not (a too-small workspace
+    # is the first thing it reports)
+    for dq in (0, 1):
+        assert lib.nf4_quantize_ex(FAKE, 4, 64, dq, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == -1
+        assert lib.nf4_quantize_ex(FAKE, 4, 64, dq, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert lib.nf4_quantize_ex(FAKE, 4, 64, 2, FAKE, None, FAKE, None, FAKE, 1, None) == -3
+    assert lib.nf4_quantize_ex(FAKE, 4, 64, 2, FAKE, None, None, None, FAKE, 1 << 20, None) == -1   # qscale needed
+    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, None, 64, 64, 2, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
+                                   1, None) == -3
+    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, FAKE, 64, 64, 1, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
+                                   1 << 30, None) == -1
+
+
 def test_codebook_null_pointer():
     assert _lib.lib().qn_codebook(None) == -1
 
