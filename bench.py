@@ -14,8 +14,10 @@ Also reported: per-kernel average durations (HIP events recorded by the library
 on each kernel's own stream, in a second pass of the same K steps right after the
 timed one, so the event records do not perturb `value`), the MFMA roofline fraction of
 the dominant kernel (the GEMM), the decode path's effective GB/s over 32 layer
-copies (> 256 MB, beyond the Infinity Cache), and the CPU oracle timed on a
-bounded sample of the same workload.
+copies (> 256 MB, beyond the Infinity Cache), the small-batch forward (2, 16 and 64
+tokens) over the same rotated copies, quantise and decode with the FP8 and no-DQ
+second levels next to INT8, and the CPU oracle timed on a bounded sample of the
+same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -88,13 +90,51 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
-def decode_bytes(cfg) -> int:
-    """Algorithmic HBM bytes of one d_seq = 1 call: packed codes, INT8 constants,
-    group scales, mean, A, B, x and y."""
+def weight_bytes(cfg, dq: str = "int8") -> int:
+    """Stored bytes of the quantised weight: packed codes plus the block constants
+    (8-bit codes, group scales and the mean; or one float32 per block without DQ)."""
     n = cfg.d_out * cfg.d_in
     n_b = n // 64
     n_g = -(-n_b // 256)
-    return n // 2 + n_b + 4 * n_g + 4 + 2 * cfg.r * (cfg.d_in + cfg.d_out) + 2 * cfg.d_in + 2 * cfg.d_out
+    return n // 2 + (4 * n_b if dq == "none" else n_b + 4 * n_g + 4)
+
+
+def decode_bytes(cfg, dq: str = "int8", d_seq: int = 1) -> int:
+    """Algorithmic HBM bytes of one forward call with few tokens: the quantised
+    weight, A, B, X and Y."""
+    return weight_bytes(cfg, dq) + 2 * cfg.r * (cfg.d_in + cfg.d_out) + 2 * d_seq * (cfg.d_in + cfg.d_out)
+
+
+def timed_calls(qn, torch, fn, iters: int):
+    """Back-to-back microseconds per call of fn(i), then the library's per-kernel
+    averages (HIP events on each kernel's stream) over a second pass."""
+    for i in range(4):
+        fn(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(iters):
+        fn(i)
+    torch.cuda.synchronize()
+    call_us = 1e6 * (time.perf_counter() - t0) / iters
+    qn.profile_enable(True)
+    for i in range(iters):
+        fn(i)
+    torch.cuda.synchronize()
+    prof = qn.profile_read()
+    qn.profile_enable(False)
+    return call_us, {k: round(1e3 * ms / n, 3) for k, (n, ms) in sorted(prof.items())}
+
+
+def rotated_copies(qn, q, n: int, dev) -> list:
+    """n device copies of the quantised weight q (rotating through them keeps each
+    call's weight out of the 256 MB Infinity Cache)."""
+    out = []
+    for _ in range(n):
+        c = qn.alloc_weight(q.d_out, q.d_in, dev, q.dq)
+        for dst, src in ((c.codes, q.codes), (c.qconst, q.qconst), (c.qscale, q.qscale), (c.qmean, q.qmean)):
+            dst.copy_(src)
+        out.append(c)
+    return out
 
 
 def cpu_baseline(cfg, dcfg, tokens: int) -> dict:
@@ -172,12 +212,7 @@ def main():
     Y = torch.empty(cfg.d_seq, cfg.d_out, dtype=torch.bfloat16, device=dev)
     dX = torch.empty(cfg.d_seq, cfg.d_in, dtype=torch.bfloat16, device=dev)
     y1 = torch.empty(1, dcfg.d_out, dtype=torch.bfloat16, device=dev)
-    copies = []
-    for _ in range(args.decode_copies):
-        c = qn.alloc_weight(dcfg.d_out, dcfg.d_in, dev)
-        for dst, src in ((c.codes, q.codes), (c.qconst, q.qconst), (c.qscale, q.qscale), (c.qmean, q.qmean)):
-            dst.copy_(src)
-        copies.append(c)
+    copies = rotated_copies(qn, q, args.decode_copies, dev)
     torch.cuda.synchronize()
 
     def step(i):
@@ -279,6 +314,38 @@ def main():
                   "call_us": round(1e6 * g_elapsed, 2),
                   "kernel_us": {k: round(1e3 * ms / n, 2) for k, (n, ms) in sorted(gprof.items())}}
 
+    # ---- small batch (2 <= d_seq <= 64): codes streamed once, over the rotated copies
+    small_batch = {}
+    for d_seq in (2, 16, 64):
+        xs = bf16(WL.make_x(WL.custom("sb", dcfg.d_out, dcfg.d_in, d_seq, dcfg.r, s=dcfg.s)))
+        ys = torch.empty(d_seq, dcfg.d_out, dtype=torch.bfloat16, device=dev)
+        sws = torch.empty(qn.linear_workspace_bytes(dcfg.d_out, dcfg.d_in, d_seq, dcfg.r), dtype=torch.uint8,
+                          device=dev)
+        log(f"[bench] small batch d_seq={d_seq}")
+        call_us, kus = timed_calls(qn, torch, lambda i: qn.linear_fwd(copies[i % len(copies)], A, B, dcfg.s, xs,
+                                                                      out=ys, workspace=sws), args.decode_iters)
+        kern = sum(kus.values())
+        nb = decode_bytes(dcfg, "int8", d_seq)
+        small_batch[str(d_seq)] = {"call_us_back_to_back": round(call_us, 3), "kernel_us": kus,
+                                   "bytes_per_call": nb, "effective_GBps": round(nb / (kern * 1e-6) / 1e9, 1)}
+
+    # ---- second-level formats: quantise and decode with FP8 constants and with none
+    dq_formats = {}
+    for dq in ("int8", "fp8", "none"):
+        log(f"[bench] format {dq}")
+        qf = qn.quantize(W, dq=dq)
+        q_us, q_k = timed_calls(qn, torch, lambda i: qn.quantize(W, out=qf, workspace=qws, dq=dq), args.steps)
+        fcopies = rotated_copies(qn, qf, args.decode_copies, dev)
+        d_us, d_k = timed_calls(qn, torch, lambda i: qn.linear_fwd(fcopies[i % len(fcopies)], A, B, dcfg.s, x1,
+                                                                    out=y1, workspace=dws), args.decode_iters)
+        nb = decode_bytes(dcfg, dq)
+        dq_formats[dq] = {"bits_per_param": round(8 * weight_bytes(dcfg, dq) / (dcfg.d_out * dcfg.d_in), 4),
+                          "quantize_call_us": round(q_us, 3), "quantize_kernel_us": q_k,
+                          "decode_call_us_back_to_back": round(d_us, 3), "decode_kernel_us": d_k,
+                          "decode_bytes_per_call": nb,
+                          "decode_effective_GBps": round(nb / (sum(d_k.values()) * 1e-6) / 1e9, 1)}
+        del fcopies
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -299,6 +366,8 @@ def main():
         "roofline": roofline,
         "decode": decode,
         "lora_grads": lora_grads,
+        "small_batch": small_batch,
+        "dq_formats": dq_formats,
         "kernels": kernels,
         "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
     }

@@ -65,13 +65,13 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
 // two chunks of 2048 weights, in each the weights [32 l, 32 l + 32) = 16 code bytes
 // (one 16-byte load; the wave reads 1 KB contiguous), half of block 32 h + l/2.
 // The vector-memory address unit takes about as long for a 1-byte load as for a
-// 16-byte one, so everything but the codes is loaded once per workgroup with wide
+// 16-byte one, so what all 16 rows share is loaded once per workgroup with wide
 // loads by one wave each and passed through LDS: the x segment (waves 0..7), the
-// 16 rows' 8-bit constants (wave 8, when the rows' 64-block runs are 16-byte
-// aligned; else each wave loads its own), their group scales (wave 9), the A x
-// slice partials (waves 10..13) and the 16 rows of B (wave 14). Every wave issues
-// the loads it must wait for before its code loads, so that wait never covers the
-// codes, and the next segment's loads go out before the current one is computed.
+// A x slice partials (waves 10..13) and the 16 rows of B (wave 14). The block
+// constants are per row: lane l loads block l's 8-bit code (or a_j) and scale with
+// its code words. Every wave issues the loads it must wait for before its code
+// loads, so that wait never covers the codes, and the next segment's loads go out
+// before the current one is computed.
 // A lane forms a_hat of block l and hands it to the two lanes owning the block's
 // halves by a cross-lane read. Each code byte (two weights) is looked up as a pair
 // of bf16 code values and dotted with the bf16 x pair (v_dot2_f32_bf16); a_hat
@@ -86,13 +86,8 @@ constexpr int kLutCopies = 32;
 
 struct GvRowSeg {
     uint4 cw[2];            // code words of the two chunks
-    int8_t qv;              // constant of block l (only when each wave loads its own)
-    float sv;               // its group scale (idem)
-};
-
-struct GvStage {            // per-workgroup staging loads of one segment
-    uint4 v;                // x (waves 0..7) or constants (wave 8)
-    float sc;               // group scale (wave 9, lanes < 32)
+    int8_t qv;              // second-level code of block l
+    float sv;               // its group scale (a_j without a second level)
 };
 
 __device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv, const uint32_t* lut,
@@ -116,7 +111,6 @@ __device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv,
 // chunks 4 l .. 4 l + 3; their order is XORed with bits 2..3 of l
 __device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c >> 4) & 3)); }
 
-template <bool kStageQ>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                      int d_out, int d_in, const uint16_t* __restrict__ x,
@@ -124,8 +118,6 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                      int nparts, uint16_t* __restrict__ y, NF4Tables tab) {
     __shared__ uint4 lut4[256 * kLutCopies / 4];
     __shared__ uint4 xs[2][kGvSeg / 8];
-    __shared__ uint4 qcs[2][kGvWaves * 64 / 16];      // row i's 64 constants at bytes 64 i ..
-    __shared__ float qss[2][2 * kGvWaves];            // row i: scales of groups base_i, base_i + 1
     __shared__ float tvs[1024];
     __shared__ uint4 bs[kGvWaves * 256 * 2 / 16];     // the 16 rows of B (r <= 256)
     __shared__ float qlut[256];
@@ -140,34 +132,21 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     const int nbpr = d_in / 64;
     const int upr = d_in / 32;                    // 16-byte code words per row
     const int nseg = (d_in + kGvSeg - 1) / kGvSeg;
-    const int64_t n_b = static_cast<int64_t>(d_out) * nbpr;
-    const int64_t n_g = (n_b + 255) / 256;
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
     const int64_t row_u = static_cast<int64_t>(row) * upr;
 
-    // first block of row i's run in segment S, and the first group it touches
-    auto run0 = [&](int i, int S) { return static_cast<int64_t>(min(row0 + i, d_out - 1)) * nbpr + S * 64; };
-    auto stage_issue = [&](GvStage& g, int S) {
+    // the x segment: waves 0..7, one 16-byte chunk per lane
+    auto stage_issue = [&](uint4& g, int S) {
         if (wave < 8) {
             const int col = S * kGvSeg + 8 * tid;
-            g.v = x4[min(col, d_in - 8) / 8];
-        } else if (kStageQ && wave == 8) {
-            // row lane/4, bytes 16 (lane%4) .. of its 64-block run (16-byte aligned);
-            // the tail of the last row is clamped into the array (those bytes are unused)
-            const int64_t b = min(run0(lane >> 2, S) + 16 * (lane & 3), n_b - 16);
-            g.v = *reinterpret_cast<const uint4*>(bc.q + b);
-        } else if (wave == 9 && lane < 2 * kGvWaves) {
-            g.sc = bc.scale[min((run0(lane >> 1, S) >> 8) + (lane & 1), n_g - 1)];
+            g = x4[min(col, d_in - 8) / 8];
         }
     };
-    auto stage_store = [&](const GvStage& g, int S) {
-        const int k = S & 1;
-        if (wave < 8) xs[k][gv_xpos(tid)] = S * kGvSeg + 8 * tid < d_in ? g.v : uint4{0, 0, 0, 0};
-        else if (kStageQ && wave == 8) qcs[k][lane] = g.v;
-        else if (wave == 9 && lane < 2 * kGvWaves) qss[k][lane] = g.sc;
+    auto stage_store = [&](const uint4& g, int S) {
+        if (wave < 8) xs[S & 1][gv_xpos(tid)] = S * kGvSeg + 8 * tid < d_in ? g : uint4{0, 0, 0, 0};
     };
     auto seg_issue = [&](GvRowSeg& k, int S) {
-        if (!kStageQ) {
+        {
             const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
             k.qv = bc.q[b];
             k.sv = bc.scale[b >> bc.gshift];
@@ -180,9 +159,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     };
 
     // ---- loads: staged data first, then the codes
-    GvStage st;
-    st.v = uint4{0, 0, 0, 0};
-    st.sc = 0.0f;
+    uint4 st = uint4{0, 0, 0, 0};
     stage_issue(st, 0);
     const int nval = nparts * r;                  // <= 1024
     uint4 tst = uint4{0, 0, 0, 0};
@@ -240,18 +217,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     float acc = 0.0f;
     auto compute = [&](const GvRowSeg& k, int S) {
         const int kb = S & 1;
-        const int64_t b = static_cast<int64_t>(row) * nbpr + S * 64 + lane;
         const bool bok = S * 64 + lane < nbpr;
-        int q;
-        float sc;
-        if (kStageQ) {
-            q = reinterpret_cast<const int8_t*>(qcs[kb])[wave * 64 + lane];
-            sc = qss[kb][2 * wave + static_cast<int>((b >> 8) - (run0(wave, S) >> 8))];
-        } else {
-            q = k.qv;
-            sc = k.sv;
-        }
-        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? sc : mu + sc * qlut[q + 128];
+        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? k.sv : mu + k.sv * qlut[k.qv + 128];
         const uint4* xb = xs[kb];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -304,17 +271,9 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
     const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
-    // the staged variant takes each row's constants and group scales per segment,
-    // which needs groups of 256 blocks
-    if ((d_in / 64) % 16 == 0 && bc.gshift == 8) {
-        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<true>, grid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out),
-                  static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
-    } else {
-        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<false>, grid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out),
-                  static_cast<int>(d_in), x, B, r, s, ws_part, nparts, y, tables());
-    }
+    QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel, grid, dim3(64 * kGvWaves), 0, st,
+              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B,
+              r, s, ws_part, nparts, y, tables());
     return hipGetLastError();
 }
 
