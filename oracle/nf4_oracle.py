@@ -19,6 +19,8 @@ they appear on each page):
        book), "Double Quantization" (blocks of 64, 8-bit constants in blocks of
        256, the 0.127 bit/param count), "QLoRA" (doubleDequant order) and
        "量化原理" (absmax integer quantisation).
+  [P5] gist.science, "Sintesi Tecnica: GPTQ-intrinsic LoRA": W ~ Q + L R, and the
+       low-rank factors kept at 4 or 8 bits ("Risultati Chiave", "Empirici").
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes): code-book probability offset, nearest-code tie rule, nibble
@@ -363,6 +365,53 @@ def dequant_rows(q: dict, d_in: int, rows: np.ndarray) -> np.ndarray:
         vals = cb[unpack_codes(codes[bj])].reshape(per_row, BLOCK)
         out[k] = f32_to_bf16_bits((vals * ahat[bj][:, None]).astype(np.float32)).reshape(-1)
     return out
+
+
+# --------------------------------------------------------------------------
+# 8-bit block quantisation of a weight (adapter factors of the W ~ Q + L R form)
+# [P4 量化原理: absmax integer quantisation; P5 (gist.science GPTQ-intrinsic LoRA),
+#  "Risultati Chiave / Empirici": the factors L and R kept at 4 or 8 bits]
+# --------------------------------------------------------------------------
+
+def int8_quantize(w: np.ndarray):
+    """Symmetric absmax INT8 per block of 64 flat elements (row-major, padded with
+    +0.0): a_j = max |w|; x = fl32(w / a_j); q = round-half-even(fl32(x * 127)) in
+    [-127, 127]; a zero block gets q = 0. Returns (q int8 [n_b * 64], a float32 [n_b])."""
+    blocks = to_blocks(w)
+    a = block_absmax(blocks)
+    safe = np.where(a > 0, a, np.float32(1.0)).astype(np.float32)
+    x = (blocks / safe[:, None]).astype(np.float32)
+    q = np.rint((x * np.float32(INT8_STEP)).astype(np.float32))
+    q[a == 0] = 0
+    return q.astype(np.int8).reshape(-1), a
+
+
+def int8_dequant(q: np.ndarray, a: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """w_hat = bf16(fl32(fl32(q / 127) * a_j)) as bf16 bits [rows, cols]."""
+    n = rows * cols
+    qf = (np.asarray(q, dtype=np.int8).reshape(-1, BLOCK).astype(np.float32) / np.float32(INT8_STEP)).astype(np.float32)
+    prod = (qf * np.asarray(a, dtype=np.float32)[:, None]).astype(np.float32).reshape(-1)[:n]
+    return f32_to_bf16_bits(prod).reshape(rows, cols)
+
+
+def quantize_factor(w: np.ndarray, bits: int):
+    """A low-rank factor at 4 bits (NF4 codes, float32 a_j per block: the layout
+    without a second level) or 8 bits (int8_quantize). Returns (codes, a)."""
+    if bits == 4:
+        q = quantize(w, dq="none")
+        return q["codes"], q["qscale"]
+    if bits == 8:
+        return int8_quantize(w)
+    raise ValueError("bits must be 4 or 8")
+
+
+def dequant_factor(codes: np.ndarray, a: np.ndarray, bits: int, rows: int, cols: int) -> np.ndarray:
+    """bf16 bits [rows, cols] of a factor from quantize_factor."""
+    if bits == 4:
+        return double_dequant(codes, np.zeros(0, np.int8), a, np.zeros(1, np.float32), rows, cols, dq="none")
+    if bits == 8:
+        return int8_dequant(codes, a, rows, cols)
+    raise ValueError("bits must be 4 or 8")
 
 
 # --------------------------------------------------------------------------
