@@ -46,6 +46,11 @@ SIGNATURES = {
                                      _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
                                        _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+    "int8_quantize": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "int8_dequant": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "qlr_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "qlr_linear_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_int,
+                                _c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qn_profile_enable": (_c_int, [_c_int]),
     "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
 }
@@ -274,3 +279,88 @@ def profile_read(cap: int = 64) -> dict:
         nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
         out[nm] = (int(launches[i]), float(total[i]))
     return out
+
+
+# ---- quantised low-rank factors (W ~ Q + L R with L, R at 4 or 8 bits) ----------
+
+@dataclass
+class QFactor:
+    """A low-rank factor [rows, cols] kept at 4 bits (NF4 codes, float32 a_j per block
+    of 64) or 8 bits (absmax INT8 per block of 64, float32 a_j)."""
+    bits: int
+    codes: torch.Tensor    # uint8 [n_b * 32] (4 bits) or int8 [n_b * 64] (8 bits)
+    scale: torch.Tensor    # float32 [n_b]
+    rows: int
+    cols: int
+
+
+def int8_quantize(W: torch.Tensor):
+    """int8_quantize on a float32 [rows, cols] CUDA tensor -> (q int8 [n_b*64], absmax float32 [n_b])."""
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D")
+    rows, cols = W.shape
+    _need(W, torch.float32, (rows, cols), "W", W.device)
+    n_b = -(-rows * cols // 64)
+    q = torch.empty(n_b * 64, dtype=torch.int8, device=W.device)
+    a = torch.empty(n_b, dtype=torch.float32, device=W.device)
+    _check(lib().int8_quantize(_ptr(W), rows, cols, _ptr(q), _ptr(a), _stream(W.device)), "int8_quantize")
+    return q, a
+
+
+def int8_dequant(q: torch.Tensor, absmax: torch.Tensor, rows: int, cols: int) -> torch.Tensor:
+    """int8_dequant -> bfloat16 [rows, cols]."""
+    n_b = -(-rows * cols // 64)
+    _need(q, torch.int8, (n_b * 64,), "q", q.device)
+    _need(absmax, torch.float32, (n_b,), "absmax", q.device)
+    o = torch.empty(rows, cols, dtype=torch.bfloat16, device=q.device)
+    _check(lib().int8_dequant(_ptr(q), _ptr(absmax), rows, cols, _ptr(o), _stream(q.device)), "int8_dequant")
+    return o
+
+
+def quantize_factor(M: torch.Tensor, bits: int) -> QFactor:
+    """A factor at 4 bits (nf4_quantize_ex without a second level) or 8 bits (int8_quantize)."""
+    rows, cols = M.shape
+    if bits == 4:
+        q = quantize(M, dq="none")
+        return QFactor(4, q.codes, q.qscale, rows, cols)
+    if bits == 8:
+        c, a = int8_quantize(M)
+        return QFactor(8, c, a, rows, cols)
+    raise ValueError("bits must be 4 or 8")
+
+
+def dequant_factor(f: QFactor) -> torch.Tensor:
+    """bfloat16 [rows, cols] of a quantised factor."""
+    if f.bits == 4:
+        empty_q = torch.empty(0, dtype=torch.int8, device=f.codes.device)
+        empty_m = torch.empty(0, dtype=torch.float32, device=f.codes.device)
+        return double_dequant(NF4Weight(f.codes, empty_q, f.scale, empty_m, f.rows, f.cols, "none"))
+    return int8_dequant(f.codes, f.scale, f.rows, f.cols)
+
+
+def qlr_linear_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
+    return lib().qlr_linear_workspace_bytes(d_out, d_in, d_seq, r)
+
+
+def qlr_linear_fwd(q: NF4Weight, Af: QFactor, Bf: QFactor, s: float, X: torch.Tensor,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """qlr_linear_fwd: Y [d_seq, d_out] = X Q_hat^T + s (X A_hat^T) B_hat^T with A [r, d_in]
+    and B [d_out, r] quantised (W ~ Q + L R with B = R^T, A = L^T)."""
+    dev = q.device
+    r = Af.rows
+    if (Af.rows, Af.cols) != (r, q.d_in) or (Bf.rows, Bf.cols) != (q.d_out, r):
+        raise ValueError("factor shapes must be A [r, d_in] and B [d_out, r]")
+    if X.dim() != 2 or X.shape[1] != q.d_in:
+        raise ValueError(f"input must be [d_seq, {q.d_in}]")
+    d_seq = X.shape[0]
+    _need(X, torch.bfloat16, (d_seq, q.d_in), "input", dev)
+    o = out if out is not None else torch.empty(d_seq, q.d_out, dtype=torch.bfloat16, device=dev)
+    _need(o, torch.bfloat16, (d_seq, q.d_out), "out", dev)
+    need = qlr_linear_workspace_bytes(q.d_out, q.d_in, d_seq, r)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib().qlr_linear_fwd(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
+                              _dq_code(q.dq), Af.bits, _ptr(Af.codes), _ptr(Af.scale), Bf.bits, _ptr(Bf.codes),
+                              _ptr(Bf.scale), r, float(s), _ptr(X), d_seq, _ptr(o), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(dev))
+    _check(rc, "qlr_linear_fwd")
+    return o

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlora_nf4.so")
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "prologue.hip", "gemv.hip", "skinny.hip", "lora_grads.hip",
+SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "prologue.hip", "gemv.hip", "skinny.hip", "lora_grads.hip", "factors.hip",
            "tables.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

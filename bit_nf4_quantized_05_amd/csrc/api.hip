@@ -170,6 +170,45 @@ void prof_end(void* token, const char* name, hipStream_t st) {
 }
 }  // namespace qn
 
+namespace {
+
+// The forward once the arguments are checked: d_seq == 1 streams the codes (GEMV),
+// d_seq <= 64 runs the small-batch kernel, otherwise dequantise + pre-pass + GEMM.
+int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_out, int64_t d_in,
+                   const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t d_seq,
+                   uint16_t* Y, char* ws, const LinWs& lw, hipStream_t st) {
+    hipError_t e;
+    if (d_seq == 1) {
+        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, Y,
+                                reinterpret_cast<float*>(ws + lw.t), st);
+        if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
+        return 0;
+    }
+    if (d_seq <= qn::kSkinnyMaxTokens) {
+        // few tokens: the codes streamed once, A x in the same launch
+        float* part = reinterpret_cast<float*>(ws + lw.part);
+        float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * d_out;
+        if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
+                                       part, part_a, Y, st)) != hipSuccess)
+            return hip_fail(e, "qlora_linear_fwd (small batch)");
+        return 0;
+    }
+    uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);
+    uint16_t* t = reinterpret_cast<uint16_t*>(ws + lw.lora);
+    uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
+    const bool pad = r != lw.r_pad;
+    // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
+    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
+                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (prologue)");
+    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
+                                d_out, d_seq, d_out, st)) != hipSuccess)
+        return hip_fail(e, "qlora_linear_fwd (gemm)");
+    return 0;
+}
+
+}  // namespace
+
 // workspace of qlora_lora_grads
 namespace {
 struct GradWs {
@@ -318,36 +357,8 @@ int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float*
     int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, X, d_seq, Y, workspace,
                           workspace_bytes, &lw, &bc);
     if (rc) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(workspace);
-    hipError_t e;
-    if (d_seq == 1) {
-        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, Y,
-                                reinterpret_cast<float*>(ws + lw.t), st);
-        if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
-        return 0;
-    }
-    if (d_seq <= qn::kSkinnyMaxTokens) {
-        // few tokens: the codes streamed once, A x in the same launch
-        float* part = reinterpret_cast<float*>(ws + lw.part);
-        float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * d_out;
-        if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
-                                       part, part_a, Y, st)) != hipSuccess)
-            return hip_fail(e, "qlora_linear_fwd (small batch)");
-        return 0;
-    }
-    uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);
-    uint16_t* t = reinterpret_cast<uint16_t*>(ws + lw.lora);
-    uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
-    const bool pad = r != lw.r_pad;
-    // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
-    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
-                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_fwd (prologue)");
-    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
-                                d_out, d_seq, d_out, st)) != hipSuccess)
-        return hip_fail(e, "qlora_linear_fwd (gemm)");
-    return 0;
+    return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, d_seq, Y, static_cast<char*>(workspace), lw,
+                          static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
@@ -393,6 +404,71 @@ int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* 
                        int64_t workspace_bytes, void* stream) {
     return qlora_linear_bwd_x_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, dY, d_seq, dX,
                                  workspace, workspace_bytes, stream);
+}
+
+// ---- quantised low-rank factors (W ~ Q + L R) --------------------------------
+int int8_quantize(const float* W, int64_t rows, int64_t cols, int8_t* q, float* absmax, void* stream) {
+    if (!W || !q || !absmax) return fail(-1, "null pointer argument");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(rows, cols, &n, &n_b, &n_g)) return fail(-1, "bad shape");
+    if (!aligned(W, 16) || !aligned(q, 16) || !aligned(absmax, 4)) return fail(-1, "misaligned pointer");
+    hipError_t e = qn::launch_int8_quantize(W, n, q, absmax, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "int8_quantize");
+    return 0;
+}
+
+int int8_dequant(const int8_t* q, const float* absmax, int64_t rows, int64_t cols, uint16_t* W_bf16, void* stream) {
+    if (!q || !absmax || !W_bf16) return fail(-1, "null pointer argument");
+    int64_t n, n_b, n_g;
+    if (!nf4_counts(rows, cols, &n, &n_b, &n_g)) return fail(-1, "bad shape");
+    if (!aligned(q, 16) || !aligned(absmax, 4) || !aligned(W_bf16, 16)) return fail(-1, "misaligned pointer");
+    hipError_t e = qn::launch_int8_dequant(q, absmax, n, W_bf16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "int8_dequant");
+    return 0;
+}
+
+int64_t qlr_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
+    return linear_ws(d_out, d_in, d_seq, r).bytes + align_up(2 * r * d_in, 256) + align_up(2 * d_out * r, 256);
+}
+
+int qlr_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                   int64_t d_out, int64_t d_in, int dq, int a_bits, const void* a_codes, const float* a_scale,
+                   int b_bits, const void* b_codes, const float* b_scale, int r, float s, const uint16_t* X,
+                   int64_t d_seq, uint16_t* Y, void* workspace, int64_t workspace_bytes, void* stream) {
+    if ((a_bits != 4 && a_bits != 8) || (b_bits != 4 && b_bits != 8)) return fail(-1, "factor bits must be 4 or 8");
+    if (!a_codes || !a_scale || !b_codes || !b_scale) return fail(-1, "null pointer argument");
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4))
+        return fail(-1, "misaligned pointer");
+    if (r < 1 || r > 256 || d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1, r <= 256");
+    // the dequantised factors sit after the linear workspace (A [r, d_in], then B [d_out, r])
+    const LinWs lw0 = linear_ws(d_out, d_in, d_seq, r);
+    if (workspace_bytes < qlr_linear_workspace_bytes(d_out, d_in, d_seq, r)) return fail(-3, "workspace too small");
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + lw0.bytes);
+    uint16_t* b_hat = reinterpret_cast<uint16_t*>(ws + lw0.bytes + align_up(2 * r * d_in, 256));
+    LinWs lw;
+    qn::BlockConsts bc;
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, a_hat, b_hat, r, X, d_seq, Y, workspace,
+                          workspace_bytes, &lw, &bc);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    struct { int bits; const void* codes; const float* scale; int64_t n; uint16_t* out; } f[2] = {
+        {a_bits, a_codes, a_scale, static_cast<int64_t>(r) * d_in, a_hat},
+        {b_bits, b_codes, b_scale, d_out * static_cast<int64_t>(r), b_hat}};
+    for (auto& fa : f) {
+        if (fa.bits == 4) {
+            const uint8_t* c = static_cast<const uint8_t*>(fa.codes);
+            e = qn::launch_dequant_rows(c, qn::BlockConsts{reinterpret_cast<const int8_t*>(c), fa.scale, fa.scale,
+                                                           qn::kDqNone, 0},
+                                        fa.n, fa.out, st);
+        } else {
+            e = qn::launch_int8_dequant(static_cast<const int8_t*>(fa.codes), fa.scale, fa.n, fa.out, st);
+        }
+        if (e != hipSuccess) return hip_fail(e, "qlr_linear_fwd (factors)");
+    }
+    return linear_fwd_run(codes, bc, d_out, d_in, a_hat, b_hat, r, s, X, d_seq, Y, ws, lw, st);
 }
 
 // ---- adapter gradients ----------------------------------------------------

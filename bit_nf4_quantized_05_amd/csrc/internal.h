@@ -105,6 +105,12 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
                              float* part_a, uint16_t* Y, hipStream_t st);
 
+// ---- factors.hip ----
+// Symmetric absmax INT8 per block of 64 flat elements of W [n] (padded with +0.0):
+// q [ceil(n/64)*64] int8, absmax [ceil(n/64)] f32; and its bf16 dequantisation.
+hipError_t launch_int8_quantize(const float* W, int64_t n, int8_t* q, float* absmax, hipStream_t st);
+hipError_t launch_int8_dequant(const int8_t* q, const float* absmax, int64_t n, uint16_t* out, hipStream_t st);
+
 // ---- lora_grads.hip ----
 // Column-sum partials of out[n, j] = sum_m P[m, n] T[m, j] for the two adapter
 // gradients, then their fixed-order sum:

@@ -6,7 +6,9 @@
  *        "2. Double Quantization (DQ)");
  *   [P2] learn.ifs.name, Dettmers et al. 2023 deck "3 QLoRA Finetuning", cards 1-4;
  *   [P4] jjjymmm.cn 2024/03 blog, sections "4-bit NormalFloat(NF4)",
- *        "Double Quantization" and "QLoRA".
+ *        "Double Quantization", "QLoRA" and "量化原理";
+ *   [P5] gist.science, "Sintesi Tecnica: GPTQ-intrinsic LoRA" (W ~ Q + L R with the
+ *        low-rank factors at 4 or 8 bits).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -192,6 +194,50 @@ int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const floa
                           const uint16_t* A, const uint16_t* B, int r, float s,
                           const uint16_t* dY, int64_t d_seq, uint16_t* dX,
                           void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Quantised low-rank factors: the W ~ Q + L R inference form with L and R kept at 4
+ * or 8 bits [P5 gist.science "Sintesi Tecnica: GPTQ-intrinsic LoRA": W ~ Q + L R;
+ * "Risultati Chiave / Empirici": the factors at 4 and 8 bits]. In the column form of
+ * this layer (W0 is d_out x d_in) the correction (L R)^T is B A with B = R^T
+ * [d_out, r] and A = L^T [r, d_in]; Q is the NF4 weight and s scales the product
+ * (s = 1 for the pages' form).
+ *
+ * int8_quantize - symmetric absmax INT8 per block of 64 flat elements of a row-major
+ * float32 matrix [rows, cols] (padded with +0.0) [P4 量化原理]:
+ *   a_j = max|w|, q = round-half-even((w / a_j) * 127) in [-127, 127] (0 if a_j = 0),
+ *   each step one float32 operation.
+ *   q      int8  [ceil(rows*cols/64) * 64]   (output)
+ *   absmax float [ceil(rows*cols/64)]        (output)
+ * int8_dequant - w_hat = bf16_round_nearest_even((q / 127) * a_j) -> W_bf16 [rows, cols].
+ * A factor "at 4 bits" is nf4_quantize_ex(..., QN_DQ_NONE, ...) of it: NF4 codes and the
+ * float32 a_j per block.
+ */
+int int8_quantize(const float* W, int64_t rows, int64_t cols, int8_t* q, float* absmax, void* stream);
+int int8_dequant(const int8_t* q, const float* absmax, int64_t rows, int64_t cols,
+                 uint16_t* W_bf16, void* stream);
+
+/* Workspace bytes qlr_linear_fwd needs (0 on bad sizes). */
+int64_t qlr_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+
+/*
+ * qlr_linear_fwd - Y = dequant(Q) X + s B_hat (A_hat X), with the factors quantised:
+ * qlora_linear_fwd_ex on the bf16 factors dequantised into the workspace.
+ *   codes, qconst, qscale, qmean, dq : the NF4 weight Q (d_out x d_in) in format dq.
+ *   a_bits, a_codes, a_scale : A [r, d_in]; a_bits 4 -> NF4 codes uint8 [n_b*32] and
+ *       a_j float [n_b] (nf4_quantize_ex with QN_DQ_NONE); 8 -> int8 [n_b*64] and
+ *       absmax float [n_b] (int8_quantize); n_b = ceil(r*d_in/64).
+ *   b_bits, b_codes, b_scale : B [d_out, r] likewise, n_b = ceil(d_out*r/64) (blocks of
+ *       64 consecutive flat elements, across rows when r < 64).
+ *   The other arguments and the shape rules are those of qlora_linear_fwd; the
+ *   workspace must hold qlr_linear_workspace_bytes(d_out, d_in, d_seq, r) bytes.
+ */
+int qlr_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                   const float* qmean, int64_t d_out, int64_t d_in, int dq,
+                   int a_bits, const void* a_codes, const float* a_scale,
+                   int b_bits, const void* b_codes, const float* b_scale,
+                   int r, float s, const uint16_t* X, int64_t d_seq, uint16_t* Y,
+                   void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes qlora_lora_grads needs (0 on bad sizes). */
 int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);

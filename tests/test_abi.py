@@ -131,6 +131,26 @@ def test_second_level_formats_sizes_and_validation():
                                    1 << 30, None) == -1
 
 
+def test_factor_entry_points_validation():
+    lib = _lib.lib()
+    assert lib.int8_quantize(None, 4, 64, FAKE, FAKE, None) == -1
+    assert lib.int8_quantize(FAKE, 0, 64, FAKE, FAKE, None) == -1
+    assert lib.int8_quantize(FAKE + 4, 4, 64, FAKE, FAKE, None) == -1          # misaligned W
+    assert lib.int8_dequant(FAKE, None, 4, 64, FAKE, None) == -1
+    assert lib.qlr_linear_workspace_bytes(64, 64, 4, 8) >= lib.qlora_linear_workspace_bytes(64, 64, 4, 8) + \
+        2 * 8 * 64 * 2
+    assert lib.qlr_linear_workspace_bytes(64, 64, 4, 0) == 0
+    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, 0]
+    tail = [8, 1.0, FAKE, 4, FAKE, FAKE, 1 << 30, None]
+    assert lib.qlr_linear_fwd(*args, 3, FAKE, FAKE, 4, FAKE, FAKE, *tail) == -1       # bits
+    assert lib.qlr_linear_fwd(*args, 4, FAKE, FAKE, 16, FAKE, FAKE, *tail) == -1      # bits
+    assert lib.qlr_linear_fwd(*args, 4, None, FAKE, 8, FAKE, FAKE, *tail) == -1       # null factor
+    small = [8, 1.0, FAKE, 4, FAKE, FAKE, 1024, None]
+    assert lib.qlr_linear_fwd(*args, 4, FAKE, FAKE, 8, FAKE, FAKE, *small) == -3      # workspace
+    bad_shape = [FAKE, FAKE, FAKE, FAKE, 64, 100, 0]
+    assert lib.qlr_linear_fwd(*bad_shape, 8, FAKE, FAKE, 8, FAKE, FAKE, *tail) == -2
+
+
 def test_codebook_null_pointer():
     assert _lib.lib().qn_codebook(None) == -1
 
