@@ -13,9 +13,10 @@
 //
 // Kernels:
 //   quant_blocks   - HBM-streaming pass over W (16 waves per workgroup, each with the
-//                    next tile's loads in flight while it codes the current one): per
-//                    64-block absmax (8-lane DPP max), codes by a 32-cell threshold
-//                    table in LDS, packed nibbles, the block constants, and an exact
+//                    next tile's loads in flight while it codes the current one):
+//                    per 64-block absmax (8-lane DPP max), w / a by a per-block
+//                    reciprocal and one correction, codes by a 32-cell threshold table
+//                    in LDS, packed nibbles, the block constants, and an exact
 //                    per-workgroup sum of the constants as 32-bit-limb integers.
 //   dq_encode      - each workgroup first forms mu itself: it adds the per-workgroup
 //                    limb sums (integers, so the order is free and every workgroup gets
@@ -75,14 +76,10 @@ __global__ __launch_bounds__(kQuantThreads)
 void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
                   uint32_t* __restrict__ codes32, float* __restrict__ absmax,
                   unsigned long long* __restrict__ limb_part, NF4Tables tab) {
-    __shared__ float s_thr[kCells];
-    __shared__ uint32_t s_base[kCells];
+    __shared__ float2 s_cell[kCells];               // (threshold, base) of each cell: one 8-byte read
     __shared__ unsigned long long s_limb[kLimbs];
     const int tid = threadIdx.x;
-    if (tid < kCells) {
-        s_thr[tid] = tab.cell_thr[tid];
-        s_base[tid] = tab.cell_base[tid];
-    }
+    if (tid < kCells) s_cell[tid] = float2{tab.cell_thr[tid], __uint_as_float(tab.cell_base[tid])};
     if (tid < kLimbs) s_limb[tid] = 0ull;
     __syncthreads();
 
@@ -102,13 +99,28 @@ void quant_blocks(const float* __restrict__ W, int64_t n, int64_t n_b,
         for (int e = 0; e < 8; ++e) m = max(m, __float_as_uint(cur.v[e]) & 0x7FFFFFFFu);
         m = max8(m);                         // exact absmax bits of the block
         const float a = __uint_as_float(m);
+        // x = w / a. For 2^-96 <= a < 2^126: y = 1/a correctly rounded once per block,
+        // q0 = w y, then one correction q0 + y (w - a q0) with the residual exact by
+        // FMA, which yields the correctly rounded quotient wherever |x| is at least
+        // ~1e-9 (Markstein); below that every x codes to 7 either way, since the
+        // thresholds nearest zero are about +-0.04. Other blocks divide directly.
+        const bool fast = m >= 0x0F800000u && m < 0x7E800000u;
+        const float y = fast ? 1.0f / a : 0.0f;
 
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = (m == 0) ? 0.0f : cur.v[e] / a;   // IEEE division, |x| <= 1
+            float x;
+            if (fast) {
+                const float q0 = cur.v[e] * y;
+                const float r = __builtin_fmaf(-q0, a, cur.v[e]);
+                x = __builtin_fmaf(r, y, q0);
+            } else {
+                x = (m == 0) ? 0.0f : cur.v[e] / a;   // IEEE division, |x| <= 1
+            }
             const int cell = min(max(static_cast<int>((x + 1.0f) * 16.0f), 0), kCells - 1);
-            const uint32_t c = s_base[cell] + (x > s_thr[cell] ? 1u : 0u);
+            const float2 cl = s_cell[cell];
+            const uint32_t c = __float_as_uint(cl.y) + (x > cl.x ? 1u : 0u);
             packed |= c << (4 * e);
         }
         const int64_t blk = t * 8 + (lane >> 3);
