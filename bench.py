@@ -16,8 +16,9 @@ timed one, so the event records do not perturb `value`), the MFMA roofline fract
 the dominant kernel (the GEMM), the decode path's effective GB/s over 32 layer
 copies (> 256 MB, beyond the Infinity Cache), the small-batch forward (2, 16 and 64
 tokens) over the same rotated copies, quantise and decode with the FP8 and no-DQ
-second levels next to INT8, and the CPU oracle timed on a bounded sample of the
-same workload.
+second levels next to INT8, quantise / forward / dX of the MLP pair (11008x4096 and
+4096x11008, r = 64, 2048 tokens) and the large layer (28672x8192, r = 64, 8192
+tokens), and the CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5]
 """
@@ -45,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-copies", type=int, default=32)
     ap.add_argument("--decode-iters", type=int, default=256)
+    ap.add_argument("--no-layers", action="store_true",
+                    help="skip the MLP-pair and large-layer legs (quantise, fwd, dX on 11008x4096, 4096x11008 "
+                         "and 28672x8192)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the prefill workload the CPU oracle runs (0 = skip the CPU baseline)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -123,6 +127,50 @@ def timed_calls(qn, torch, fn, iters: int):
     prof = qn.profile_read()
     qn.profile_enable(False)
     return call_us, {k: round(1e3 * ms / n, 3) for k, (n, ms) in sorted(prof.items())}
+
+
+def layer_leg(qn, torch, WL, name: str, dev) -> dict:
+    """Quantise, forward and input gradient of one full-size layer (inputs resident in
+    HBM): call times back to back, and the GEMM's TFLOP/s from its kernel events."""
+    import numpy as np
+    cfg = WL.CONFIGS[name]
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    W = torch.from_numpy(WL.make_weight(cfg)).to(dev)
+    a, b = WL.make_lora(cfg)
+    A, B = bf16(a), bf16(b)
+    X, dY = bf16(WL.make_x(cfg)), bf16(WL.make_dy(cfg))
+    q = qn.quantize(W)
+    qws = torch.empty(qn.quantize_workspace_bytes(cfg.d_out, cfg.d_in), dtype=torch.uint8, device=dev)
+    lws = torch.empty(qn.linear_workspace_bytes(cfg.d_out, cfg.d_in, cfg.d_seq, cfg.r), dtype=torch.uint8, device=dev)
+    Y = torch.empty(cfg.d_seq, cfg.d_out, dtype=torch.bfloat16, device=dev)
+    dX = torch.empty(cfg.d_seq, cfg.d_in, dtype=torch.bfloat16, device=dev)
+    n = cfg.d_out * cfg.d_in
+    q_us, q_k = timed_calls(qn, torch, lambda i: qn.quantize(W, out=q, workspace=qws), 5)
+    f_us, f_k = timed_calls(qn, torch, lambda i: qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=lws), 3)
+    b_us, b_k = timed_calls(qn, torch, lambda i: qn.linear_bwd_x(q, A, B, cfg.s, dY, out=dX, workspace=lws), 3)
+    gemm_flops = cfg.fwd_flops()                     # fwd and dX have the same algorithmic flops
+
+    def tf(us):
+        return round(gemm_flops / (us * 1e-6) / 1e12, 1)
+
+    def gemm_us(k):
+        # the GEMM of a call: one gemm_nt_kernel, or (few tiles) gemm_nt_split + its reduce
+        return sum(v for name, v in k.items() if name.startswith("gemm_"))
+    gf, gb = gemm_us(f_k), gemm_us(b_k)
+    out = {"d_out": cfg.d_out, "d_in": cfg.d_in, "d_seq": cfg.d_seq, "r": cfg.r,
+           "quantize_us": round(q_us, 2), "quantize_kernel_us": q_k,
+           "quantize_GBps": round(4.516 * n / (q_us * 1e-6) / 1e9, 1),
+           "fwd_call_us": round(f_us, 2), "fwd_kernel_us": f_k, "fwd_TFLOPs": tf(f_us),
+           "bwd_x_call_us": round(b_us, 2), "bwd_x_kernel_us": b_k, "bwd_x_TFLOPs": tf(b_us),
+           "fwd_gemm_TFLOPs": tf(gf), "fwd_gemm_frac_of_peak": round(gemm_flops / (gf * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "bwd_x_gemm_TFLOPs": tf(gb),
+           "bwd_x_gemm_frac_of_peak": round(gemm_flops / (gb * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del W, X, dY, Y, dX, lws, qws, q
+    torch.cuda.empty_cache()
+    return out
 
 
 def rotated_copies(qn, q, n: int, dev) -> list:
@@ -346,6 +394,13 @@ def main():
                           "decode_effective_GBps": round(nb / (sum(d_k.values()) * 1e-6) / 1e9, 1)}
         del fcopies
 
+    # ---- the MLP pair and the large layer (outside the timed step)
+    layers = {}
+    if not args.no_layers:
+        for name in ("mlp_up", "mlp_down", "large"):
+            log(f"[bench] layer {name}")
+            layers[name] = layer_leg(qn, torch, WL, name, dev)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -368,6 +423,7 @@ def main():
         "lora_grads": lora_grads,
         "small_batch": small_batch,
         "dq_formats": dq_formats,
+        "layers": layers,
         "kernels": kernels,
         "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
     }

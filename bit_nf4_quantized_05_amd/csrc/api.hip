@@ -4,6 +4,7 @@
 // no arithmetic on the data.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -80,7 +81,7 @@ QuantWs quant_ws(int64_t n_b) {
 }
 
 struct LinWs {
-    int64_t what, lora, adapt, adapt2, t, part, bytes;
+    int64_t what, lora, adapt, adapt2, t, part, gpart, bytes;
     int r_pad;
 };
 
@@ -96,6 +97,12 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.part = off;                                                                // small batch: K-split partials
     if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
         off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * (d_out + w.r_pad), 256);
+    w.gpart = off;                                                               // GEMM K-split partials (few tiles)
+    if (d_seq > qn::kSkinnyMaxTokens) {
+        const int64_t fwd = qn::gemm_splits(d_seq, d_out, d_in), bwd = qn::gemm_splits(d_seq, d_in, d_out);
+        const int64_t need = std::max(fwd > 1 ? fwd * d_out : 0, bwd > 1 ? bwd * d_in : 0) * d_seq * 4;
+        off += align_up(need, 256);
+    }
     w.bytes = off;
     return w;
 }
@@ -202,7 +209,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
                                  A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
     if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
-                                d_out, d_seq, d_out, st)) != hipSuccess)
+                                d_out, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (gemm)");
     return 0;
 }
@@ -393,7 +400,7 @@ int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const floa
                                  bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (prologue)");
     if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
-                                d_in, d_seq, d_in, st)) != hipSuccess)
+                                d_in, d_seq, d_in, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (gemm)");
     return 0;
 }

@@ -21,6 +21,11 @@
 // barrier sits before the last k16 sub-step, so the next stage's first fragments are
 // read under the last MFMAs. Tiles are handed to the 8 XCDs in contiguous ranges so
 // each XCD's L2 sees a compact block of P and Q panels.
+//
+// gemm_nt_split: the same body when there are at most 128 tiles (half the CUs): the
+// K-steps of P Q^T are split over S = 2..4 workgroups per tile, the LoRA K-steps go to
+// the last split, each split writes its fp32 partial tile, and gemm_split_reduce adds
+// the S partials in split order and rounds to bf16.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -59,6 +64,7 @@ struct GemmArgs {
     const uint16_t* Q2; int64_t ldq2; int kt2;
     uint16_t* C; int64_t ldc; int M, N, tiles_m, tiles_n;
     uint32_t bytesP, bytesQ, bytesP2, bytesQ2;   // buffer extents for the load descriptors
+    float* part; int splits, kper;               // split path: partials [splits][M][N], K-steps per split
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -75,7 +81,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 #define QN_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 // WM x WN waves; each wave owns a (256/WM) x (256/WN) sub-tile of 32x32 MFMA tiles.
-template <int WM, int WN>
+template <int WM, int WN, bool kSplit>
 __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     constexpr int NW = WM * WN;                 // waves
     constexpr int NT = 64 * NW;                 // threads
@@ -90,7 +96,8 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 
     // ---- tile assignment: contiguous logical ranges per XCD, grouped raster
     const int T = g.tiles_m * g.tiles_n;
-    const int w = blockIdx.x;
+    const int w = kSplit ? static_cast<int>(blockIdx.x) % T : static_cast<int>(blockIdx.x);
+    const int sk = kSplit ? static_cast<int>(blockIdx.x) / T : 0;   // split of this workgroup
     const int logical = (T % 8 == 0) ? (w & 7) * (T >> 3) + (w >> 3) : w;
     const int gsize = kGroupM * g.tiles_n;
     const int grp = logical / gsize;
@@ -128,22 +135,28 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     const __amdgpu_buffer_rsrc_t rsQ = make_rsrc(g.Q, g.bytesQ);
     const __amdgpu_buffer_rsrc_t rsP2 = make_rsrc(g.P2, g.bytesP2);
     const __amdgpu_buffer_rsrc_t rsQ2 = make_rsrc(g.Q2, g.bytesQ2);
-    const int KT = g.kt1 + g.kt2;
-    constexpr int kLoadsPerStep = 2 * SEG;      // per wave
+    // K-steps of this workgroup: main steps [kb, ke) of P Q^T, then (last split, or no
+    // split) the kt2 LoRA steps; step k of the loop is global step kb + k while k < ke - kb
+    const int kb = kSplit ? sk * g.kper : 0;
+    const int ke = kSplit ? min(kb + g.kper, g.kt1) : g.kt1;
+    const bool lora = !kSplit || sk == g.splits - 1;
+    const int KT = (ke - kb) + (lora ? g.kt2 : 0);
+    const int kshift = kb;                      // global main step = local + kshift
+    const int kmain = ke - kb;
 
 #define QN_ISSUE(KTV, ST)                                                                         \
     {                                                                                             \
-        const int kk_ = (KTV);                                                                    \
+        const int kl_ = (KTV);                                                                    \
         uint4* sp_ = (ST) + wave * (64 * SEG);                                                    \
         uint4* sq_ = sp_ + kChunks;                                                               \
-        if (kk_ < g.kt1) {                                                                        \
-            const int so_ = kk_ * (BK * 2);                                                       \
+        if (kl_ < kmain) {                                                                        \
+            const int so_ = (kl_ + kshift) * (BK * 2);                                            \
             _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP, (lds_ptr_t)(sp_ + 64 * j), 16, voP[j], so_, 0, 0); \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ, (lds_ptr_t)(sq_ + 64 * j), 16, voQ[j], so_, 0, 0); \
             }                                                                                     \
         } else {                                                                                  \
-            const int so_ = (kk_ - g.kt1) * (BK * 2);                                             \
+            const int so_ = (kl_ - kmain) * (BK * 2);                                             \
             _Pragma("unroll") for (int j = 0; j < SEG; ++j) {                                     \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsP2, (lds_ptr_t)(sp_ + 64 * j), 16, voP2[j], so_, 0, 0); \
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsQ2, (lds_ptr_t)(sq_ + 64 * j), 16, voQ2[j], so_, 0, 0); \
@@ -217,6 +230,26 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 #undef QN_FRAGS
 #undef QN_ISSUE
 
+    if constexpr (kSplit) {
+        // fp32 partial tile of this split: the lane's 4 consecutive n of row m as 16 bytes
+        float* pt = g.part + static_cast<int64_t>(sk) * M * N;
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+            const int m = m0 + wm * (TM * 32) + b * 32 + static_cast<int>(frow);
+#pragma unroll
+            for (int a = 0; a < TN; ++a) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int n = n0 + wn * (TN * 32) + a * 32 + 8 * gq + 4 * (lane >> 5);
+                    if (m < M && n < N)
+                        *reinterpret_cast<float4*>(pt + static_cast<int64_t>(m) * N + n) =
+                            float4{acc[a][b][4 * gq], acc[a][b][4 * gq + 1], acc[a][b][4 * gq + 2],
+                                   acc[a][b][4 * gq + 3]};
+                }
+            }
+        }
+        return;
+    }
     // ---- epilogue. Every wave is past the last barrier, so the LDS stages are free
     // and no load is in flight. The bf16 C tile (256 rows x 512 B) goes to LDS: rows
     // 128q .. 128q+127 in stage q (q = 0, 1), 16-byte chunk j of row r at position
@@ -263,14 +296,45 @@ constexpr int kGemmWM = 2, kGemmWN = QN_GEMM_WAVES_N;
 
 __global__ __launch_bounds__(64 * kGemmWM * kGemmWN, 1)
 void gemm_nt_kernel(GemmArgs g) {
-    gemm_nt_body<kGemmWM, kGemmWN>(g);
+    gemm_nt_body<kGemmWM, kGemmWN, false>(g);
+}
+
+__global__ __launch_bounds__(64 * kGemmWM * kGemmWN, 1)
+void gemm_nt_split(GemmArgs g) {
+    gemm_nt_body<kGemmWM, kGemmWN, true>(g);
+}
+
+// C[m, n..n+3] = bf16(sum over splits in order), 4 outputs per thread (N % 4 == 0)
+__global__ __launch_bounds__(256)
+void gemm_split_reduce(const float* __restrict__ part, int splits, int64_t MN, int N, uint16_t* __restrict__ C,
+                       int64_t ldc) {
+    const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+    if (e >= MN) return;
+    float4 v[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        v[s] = s < splits ? *reinterpret_cast<const float4*>(part + s * MN + e) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    float4 t = v[0];
+#pragma unroll
+    for (int s = 1; s < 4; ++s) {
+        if (s < splits) { t.x += v[s].x; t.y += v[s].y; t.z += v[s].z; t.w += v[s].w; }
+    }
+    const int64_t m = e / N, n = e % N;
+    *reinterpret_cast<uint2*>(C + m * ldc + n) = uint2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
 }
 
 }  // namespace
 
+int gemm_splits(int64_t M, int64_t N, int64_t K1) {
+    const int64_t T = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    if (T > 128) return 1;
+    const int64_t s = std::min<int64_t>({4, 256 / T, K1 / BK / 8});   // at least 8 K-steps per split
+    return static_cast<int>(std::max<int64_t>(1, s));
+}
+
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
-                          int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N,
+                          int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N, float* part,
                           hipStream_t st) {
     GemmArgs g;
     g.tiles_m = static_cast<int>((M + BM - 1) / BM);
@@ -284,8 +348,20 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.bytesQ = static_cast<uint32_t>(2 * ldq * N);
     g.bytesP2 = static_cast<uint32_t>(2 * ldp2 * M);
     g.bytesQ2 = static_cast<uint32_t>(2 * ldq2 * N);
-    QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(64 * kGemmWM * kGemmWN), 0,
-              st, g);
+    g.splits = gemm_splits(M, N, K1);
+    g.kper = (g.kt1 + g.splits - 1) / g.splits;
+    g.part = part;
+    if (g.splits <= 1 || part == nullptr) {
+        g.splits = 1;
+        QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(64 * kGemmWM * kGemmWN), 0,
+                  st, g);
+        return hipGetLastError();
+    }
+    QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.tiles_m * g.tiles_n * g.splits),
+              dim3(64 * kGemmWM * kGemmWN), 0, st, g);
+    const int64_t MN = M * N;
+    QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce, dim3(static_cast<unsigned>((MN / 4 + 255) / 256)), dim3(256),
+              0, st, part, g.splits, MN, static_cast<int>(N), C, ldc);
     return hipGetLastError();
 }
 

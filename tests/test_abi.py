@@ -42,6 +42,11 @@ def test_version_and_sizes():
     # d_seq = 1: the forward streams the codes, but the input gradient still runs the
     # dequantise + GEMM path, so one workspace size must cover both
     assert qn.linear_workspace_bytes(4096, 4096, 1, 16) >= 2 * 4096 * 4096 + 4 * 64 * 16
+    # few output tiles: the GEMM splits K and keeps fp32 partials in the workspace
+    # (2 tiles of the 200 x 512 forward -> 4 splits; a small K -> no split)
+    base = qn.linear_workspace_bytes(512, 4096, 200, 16)
+    assert base >= 2 * 512 * 4096 + 4 * 200 * 512 * 4
+    assert qn.linear_workspace_bytes(320, 192, 300, 100) < 2 * 320 * 192 + 4 * 300 * 320 * 4 + (1 << 20)
     assert qn.quantize_workspace_bytes(0, 5) == 0
     assert qn.linear_workspace_bytes(64, 64, 1, 0) == 0
 

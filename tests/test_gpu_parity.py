@@ -167,6 +167,10 @@ LINEAR_SMALL = [
     WL.custom("gemv_r64", 512, 1024, 1, 64, s=1.0),
     WL.custom("gemv_ragged", 320, 4160, 1, 3, s=2.0),       # 3 column chunks, the last 64 wide
     WL.custom("gemv_wide", 128, 11008, 1, 256, s=0.5),      # 6 column chunks, r = 256
+    # at most 128 output tiles: the GEMM splits K over 2..4 workgroups per tile
+    WL.custom("split_fwd", 512, 4096, 200, 16, s=2.0),       # fwd 2 tiles -> 4 splits
+    WL.custom("split_bwd", 4096, 512, 130, 64, s=1.0),       # dX 2 tiles -> 4 splits, ragged tokens
+    WL.custom("split_both", 1536, 1536, 300, 33, s=1.5),     # 12 tiles each way -> 3 splits
 ]
 
 
