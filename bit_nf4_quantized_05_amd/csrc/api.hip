@@ -81,9 +81,15 @@ QuantWs quant_ws(int64_t n_b) {
 }
 
 struct LinWs {
-    int64_t what, lora, adapt, adapt2, t, part, gpart, bytes;
+    int64_t what, lora, adapt, adapt2, t, part, gpart, ppart, bytes;
     int r_pad;
 };
+
+// fp32 partials of a K-split LoRA pre-pass over M tokens and K columns (0 if unsplit)
+int64_t prepass_part_bytes(int64_t M, int64_t K, int r) {
+    const qn::PrepassSplit ps = qn::prepass_split(M, K);
+    return ps.splits > 1 ? 4 * static_cast<int64_t>(ps.splits) * M * 32 * ((r + 31) / 32) : 0;
+}
 
 LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     LinWs w{};
@@ -103,6 +109,9 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
         const int64_t need = std::max(fwd > 1 ? fwd * d_out : 0, bwd > 1 ? bwd * d_in : 0) * d_seq * 4;
         off += align_up(need, 256);
     }
+    w.ppart = off;                                                               // pre-pass K-split partials
+    off += align_up(std::max(d_seq > qn::kSkinnyMaxTokens ? prepass_part_bytes(d_seq, d_in, r) : 0,
+                             prepass_part_bytes(d_seq, d_out, r)), 256);
     w.bytes = off;
     return w;
 }
@@ -206,7 +215,8 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
     const bool pad = r != lw.r_pad;
     // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
     if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
-                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r, st)) != hipSuccess)
+                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r,
+                                 reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
     if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
                                 d_out, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
@@ -219,7 +229,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
 // workspace of qlora_lora_grads
 namespace {
 struct GradWs {
-    int64_t tp, up, bt, part, bytes;
+    int64_t tp, up, bt, part, ppart, bytes;
     int r_pad;
 };
 
@@ -231,6 +241,8 @@ GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
     w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
     w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
+    w.ppart = off; off += align_up(std::max(prepass_part_bytes(d_seq, d_in, r), prepass_part_bytes(d_seq, d_out, r)),
+                                   256);                                            // pre-pass K-split partials
     w.bytes = off;
     return w;
 }
@@ -397,7 +409,8 @@ int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const floa
         return hip_fail(e, "qlora_linear_bwd_x (B^T)");
     // dequant W_hat^T + U = s (dY B) + A^T padded to r_pad columns, in one launch
     if ((e = qn::launch_prologue(codes, bc, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
-                                 bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in, st)) != hipSuccess)
+                                 bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in,
+                                 reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (prologue)");
     if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
                                 d_in, d_seq, d_in, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
@@ -508,13 +521,15 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const
     hipError_t e;
     // T' = bf16(s X A^T): the forward's pre-pass, without the dequantisation
     if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, X, d_in, d_seq,
-                                 d_in, A, d_in, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) != hipSuccess)
+                                 d_in, A, d_in, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0,
+                                 reinterpret_cast<float*>(ws + gw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (X A^T)");
     // U' = bf16(s dY B): the input gradient's pre-pass on B^T
     if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (B^T)");
     if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, dY, d_out,
-                                 d_seq, d_out, bt, d_out, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0, st)) !=
+                                 d_seq, d_out, bt, d_out, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0,
+                                 reinterpret_cast<float*>(ws + gw.ppart), st)) !=
         hipSuccess)
         return hip_fail(e, "qlora_lora_grads (dY B)");
     if ((e = qn::launch_lora_grads(X, dY, tp, up, d_out, d_in, d_seq, r, gw.r_pad, part, dA, dB, st)) != hipSuccess)

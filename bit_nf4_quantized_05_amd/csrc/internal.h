@@ -79,13 +79,17 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
 // an adapter layout job (adapt_mode 1: B [arows, acols] -> [arows, r_pad] zero-padded;
 // 2: A [arows, acols] -> A^T [acols, r_pad] zero-padded; 0: none), and the double
 // dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed; none if
-// what is null).
+// what is null). The pre-pass splits K over prepass_split(M, K).splits workgroups per
+// 128 tokens, whose fp32 partials go to ppart (splits * M * 32 ceil(r/32) floats) and
+// are added by a second small launch; a null ppart runs it unsplit.
+struct PrepassSplit { int splits, kper; };
+PrepassSplit prepass_split(int64_t M, int64_t K);
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
                            const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
                            int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
-                           int64_t acols, hipStream_t st);
+                           int64_t acols, float* ppart, hipStream_t st);
 // dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);

@@ -16,9 +16,10 @@ namespace {
 // ---------------------------------------------------------------------------
 // Prologue of a linear call: one launch whose workgroups take three independent
 // jobs, all memory-bound, so they overlap on the chip:
-//   [0, n_pre)            LoRA pre-pass  OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T),
-//                         32 tokens per workgroup, the 4 waves on K-quarters,
-//                         summed through LDS; columns r..r_pad-1 come out 0.
+//   [0, n_pre)            LoRA pre-pass  OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T):
+//                         128 tokens (32 per wave) and one K-slice per workgroup;
+//                         with one slice it writes OUT (columns r..r_pad-1 as 0),
+//                         else fp32 partials that prepass_reduce adds in slice order.
 //   [n_pre, +n_adapt)     adapter layout: B padded to r_pad columns (forward) or
 //                         A^T padded to r_pad columns (input gradient).
 //   [.., +n_deq)          double dequantisation to bf16: W_hat row-major
@@ -35,149 +36,147 @@ struct PrologueArgs {
     int adapt_mode;                 // 0 none, 1 pad columns, 2 transpose + pad
     const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
     int n_pre, n_adapt, n_deq;
+    int psplits, kper;              // pre-pass K-slices and 64-wide K-chunks per slice
+    float* ppart;                   // [psplits][M][32 NT] fp32 partials when psplits > 1
 };
 
 constexpr int kDeqPerWG = 8192;                  // weights per row-major dequant workgroup (128 blocks)
 constexpr int kTP = 64 + 8;                      // LDS pitch (bf16) of the transpose tile
 
-// Three LDS ring slots of the pre-pass, as distinct objects (each 4 waves x 32 rows x
-// 128 B) so the compiler can tell that reading one does not depend on direct-to-LDS
-// loads into another. The other prologue jobs use them as scratch.
-__shared__ uint4 g_pre0[4 * 256];
-__shared__ uint4 g_pre1[4 * 256];
-__shared__ uint4 g_pre2[4 * 256];
-
-// NT = ceil(r / 32) rank tiles are computed; columns NT*32 .. r_pad-1 are written as
-// zeros. The 4 waves take K-quarters; each streams its quarter in chunks of 32 rows
-// x 64 K of X through a ring of 3 LDS slots, two chunks ahead: a chunk is loaded
-// by 4 direct-to-LDS loads of 8 whole 128-byte rows each (coalesced), with the
-// 16-byte pieces of row r XOR-swizzled by ((r >> 1) & 7) so the MFMA fragment
-// reads (32 rows, one piece each) are free of bank conflicts. For NT <= 2 the
-// matching chunk of R is fetched into registers with the chunk of X (vector loads
-// complete in issue order, so both must run equally far ahead); for NT > 2 (rank
-// >= 96) R fragments are loaded at their use.
+// LoRA pre-pass. A workgroup takes 128 tokens (wave w: tokens 32 w .. 32 w + 31) and a
+// slice of K; per 64-wide K chunk, the 128 rows of P and the 32 NT rows of R are fetched
+// straight into LDS (direct loads, two stages that are distinct LDS objects), so every
+// wave reuses the same R chunk (R is read once per 128 tokens, not once per 32). A row
+// is 128 B = 8 chunks of 16 B; chunk c of row r sits at c ^ ((r >> 1) & 7), which keeps
+// the 32-row MFMA fragment reads free of bank conflicts. D = R P^T per 32x32 tile:
+// rank rows, token columns. Rows of R past r and tokens past M are clamped into the
+// arrays; their results are not stored (ranks past r are written as 0).
 template <int NT>
-__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b) {
-    constexpr bool kPrefR = NT <= 2;
-    constexpr int kRS = kPrefR ? NT : 1;               // R tiles held per ring slot
-    constexpr int kLoads = 4 + (kPrefR ? 4 * NT : 0);  // vector loads per chunk
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int m0 = b * 32;
-    const int nchunk = a.K / 64;                       // whole 64-wide K chunks, split over 4 waves
-    const int kbeg = (wave * nchunk / 4) * 64;
-    const int kend = ((wave + 1) * nchunk / 4) * 64;
-    const int ksub = 8 * (lane >> 5);
+struct PreStage {
+    uint4 x[128 * 8];               // 128 token rows
+    uint4 r[32 * NT * 8];           // 32 NT rank rows
+};
+
+template <int NT>
+__device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& a, int wave, int lane, int m0,
+                                          int kc) {
+    const int64_t k0 = static_cast<int64_t>(kc) * 64;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {                      // P rows 32 w + 8 u .. +7
+        const int row = 32 * wave + 8 * u + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t m = min(m0 + row, a.M - 1);
+        __builtin_amdgcn_global_load_lds((global_ptr)(a.P + m * a.ldp + k0 + 8 * c),
+                                         (lds_ptr)(&st.x[(32 * wave + 8 * u) * 8]), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {                     // R rows 8 (4 i + w) .. +7
+        const int row = 8 * (4 * i + wave) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        const int64_t j = min(row, a.r - 1);
+        __builtin_amdgcn_global_load_lds((global_ptr)(a.R + j * a.ldr + k0 + 8 * c),
+                                         (lds_ptr)(&st.r[8 * (4 * i + wave) * 8]), 16, 0, 0);
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void pre_compute(const PreStage<NT>& st, int wave, int lane, f32x16 (&acc)[NT]) {
+    const int frow = lane & 31;
+    const int sw = (frow >> 1) & 7;                    // rows 32 w + frow and 32 t + frow share it
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = (2 * u + (lane >> 5)) ^ sw;
+        const uint4 xf = st.x[(32 * wave + frow) * 8 + c];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t] = mfma32(st.r[(32 * t + frow) * 8 + c], xf, acc[t]);
+    }
+}
+
+#define QN_PRE_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+template <int NT>
+__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreStage<NT>& s0, PreStage<NT>& s1) {
+    constexpr int kLoads = 4 + NT;                     // direct loads per wave and stage
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tiles = (a.M + 127) / 128;
+    const int tile = b % tiles, sp = b / tiles;
+    const int m0 = tile * 128;
+    const int kb = sp * a.kper;
+    const int ke = min(kb + a.kper, a.K / 64);
     f32x16 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
-    const uint16_t* rrow[NT];
-    bool rok[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const int rr = t * 32 + (lane & 31);
-        rok[t] = rr < a.r;
-        rrow[t] = a.R + static_cast<int64_t>(rok[t] ? rr : 0) * a.ldr + ksub;
+    // The barriers wait for LDS traffic only; each wave first waits for its own loads
+    // of the stage about to be read (loads complete in issue order).
+    pre_issue<NT>(s0, a, wave, lane, m0, kb);
+    for (int kc = kb; kc < ke; kc += 2) {
+        if (kc + 1 < ke) { pre_issue<NT>(s1, a, wave, lane, m0, kc + 1); QN_WAIT_VM(kLoads); }
+        else QN_WAIT_VM(0);
+        QN_PRE_BARRIER();
+        pre_compute<NT>(s0, wave, lane, acc);
+        QN_PRE_BARRIER();
+        if (kc + 1 >= ke) break;
+        if (kc + 2 < ke) { pre_issue<NT>(s0, a, wave, lane, m0, kc + 2); QN_WAIT_VM(kLoads); }
+        else QN_WAIT_VM(0);
+        QN_PRE_BARRIER();
+        pre_compute<NT>(s1, wave, lane, acc);
+        QN_PRE_BARRIER();
     }
-    // DMA source of lane i in load u: row 8u + i/8 of the chunk, piece (i%8) ^ swz
-    const uint16_t* xsrc[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int r = 8 * u + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        xsrc[u] = a.P + static_cast<int64_t>(min(m0 + r, a.M - 1)) * a.ldp + 8 * c;
-    }
-    // fragment of sub-step u: row lane%32, piece (2u + lane/32) ^ ((row >> 1) & 7)
-    const int frow = lane & 31;
-    int fpos[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) fpos[u] = frow * 8 + ((2 * u + (lane >> 5)) ^ ((frow >> 1) & 7));
-    uint4 pr[3][kRS][4];
-#define QN_CLOAD(K0, SL, S)                                                                    \
-    {                                                                                          \
-        uint4* sl_ = (SL) + wave * 256;                                                        \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u)                                          \
-            __builtin_amdgcn_global_load_lds((global_ptr)(xsrc[u] + (K0)), (lds_ptr)(sl_ + 64 * u), 16, 0, 0); \
-        if constexpr (kPrefR) {                                                                \
-            _Pragma("unroll") for (int t = 0; t < kRS; ++t)                                    \
-                _Pragma("unroll") for (int u = 0; u < 4; ++u)                                  \
-                    pr[S][t][u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) \
-                                         : uint4{0, 0, 0, 0};                                  \
-        }                                                                                      \
-    }
-#define QN_PCOMP(K0, SL, S)                                                                    \
-    {                                                                                          \
-        const uint4* sl_ = (SL) + wave * 256;                                                  \
-        uint4 xf[4];                                                                           \
-        _Pragma("unroll") for (int u = 0; u < 4; ++u) xf[u] = sl_[fpos[u]];                    \
-        if constexpr (kPrefR) {                                                                \
-            _Pragma("unroll") for (int u = 0; u < 4; ++u)                                      \
-                _Pragma("unroll") for (int t = 0; t < NT; ++t)                                 \
-                    acc[t] = mfma32(pr[S][t % kRS][u], xf[u], acc[t]);                         \
-        } else {                                                                               \
-            _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                   \
-                uint4 rf[4];                                                                   \
-                _Pragma("unroll") for (int u = 0; u < 4; ++u)                                  \
-                    rf[u] = rok[t] ? *reinterpret_cast<const uint4*>(rrow[t] + (K0) + 16 * u) : uint4{0, 0, 0, 0}; \
-                _Pragma("unroll") for (int u = 0; u < 4; ++u) acc[t] = mfma32(rf[u], xf[u], acc[t]); \
-            }                                                                                  \
-        }                                                                                      \
-    }
-    // chunk kc: wait until its loads are done (those of the up to two later chunks may
-    // still be in flight), compute, then refill its slot with chunk kc + 3
-#define QN_PSTEP(KC, SL, S)                                                                    \
-    if ((KC) < kend) {                                                                         \
-        if ((KC) + 128 < kend) { QN_WAIT_VM(2 * kLoads); }                                    \
-        else if ((KC) + 64 < kend) { QN_WAIT_VM(kLoads); }                                    \
-        else { QN_WAIT_VM(0); }                                                                \
-        QN_PCOMP(KC, SL, S)                                                                    \
-        if ((KC) + 192 < kend) QN_CLOAD((KC) + 192, SL, S)                                     \
-    }
-    if (kbeg < kend) QN_CLOAD(kbeg, g_pre0, 0)
-    if (kbeg + 64 < kend) QN_CLOAD(kbeg + 64, g_pre1, 1)
-    if (kbeg + 128 < kend) QN_CLOAD(kbeg + 128, g_pre2, 2)
-    for (int k = kbeg; k < kend; k += 192) {
-        QN_PSTEP(k, g_pre0, 0)
-        QN_PSTEP(k + 64, g_pre1, 1)
-        QN_PSTEP(k + 128, g_pre2, 2)
-    }
-#undef QN_PSTEP
-#undef QN_CLOAD
-#undef QN_PCOMP
-    // sum the four K-quarters, one rank tile at a time through g_pre0 (every load
-    // has landed: each wave's last step waited for all of its loads)
-    f32x16* red = reinterpret_cast<f32x16*>(g_pre0);   // [2][64]
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        __syncthreads();
-        if (wave >= 2) red[(wave - 2) * 64 + lane] = acc[t];
-        __syncthreads();
-        if (wave < 2) acc[t] += red[wave * 64 + lane];
-        __syncthreads();
-        if (wave == 1) red[lane] = acc[t];
-        __syncthreads();
-        if (wave == 0) acc[t] += red[lane];
-    }
-    if (wave != 0) return;
-    const int m = m0 + (lane & 31);
+    // D of tile t: lane l holds ranks 32 t + 8 (v / 4) + 4 (l / 32) + v % 4 of token l % 32
+    const int m = m0 + 32 * wave + (lane & 31);
     if (m >= a.M) return;
-    uint16_t* orow = a.OUT + static_cast<int64_t>(m) * a.r_pad;
+    if (a.psplits == 1) {
+        uint16_t* orow = a.OUT + static_cast<int64_t>(m) * a.r_pad;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = n + e < a.r ? a.s * acc[t][4 * gq + e] : 0.0f;
+                *reinterpret_cast<uint2*>(orow + n) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+        }
+        for (int n = NT * 32 + 4 * (lane >> 5); n < a.r_pad; n += 8)      // padding columns
+            *reinterpret_cast<uint2*>(orow + n) = uint2{0u, 0u};
+        return;
+    }
+    float* prow = a.ppart + (static_cast<int64_t>(sp) * a.M + m) * (32 * NT);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const f32x16 v = acc[t];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
             const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
-            uint2 o;
-            o.x = pack_bf16x2(a.s * v[4 * gq + 0], a.s * v[4 * gq + 1]);
-            o.y = pack_bf16x2(a.s * v[4 * gq + 2], a.s * v[4 * gq + 3]);
-            *reinterpret_cast<uint2*>(orow + n) = o;
+            *reinterpret_cast<float4*>(prow + n) =
+                float4{acc[t][4 * gq], acc[t][4 * gq + 1], acc[t][4 * gq + 2], acc[t][4 * gq + 3]};
         }
     }
-    // zero padding columns NT*32 .. r_pad-1 (lanes 0..31 own this row, 4 bf16 per store)
-    for (int n = NT * 32 + 4 * (lane >> 5); n < a.r_pad; n += 8)
-        *reinterpret_cast<uint2*>(orow + n) = uint2{0u, 0u};
+}
+#undef QN_PRE_BARRIER
+
+// OUT[m, j] = bf16(s * sum of the slice partials in slice order) for j < r, 0 for
+// r <= j < r_pad; a thread takes 4 consecutive columns.
+__global__ __launch_bounds__(256)
+void prepass_reduce(const float* __restrict__ part, int splits, int M, int ncols, int r, int r_pad, float s,
+                    uint16_t* __restrict__ OUT) {
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int q4 = r_pad / 4;
+    if (idx >= static_cast<int64_t>(M) * q4) return;
+    const int64_t m = idx / q4;
+    const int j = static_cast<int>(idx % q4) * 4;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (j < ncols) {
+        const float* p = part + m * ncols + j;
+        for (int sp = 0; sp < splits; ++sp) {
+            const float4 t = *reinterpret_cast<const float4*>(p + static_cast<int64_t>(sp) * M * ncols);
+            v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = j + e < r ? s * v[e] : 0.0f;
+    *reinterpret_cast<uint2*>(OUT + m * r_pad + j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // Adapter layouts; destination is [rows, r_pad] (pad) or [acols, r_pad] (transpose).
@@ -283,10 +282,11 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
 template <int NT>
 __global__ __launch_bounds__(256)
 void prologue_kernel(PrologueArgs a, NF4Tables tab) {
-    char* lds = reinterpret_cast<char*>(g_pre1);          // 16 KB of scratch for the other jobs
+    __shared__ PreStage<NT> s0, s1;
+    char* lds = reinterpret_cast<char*>(s1.x);             // 16 KB of scratch for the other jobs
     const int b = blockIdx.x;
     if (b < a.n_pre) {
-        prepass_job<NT>(a, b);
+        prepass_job<NT>(a, b, s0, s1);
         return;
     }
     if (b < a.n_pre + a.n_adapt) {
@@ -316,19 +316,35 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t r
 
 }  // namespace
 
+PrepassSplit prepass_split(int64_t M, int64_t K) {
+    // about one pre-pass workgroup per CU: 128-token tiles times K-slices of at least
+    // 4 chunks of 64
+    const int64_t tiles = (M + 127) / 128;
+    const int64_t nk = K / 64;
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>((256 + tiles - 1) / tiles, nk / 4));
+    PrepassSplit ps;
+    ps.kper = static_cast<int>((nk + want - 1) / want);
+    ps.splits = static_cast<int>((nk + ps.kper - 1) / ps.kper);
+    return ps;
+}
+
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
                            const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
                            int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
-                           int64_t acols, hipStream_t st) {
+                           int64_t acols, float* ppart, hipStream_t st) {
     PrologueArgs a;
     a.codes = codes; a.bc = bc;
     a.d_out = d_out; a.d_in = d_in; a.transposed = transposed ? 1 : 0; a.what = what;
     a.P = P; a.ldp = ldp; a.M = static_cast<int>(M); a.K = static_cast<int>(K);
     a.R = R; a.ldr = ldr; a.r = r; a.s = s; a.OUT = OUT; a.r_pad = r_pad;
     a.adapt_mode = adapt_mode; a.asrc = asrc; a.adst = adst; a.arows = arows; a.acols = acols;
-    a.n_pre = static_cast<int>((M + 31) / 32);
+    const PrepassSplit ps = prepass_split(M, K);
+    a.psplits = ppart == nullptr ? 1 : ps.splits;
+    a.kper = a.psplits == 1 ? static_cast<int>(K / 64) : ps.kper;
+    a.ppart = ppart;
+    a.n_pre = static_cast<int>((M + 127) / 128) * a.psplits;
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
     a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
@@ -336,7 +352,7 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
                               : static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64)
                                                             : (n + kDeqPerWG - 1) / kDeqPerWG);
     const int NT = (r + 31) / 32;
-    static_assert(64 + 512 + 64 * kTP * sizeof(uint16_t) <= sizeof(g_pre1), "dequant scratch fits a ring slot");
+    static_assert(64 + 512 + 64 * kTP * sizeof(uint16_t) <= sizeof(PreStage<1>::x), "dequant scratch fits a stage");
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
     const NF4Tables& tab = tables();
     switch (NT) {
@@ -346,6 +362,11 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
         QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
 #undef QN_PRO_CASE
         default: return hipErrorInvalidValue;
+    }
+    if (a.psplits > 1) {
+        const int64_t total = M * (r_pad / 4);
+        QN_LAUNCH("prepass_reduce", st, prepass_reduce, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
+                  st, ppart, a.psplits, static_cast<int>(M), 32 * NT, r, r_pad, s, OUT);
     }
     return hipGetLastError();
 }
