@@ -23,7 +23,7 @@ namespace {
 //   [n_pre, +n_adapt)     adapter layout: B padded to r_pad columns (forward) or
 //                         A^T padded to r_pad columns (input gradient).
 //   [.., +n_deq)          double dequantisation to bf16: W_hat row-major
-//                         (forward) or W_hat^T through a 64x64 LDS tile (dX).
+//                         (forward) or W_hat^T through 64x64 LDS tiles (dX).
 // ---------------------------------------------------------------------------
 struct PrologueArgs {
     const uint8_t* codes; BlockConsts bc;
@@ -37,6 +37,7 @@ struct PrologueArgs {
     const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
     int n_pre, n_adapt, n_deq;
     int psplits, kper;              // pre-pass K-slices and 64-wide K-chunks per slice
+    int trans_tiles;                // 64 x 64 tiles per transposed-dequant workgroup (1..4)
     float* ppart;                   // [psplits][M][32 NT] fp32 partials when psplits > 1
 };
 
@@ -241,41 +242,56 @@ __device__ __forceinline__ void dequant_rows_job(const PrologueArgs& a, int b, c
     }
 }
 
-// Transposed dequantisation of a 64 (o) x 64 (i) tile: each row o of the tile is one
-// 64-block, whose a_hat threads 0..63 form into LDS; thread (o, q4) dequantises 16
-// weights into the LDS tile, which is written out transposed as W_hat^T rows.
+// Transposed dequantisation of a region of 64 (o) x 64 nt (i), nt = trans_tiles <= 4
+// tiles of 64 x 64 (more tiles per workgroup for larger weights, so that there are
+// about 2048 workgroups): thread (o, q4) loads the code words of its 16 columns in
+// every tile at once, and thread t forms a_hat of block (o = t / 4, tile t % 4) into
+// LDS, so the region costs one memory round trip. Then tile by tile, each row o
+// dequantises into an LDS tile that is written out transposed as W_hat^T rows.
+constexpr int kTransTiles = 4;
+
 __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, int b, const float* s_code,
                                                        float* s_ahat, uint16_t* tile) {
     const int tid = threadIdx.x;
     const int tiles_i = static_cast<int>(a.d_in / 64);
-    const int64_t i0 = static_cast<int64_t>(b % tiles_i) * 64;
-    const int64_t o0 = static_cast<int64_t>(b / tiles_i) * 64;
+    const int regions_i = (tiles_i + a.trans_tiles - 1) / a.trans_tiles;
+    const int t0 = (b % regions_i) * a.trans_tiles;          // first tile of the region
+    const int nt = min(a.trans_tiles, tiles_i - t0);
+    const int64_t o0 = static_cast<int64_t>(b / regions_i) * 64;
     const int ol = tid >> 2;             // local row o (becomes the output column)
-    const int q4 = tid & 3;              // which 16 of the 64 columns
+    const int q4 = tid & 3;              // which 16 of a tile's 64 columns
     const int64_t o = min(o0 + ol, a.d_out - 1);
-    const int64_t e0 = o * a.d_in + i0 + q4 * 16;
-    const uint2 cw = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
-    if (tid < 64) {
-        const int64_t blk = (min(o0 + tid, a.d_out - 1) * a.d_in + i0) >> 6;
-        s_ahat[tid] = block_constant(a.bc.fmt, a.bc.q[blk], a.bc.scale[blk >> a.bc.gshift], a.bc.mean[0]);
-    }
-    __syncthreads();
-    const float ahat = s_ahat[ol];
+    uint2 cw[kTransTiles];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const uint32_t word = e < 8 ? cw.x : cw.y;
-        tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
+    for (int k = 0; k < kTransTiles; ++k) {
+        const int64_t e0 = o * a.d_in + static_cast<int64_t>(t0 + min(k, nt - 1)) * 64 + q4 * 16;
+        cw[k] = *reinterpret_cast<const uint2*>(a.codes + (e0 >> 1));
+    }
+    {
+        const int64_t ob = min(o0 + (tid >> 2), a.d_out - 1);
+        const int64_t blk = (ob * a.d_in + static_cast<int64_t>(t0 + min(tid & 3, nt - 1)) * 64) >> 6;
+        s_ahat[tid] = block_constant(a.bc.fmt, a.bc.q[blk], a.bc.scale[blk >> a.bc.gshift], a.bc.mean[0]);
     }
     __syncthreads();
     const int il = tid >> 2;
     const int seg = (tid & 3) * 16;
-    const int64_t i = i0 + il;
     const int64_t oc = o0 + seg;
-    if (oc < a.d_out) {                  // d_out % 64 == 0 on this path: whole 16-wide segments
-        const uint4* src = reinterpret_cast<const uint4*>(&tile[il * kTP + seg]);
-        uint4* dst = reinterpret_cast<uint4*>(a.what + i * a.d_out + oc);
-        dst[0] = src[0];
-        dst[1] = src[1];
+    for (int k = 0; k < nt; ++k) {
+        if (k > 0) __syncthreads();      // the previous tile has been written out
+        const float ahat = s_ahat[ol * kTransTiles + k];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t word = e < 8 ? cw[k].x : cw[k].y;
+            tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
+        }
+        __syncthreads();
+        const int64_t i = static_cast<int64_t>(t0 + k) * 64 + il;
+        if (oc < a.d_out) {              // d_out % 64 == 0 on this path: whole 16-wide segments
+            const uint4* src = reinterpret_cast<const uint4*>(&tile[il * kTP + seg]);
+            uint4* dst = reinterpret_cast<uint4*>(a.what + i * a.d_out + oc);
+            dst[0] = src[0];
+            dst[1] = src[1];
+        }
     }
 }
 
@@ -294,11 +310,11 @@ void prologue_kernel(PrologueArgs a, NF4Tables tab) {
         return;
     }
     float* s_code = reinterpret_cast<float*>(lds);             // 16 floats
-    float* s_ahat = reinterpret_cast<float*>(lds + 64);        // up to 128 floats
+    float* s_ahat = reinterpret_cast<float*>(lds + 64);        // up to 256 floats
     if (threadIdx.x < 16) s_code[threadIdx.x] = tab.code[threadIdx.x];
     const int bd = b - a.n_pre - a.n_adapt;
     if (a.transposed)
-        dequant_transposed_job(a, bd, s_code, s_ahat, reinterpret_cast<uint16_t*>(lds + 64 + 512));
+        dequant_transposed_job(a, bd, s_code, s_ahat, reinterpret_cast<uint16_t*>(lds + 64 + 1024));
     else
         dequant_rows_job(a, bd, s_code, s_ahat);
 }
@@ -348,11 +364,13 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
     a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
+    a.trans_tiles = static_cast<int>(std::min<int64_t>(kTransTiles, std::max<int64_t>(1, (n / 4096) / 2048)));
     a.n_deq = what == nullptr ? 0   // pre-pass (and adapter layout) only
-                              : static_cast<int>(transposed ? (d_in / 64) * ((d_out + 63) / 64)
+                              : static_cast<int>(transposed ? (d_in / 64 + a.trans_tiles - 1) / a.trans_tiles *
+                                                                  ((d_out + 63) / 64)
                                                             : (n + kDeqPerWG - 1) / kDeqPerWG);
     const int NT = (r + 31) / 32;
-    static_assert(64 + 512 + 64 * kTP * sizeof(uint16_t) <= sizeof(PreStage<1>::x), "dequant scratch fits a stage");
+    static_assert(64 + 1024 + 64 * kTP * sizeof(uint16_t) <= sizeof(PreStage<1>::x), "dequant scratch fits a stage");
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
     const NF4Tables& tab = tables();
     switch (NT) {
