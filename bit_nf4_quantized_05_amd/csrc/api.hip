@@ -104,11 +104,8 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
         off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * (d_out + w.r_pad), 256);
     w.gpart = off;                                                               // GEMM K-split partials (few tiles)
-    if (d_seq > qn::kSkinnyMaxTokens) {
-        const int64_t fwd = qn::gemm_splits(d_seq, d_out, d_in), bwd = qn::gemm_splits(d_seq, d_in, d_out);
-        const int64_t need = std::max(fwd > 1 ? fwd * d_out : 0, bwd > 1 ? bwd * d_in : 0) * d_seq * 4;
-        off += align_up(need, 256);
-    }
+    off += align_up(4 * std::max(d_seq > qn::kSkinnyMaxTokens ? qn::gemm_split_part_floats(d_seq, d_out, d_in) : 0,
+                                 qn::gemm_split_part_floats(d_seq, d_in, d_out)), 256);
     w.ppart = off;                                                               // pre-pass K-split partials
     off += align_up(std::max(d_seq > qn::kSkinnyMaxTokens ? prepass_part_bytes(d_seq, d_in, r) : 0,
                              prepass_part_bytes(d_seq, d_out, r)), 256);

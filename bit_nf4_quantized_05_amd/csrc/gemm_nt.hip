@@ -22,10 +22,11 @@
 // read under the last MFMAs. Tiles are handed to the 8 XCDs in contiguous ranges so
 // each XCD's L2 sees a compact block of P and Q panels.
 //
-// gemm_nt_split: the same body when there are at most 128 tiles (half the CUs): the
-// K-steps of P Q^T are split over S = 2..4 workgroups per tile, the LoRA K-steps go to
-// the last split, each split writes its fp32 partial tile, and gemm_split_reduce adds
-// the S partials in split order and rounds to bf16.
+// gemm_nt_split: the same body when the last round of tiles would leave most CUs idle
+// (T tiles, T mod 256 <= 128): the first 256 floor(T / 256) tiles run whole, and the
+// K-steps of each of the R = T mod 256 others are split over S = min(4, 256 / R)
+// workgroups (the LoRA K-steps go to the last split), each writing its fp32 partial
+// tile; gemm_split_reduce adds a tile's S partials in split order and rounds to bf16.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -64,8 +65,19 @@ struct GemmArgs {
     const uint16_t* Q2; int64_t ldq2; int kt2;
     uint16_t* C; int64_t ldc; int M, N, tiles_m, tiles_n;
     uint32_t bytesP, bytesQ, bytesP2, bytesQ2;   // buffer extents for the load descriptors
-    float* part; int splits, kper;               // split path: partials [splits][M][N], K-steps per split
+    float* part; int splits, kper;               // split path: partials [splits][rem][256 x 256], K-steps per split
+    int full, rem;                               // split path: whole tiles, then rem split tiles
 };
+
+// logical tile index -> (tile row, tile column): grouped raster of kGroupM tile rows
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int logical, int& tm, int& tn) {
+    const int gsize = kGroupM * g.tiles_n;
+    const int grp = logical / gsize;
+    const int first_m = grp * kGroupM;
+    const int gm = min(g.tiles_m - first_m, kGroupM);
+    tm = first_m + (logical % gsize) % gm;
+    tn = (logical % gsize) / gm;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -94,17 +106,18 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     const int wm = wave / WN, wn = wave % WN;
     const int M = g.M, N = g.N;
 
-    // ---- tile assignment: contiguous logical ranges per XCD, grouped raster
-    const int T = g.tiles_m * g.tiles_n;
-    const int w = kSplit ? static_cast<int>(blockIdx.x) % T : static_cast<int>(blockIdx.x);
-    const int sk = kSplit ? static_cast<int>(blockIdx.x) / T : 0;   // split of this workgroup
-    const int logical = (T % 8 == 0) ? (w & 7) * (T >> 3) + (w >> 3) : w;
-    const int gsize = kGroupM * g.tiles_n;
-    const int grp = logical / gsize;
-    const int first_m = grp * kGroupM;
-    const int gm = min(g.tiles_m - first_m, kGroupM);
-    const int tm = first_m + (logical % gsize) % gm;
-    const int tn = (logical % gsize) / gm;
+    // ---- tile assignment: contiguous logical ranges per XCD, grouped raster. On the
+    // split path, workgroups [0, full) take whole tiles, the rest (tile full + j % rem,
+    // split j / rem) the split ones.
+    const int bid = static_cast<int>(blockIdx.x);
+    const bool split_wg = kSplit && bid >= g.full;
+    const int T = kSplit ? g.full : g.tiles_m * g.tiles_n;
+    const int w = split_wg ? 0 : bid;
+    const int sj = split_wg ? bid - g.full : 0;
+    const int sk = split_wg ? sj / g.rem : 0;                          // split of this workgroup
+    const int logical = split_wg ? g.full + sj % g.rem : ((T % 8 == 0) ? (w & 7) * (T >> 3) + (w >> 3) : w);
+    int tm, tn;
+    tile_coords(g, logical, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
     // ---- global -> LDS with buffer_load ... lds (16 B per lane). A tile row is 64
@@ -137,9 +150,9 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
     const __amdgpu_buffer_rsrc_t rsQ2 = make_rsrc(g.Q2, g.bytesQ2);
     // K-steps of this workgroup: main steps [kb, ke) of P Q^T, then (last split, or no
     // split) the kt2 LoRA steps; step k of the loop is global step kb + k while k < ke - kb
-    const int kb = kSplit ? sk * g.kper : 0;
-    const int ke = kSplit ? min(kb + g.kper, g.kt1) : g.kt1;
-    const bool lora = !kSplit || sk == g.splits - 1;
+    const int kb = split_wg ? sk * g.kper : 0;
+    const int ke = split_wg ? min(kb + g.kper, g.kt1) : g.kt1;
+    const bool lora = !split_wg || sk == g.splits - 1;
     const int KT = (ke - kb) + (lora ? g.kt2 : 0);
     const int kshift = kb;                      // global main step = local + kshift
     const int kmain = ke - kb;
@@ -230,21 +243,20 @@ __device__ __forceinline__ void gemm_nt_body(const GemmArgs& g) {
 #undef QN_FRAGS
 #undef QN_ISSUE
 
-    if constexpr (kSplit) {
-        // fp32 partial tile of this split: the lane's 4 consecutive n of row m as 16 bytes
-        float* pt = g.part + static_cast<int64_t>(sk) * M * N;
+    if (split_wg) {
+        // fp32 partial tile of this split, compact 256 x 256: the lane's 4 consecutive n
+        // of tile row ml as 16 bytes
+        float* pt = g.part + (static_cast<int64_t>(sk) * g.rem + sj % g.rem) * (BM * BN);
 #pragma unroll
         for (int b = 0; b < TM; ++b) {
-            const int m = m0 + wm * (TM * 32) + b * 32 + static_cast<int>(frow);
+            const int ml = wm * (TM * 32) + b * 32 + static_cast<int>(frow);
 #pragma unroll
             for (int a = 0; a < TN; ++a) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int n = n0 + wn * (TN * 32) + a * 32 + 8 * gq + 4 * (lane >> 5);
-                    if (m < M && n < N)
-                        *reinterpret_cast<float4*>(pt + static_cast<int64_t>(m) * N + n) =
-                            float4{acc[a][b][4 * gq], acc[a][b][4 * gq + 1], acc[a][b][4 * gq + 2],
-                                   acc[a][b][4 * gq + 3]};
+                    const int nl = wn * (TN * 32) + a * 32 + 8 * gq + 4 * (lane >> 5);
+                    *reinterpret_cast<float4*>(pt + ml * BN + nl) =
+                        float4{acc[a][b][4 * gq], acc[a][b][4 * gq + 1], acc[a][b][4 * gq + 2], acc[a][b][4 * gq + 3]};
                 }
             }
         }
@@ -304,32 +316,48 @@ void gemm_nt_split(GemmArgs g) {
     gemm_nt_body<kGemmWM, kGemmWN, true>(g);
 }
 
-// C[m, n..n+3] = bf16(sum over splits in order), 4 outputs per thread (N % 4 == 0)
+// Split tiles: C[m, n..n+3] = bf16(sum of the tile's partials in split order), 4 outputs
+// per thread; 64 workgroups per tile (4 rows each).
 __global__ __launch_bounds__(256)
-void gemm_split_reduce(const float* __restrict__ part, int splits, int64_t MN, int N, uint16_t* __restrict__ C,
-                       int64_t ldc) {
-    const int64_t e = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
-    if (e >= MN) return;
+void gemm_split_reduce(GemmArgs g) {
+    const int j = static_cast<int>(blockIdx.x) / 64;                  // split tile
+    const int ml = (static_cast<int>(blockIdx.x) % 64) * 4 + (threadIdx.x >> 6);
+    const int nl = (threadIdx.x & 63) * 4;
+    int tm, tn;
+    tile_coords(g, g.full + j, tm, tn);
+    const int m = tm * BM + ml, n = tn * BN + nl;
+    if (m >= g.M || n >= g.N) return;
+    const float* p = g.part + static_cast<int64_t>(j) * (BM * BN) + ml * BN + nl;
+    const int64_t stride = static_cast<int64_t>(g.rem) * (BM * BN);
     float4 v[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-        v[s] = s < splits ? *reinterpret_cast<const float4*>(part + s * MN + e) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float4*>(p + min(s, g.splits - 1) * stride);
     float4 t = v[0];
 #pragma unroll
-    for (int s = 1; s < 4; ++s) {
-        if (s < splits) { t.x += v[s].x; t.y += v[s].y; t.z += v[s].z; t.w += v[s].w; }
-    }
-    const int64_t m = e / N, n = e % N;
-    *reinterpret_cast<uint2*>(C + m * ldc + n) = uint2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
+    for (int s = 1; s < 4; ++s)
+        if (s < g.splits) { t.x += v[s].x; t.y += v[s].y; t.z += v[s].z; t.w += v[s].w; }
+    *reinterpret_cast<uint2*>(g.C + static_cast<int64_t>(m) * g.ldc + n) =
+        uint2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
 }
 
 }  // namespace
 
-int gemm_splits(int64_t M, int64_t N, int64_t K1) {
+GemmSplit gemm_split(int64_t M, int64_t N, int64_t K1) {
     const int64_t T = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    if (T > 128) return 1;
-    const int64_t s = std::min<int64_t>({4, 256 / T, K1 / BK / 8});   // at least 8 K-steps per split
-    return static_cast<int>(std::max<int64_t>(1, s));
+    const int64_t rem = T % 256;
+    GemmSplit gs{1, static_cast<int>(T), 0};
+    if (rem == 0 || rem > 128) return gs;
+    const int64_t s = std::min<int64_t>({4, 256 / rem, K1 / BK / 8});    // at least 8 K-steps per split
+    if (s < 2) return gs;
+    gs.splits = static_cast<int>(s);
+    gs.full = static_cast<int>(T - rem);
+    gs.rem = static_cast<int>(rem);
+    return gs;
+}
+
+int64_t gemm_split_part_floats(int64_t M, int64_t N, int64_t K1) {
+    const GemmSplit gs = gemm_split(M, N, K1);
+    return gs.splits > 1 ? static_cast<int64_t>(gs.splits) * gs.rem * BM * BN : 0;
 }
 
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
@@ -348,7 +376,10 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.bytesQ = static_cast<uint32_t>(2 * ldq * N);
     g.bytesP2 = static_cast<uint32_t>(2 * ldp2 * M);
     g.bytesQ2 = static_cast<uint32_t>(2 * ldq2 * N);
-    g.splits = gemm_splits(M, N, K1);
+    const GemmSplit gs = gemm_split(M, N, K1);
+    g.splits = gs.splits;
+    g.full = gs.full;
+    g.rem = gs.rem;
     g.kper = (g.kt1 + g.splits - 1) / g.splits;
     g.part = part;
     if (g.splits <= 1 || part == nullptr) {
@@ -357,11 +388,9 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
                   st, g);
         return hipGetLastError();
     }
-    QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.tiles_m * g.tiles_n * g.splits),
-              dim3(64 * kGemmWM * kGemmWN), 0, st, g);
-    const int64_t MN = M * N;
-    QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce, dim3(static_cast<unsigned>((MN / 4 + 255) / 256)), dim3(256),
-              0, st, part, g.splits, MN, static_cast<int>(N), C, ldc);
+    QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.full + g.rem * g.splits), dim3(64 * kGemmWM * kGemmWN), 0,
+              st, g);
+    QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce, dim3(static_cast<unsigned>(g.rem * 64)), dim3(256), 0, st, g);
     return hipGetLastError();
 }
 

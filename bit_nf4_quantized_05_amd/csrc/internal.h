@@ -63,11 +63,13 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const BlockConsts& bc, int6
 
 // ---- gemm_nt.hip ----
 // C[M,N] = bf16( P[M,K1] Q[N,K1]^T + P2[M,K2] Q2[N,K2]^T ), all row-major, K contiguous.
-// K1, K2 multiples of 64 (K2 may be 0); N multiple of 4. With at most 128 output tiles
-// the K-steps are split over gemm_splits(M, N, K1) workgroups per tile, whose fp32
-// partials go to part (gemm_splits * M * N floats, C contiguous: ldc == N); a null
-// part runs unsplit.
-int gemm_splits(int64_t M, int64_t N, int64_t K1);
+// K1, K2 multiples of 64 (K2 may be 0); N multiple of 4. When the last round of
+// 256 x 256 tiles holds at most 128 tiles, their K-steps are split over gemm_split().splits
+// workgroups each, with fp32 partials in part (gemm_split_part_floats(M, N, K1) floats);
+// a null part runs unsplit.
+struct GemmSplit { int splits, full, rem; };
+GemmSplit gemm_split(int64_t M, int64_t N, int64_t K1);
+int64_t gemm_split_part_floats(int64_t M, int64_t N, int64_t K1);
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
                           int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N, float* part,

@@ -208,6 +208,34 @@ def test_small_batch_forward_full_layer():
     _fwd_bwd_full_check(cfg, check_bwd=False)
 
 
+# Every path must stay inside the workspace size the library reports: the workspace is
+# allocated with a guard region behind it, filled with a pattern that must survive the
+# forward and input-gradient calls (covers the GEMV, small-batch, whole and split GEMMs
+# and the K-split pre-pass).
+GUARD_CASES = [(4096, 4096, 1, 16), (4096, 4096, 16, 16), (256, 2048, 65, 8), (512, 4096, 200, 16),
+               (4096, 512, 130, 64), (1536, 1536, 300, 33), (320, 192, 300, 100), (11008, 4096, 2048, 64)]
+
+
+@pytest.mark.parametrize("shape", GUARD_CASES, ids=[f"{a}x{b}_t{c}_r{d}" for a, b, c, d in GUARD_CASES])
+def test_calls_stay_inside_reported_workspace(shape):
+    d_out, d_in, d_seq, r = shape
+    _say(f"[workspace guard] {d_out}x{d_in} d_seq={d_seq} r={r}")
+    cfg = WL.custom("g", d_out, d_in, d_seq, r)
+    q = _gpu_quantize(_normal((d_out, d_in), 21))
+    a, b = WL.make_lora(cfg)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    need = qn.linear_workspace_bytes(d_out, d_in, d_seq, r)
+    guard = 1 << 20
+    buf = torch.full((need + guard,), 0xAB, dtype=torch.uint8, device=dev())
+    ws = buf[:need]
+    X = torch.randn(d_seq, d_in, device=dev()).to(torch.bfloat16)
+    dY = torch.randn(d_seq, d_out, device=dev()).to(torch.bfloat16)
+    qn.linear_fwd(q, A, B, cfg.s, X, workspace=ws)
+    qn.linear_bwd_x(q, A, B, cfg.s, dY, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xAB).all()), "a call wrote past the reported workspace"
+
+
 def test_identity_input_returns_dequantised_weight_exactly():
     cfg = WL.custom("eye", 192, 256, 256, 8)
     w, a, b = _layer(cfg)
