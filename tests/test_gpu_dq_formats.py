@@ -91,8 +91,8 @@ def test_e4m3_stress_weight_hits_ties():
 
 
 LINEAR = [
-    WL.custom("f_gemv_staged", 256, 1024, 1, 16, s=2.0),      # constants staged per workgroup
-    WL.custom("f_gemv_ragged", 192, 4160, 1, 3, s=1.0),       # constants loaded per lane
+    WL.custom("f_gemv", 256, 1024, 1, 16, s=2.0),             # one 4096-weight segment per row
+    WL.custom("f_gemv_ragged", 192, 4160, 1, 3, s=1.0),       # two segments, the last 64 wide
     WL.custom("f_sb_9", 256, 4160, 9, 8, s=2.0),
     WL.custom("f_sb_40", 128, 2048, 40, 64, s=1.0, outlier_frac=0.01),
     WL.custom("f_gemm", 320, 512, 200, 16, s=1.5),
