@@ -273,10 +273,13 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
         s_ahat[tid] = block_constant(a.bc.fmt, a.bc.q[blk], a.bc.scale[blk >> a.bc.gshift], a.bc.mean[0]);
     }
     __syncthreads();
-    const int il = tid >> 2;
-    const int seg = (tid & 3) * 16;
-    const int64_t oc = o0 + seg;
-    for (int k = 0; k < nt; ++k) {
+    // write-out: the tile is 64 rows of 128 B = 512 chunks of 16 B; store u of thread t
+    // takes chunk 256 u + t, so 8 consecutive lanes write one whole 128-byte row.
+    // The loop runs to the constant kTransTiles so that cw[k] has a constant index
+    // (a runtime index would put cw in scratch memory); nt is uniform per workgroup.
+#pragma unroll
+    for (int k = 0; k < kTransTiles; ++k) {
+        if (k >= nt) break;
         if (k > 0) __syncthreads();      // the previous tile has been written out
         const float ahat = s_ahat[ol * kTransTiles + k];
 #pragma unroll
@@ -285,12 +288,15 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
             tile[(q4 * 16 + e) * kTP + ol] = bf16_bits(s_code[(word >> (4 * (e & 7))) & 0xFu] * ahat);
         }
         __syncthreads();
-        const int64_t i = static_cast<int64_t>(t0 + k) * 64 + il;
-        if (oc < a.d_out) {              // d_out % 64 == 0 on this path: whole 16-wide segments
-            const uint4* src = reinterpret_cast<const uint4*>(&tile[il * kTP + seg]);
-            uint4* dst = reinterpret_cast<uint4*>(a.what + i * a.d_out + oc);
-            dst[0] = src[0];
-            dst[1] = src[1];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = 256 * u + tid;
+            const int il = c >> 3;           // tile row = output row i - 64 (t0 + k)
+            const int cc = c & 7;            // 16-byte chunk: output columns o0 + 8 cc .. + 7
+            const int64_t i = static_cast<int64_t>(t0 + k) * 64 + il;
+            if (o0 + 8 * cc < a.d_out)       // d_out % 64 == 0 on this path: whole chunks
+                *reinterpret_cast<uint4*>(a.what + i * a.d_out + o0 + 8 * cc) =
+                    *reinterpret_cast<const uint4*>(&tile[il * kTP + 8 * cc]);
         }
     }
 }
@@ -313,10 +319,15 @@ void prologue_kernel(PrologueArgs a, NF4Tables tab) {
     float* s_ahat = reinterpret_cast<float*>(lds + 64);        // up to 256 floats
     if (threadIdx.x < 16) s_code[threadIdx.x] = tab.code[threadIdx.x];
     const int bd = b - a.n_pre - a.n_adapt;
-    if (a.transposed)
-        dequant_transposed_job(a, bd, s_code, s_ahat, reinterpret_cast<uint16_t*>(lds + 64 + 1024));
-    else
+    if (a.transposed) {
+        // Workgroups go to the 8 XCDs in turn; a code row's 128-byte line spans several
+        // neighbouring regions, so each XCD takes a contiguous range of regions and a
+        // line is fetched into one XCD's L2 rather than into several.
+        const int bl = (a.n_deq & 7) == 0 ? (bd & 7) * (a.n_deq >> 3) + (bd >> 3) : bd;
+        dequant_transposed_job(a, bl, s_code, s_ahat, reinterpret_cast<uint16_t*>(lds + 64 + 1024));
+    } else {
         dequant_rows_job(a, bd, s_code, s_ahat);
+    }
 }
 
 // ---------------------------------------------------------------------------
