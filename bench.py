@@ -57,21 +57,23 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "gemm_nt_kernel_4096x4096x4160_traffic.md")
-GEMM_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_nf4_quantized_05_amd", "csrc",
-                           "gemm_nt.hip")
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+# counter summaries under profiles/ and the kernel source each was measured with
+GEMM_TRAFFIC = ("gemm_nt_kernel_4096x4096x4160_traffic.md", "gemm_nt.hip")
+DECODE_TRAFFIC = ("gemv_nf4_kernel_4096x4096_decode_traffic.md", "gemv.hip")
 
 
-def measured_traffic():
-    """HBM bytes per GEMM launch from the committed counter summary, or None when the
-    GEMM source has changed since the counters were taken (the summary records the
-    SHA-256 of gemm_nt.hip it was measured with)."""
+def measured_traffic(which):
+    """HBM bytes per launch (per call for the decode pair) from a committed counter
+    summary, or None when the kernel source has changed since the counters were taken
+    (the summary records the SHA-256 of the source file it was measured with)."""
     import hashlib
     import re
+    profile, source = which
     try:
-        text = open(TRAFFIC_FILE).read()
-        src_hash = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+        text = open(os.path.join(_ROOT, "profiles", profile)).read()
+        src = os.path.join(_ROOT, "bit_nf4_quantized_05_amd", "csrc", source)
+        src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
     h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
@@ -305,7 +307,7 @@ def main():
     achieved = gemm_flops / (g_ms / g_n * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": "gemm_nt_kernel", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic()}
+                "traffic": measured_traffic(GEMM_TRAFFIC)}
 
     # ---- decode (d_seq = 1) over rotated layer copies
     log(f"[bench] decode: {args.decode_iters} calls over {len(copies)} copies")
@@ -332,7 +334,7 @@ def main():
               "roofline": {"bound": "hbm", "kernel": "gemv_nf4_kernel + lora_ax_partial_kernel",
                            "achieved": round(nbytes / (kern_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
                            "unit": "GB/s", "frac": round(nbytes / (kern_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                           "traffic": None}}
+                           "traffic": measured_traffic(DECODE_TRAFFIC)}}
 
     # ---- adapter gradients (dA, dB) of the same layer, outside the timed step
     log(f"[bench] adapter gradients: {args.steps} calls")
