@@ -12,12 +12,16 @@ namespace qn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// d_seq = 1 (decode), two launches:
+// d_seq = 1 (decode). When all of A fits one 4096-column segment with r <= 16
+// (A <= 128 KB, read from L2 by every workgroup), one launch: each gemv_nf4
+// workgroup forms s A x itself, wave j the dot product of row j of A with the x
+// segment it has staged in LDS anyway. Otherwise two launches:
 //   lora_ax_partial: the 64-column blocks of x are split into nparts contiguous
 //     slices (nparts * r <= 1024); workgroup w writes, for every rank row j, the dot
 //     product of A[j] and x over slice w to part[w][j] (fixed summation order).
 //   gemv_nf4: streams the packed codes once and adds B (s A x), summing the slice
-//     partials in a fixed order: y = W_hat x + B (s A x). Deterministic.
+//     partials in a fixed order: y = W_hat x + B (s A x).
+// Both are deterministic, and every workgroup forms the same s A x bits.
 // ---------------------------------------------------------------------------
 constexpr int kAxMaxParts = 16;
 
@@ -111,11 +115,12 @@ __device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv,
 // chunks 4 l .. 4 l + 3; their order is XORed with bits 2..3 of l
 __device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c >> 4) & 3)); }
 
+template <bool kAx>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                      int d_out, int d_in, const uint16_t* __restrict__ x,
                      const uint16_t* __restrict__ B, int r, float s, const float* __restrict__ part,
-                     int nparts, uint16_t* __restrict__ y, NF4Tables tab) {
+                     int nparts, const uint16_t* __restrict__ A, uint16_t* __restrict__ y, NF4Tables tab) {
     __shared__ uint4 lut4[256 * kLutCopies / 4];
     __shared__ uint4 xs[2][kGvSeg / 8];
     __shared__ float tvs[1024];
@@ -163,8 +168,18 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     stage_issue(st, 0);
     const int nval = nparts * r;                  // <= 1024
     uint4 tst = uint4{0, 0, 0, 0};
-    if (wave >= 10 && wave < 14)
-        tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nval + 3) / 4 - 1)];
+    // one-launch form: wave j loads row j of A (rows past r repeat row r - 1 and are not
+    // used), lane l the 16-byte chunks l + 64 e, so each load is 1 KB contiguous
+    const int nch = d_in / 8;                     // 16-byte chunks of a row (d_in <= 4096)
+    uint4 av[8];
+    if constexpr (kAx) {
+        const uint4* ar = reinterpret_cast<const uint4*>(A) + static_cast<int64_t>(min(wave, r - 1)) * nch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = ar[min(lane + 64 * e, nch - 1)];
+    } else {
+        if (wave >= 10 && wave < 14)
+            tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nval + 3) / 4 - 1)];
+    }
     const int nbv = 2 * r;                        // 16-byte pieces of the 16 rows of B
     const uint4* b4 = reinterpret_cast<const uint4*>(B + static_cast<int64_t>(row0) * r);
     uint4 bst[8];
@@ -196,18 +211,39 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
         qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));      // T[q] at q + 128
     }
     stage_store(st, 0);
-    if (wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
+    if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
     if (wave == 14) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             if (lane + 64 * i < nbv) bs[lane + 64 * i] = bst[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // s (A x), summed per rank row in slice order
-    if (tid < r) {
+    if constexpr (kAx) {
+        // s (A x) of rank row `wave`: 8 chunk dot products per lane, then a fixed xor tree
         float t = 0.0f;
-        for (int p = 0; p < nparts; ++p) t += tvs[p * r + tid];
-        s_t[tid] = s * t;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = lane + 64 * e;
+            if (c < nch) {
+                const uint4 xv = xs[0][gv_xpos(c)];
+                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                        __builtin_bit_cast(bf16x2, xw[q]), t, false);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+        if (lane == 0 && wave < r) s_t[wave] = s * t;
+    } else {
+        // s (A x), summed per rank row in slice order
+        if (tid < r) {
+            float t = 0.0f;
+            for (int p = 0; p < nparts; ++p) t += tvs[p * r + tid];
+            s_t[tid] = s * t;
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -263,6 +299,14 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
+    if (r <= kGvWaves && d_in <= kGvSeg) {
+        // one launch: every workgroup forms s A x from A (r x d_in <= 16 x 4096 bf16)
+        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<true>, grid, dim3(64 * kGvWaves), 0, st,
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B,
+                  r, s, ws_part, 0, A, y, tables());
+        return hipGetLastError();
+    }
     // slices of A x: at most 16, and nparts * r <= 1024 partials in all
     const int nb64 = static_cast<int>(d_in / 64);
     const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / r}));
@@ -270,10 +314,9 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     const int nparts = (nb64 + per - 1) / per;   // <= want
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
-    const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
-    QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel, grid, dim3(64 * kGvWaves), 0, st,
+    QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<false>, grid, dim3(64 * kGvWaves), 0, st,
               reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B,
-              r, s, ws_part, nparts, y, tables());
+              r, s, ws_part, nparts, A, y, tables());
     return hipGetLastError();
 }
 

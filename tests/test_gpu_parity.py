@@ -167,6 +167,11 @@ LINEAR_SMALL = [
     WL.custom("gemv_r64", 512, 1024, 1, 64, s=1.0),
     WL.custom("gemv_ragged", 320, 4160, 1, 3, s=2.0),       # 3 column chunks, the last 64 wide
     WL.custom("gemv_wide", 128, 11008, 1, 256, s=0.5),      # 6 column chunks, r = 256
+    # one launch forms A x in every workgroup when r <= 16 and d_in <= 4096; else two launches
+    WL.custom("gemv_one_r1_k64", 64, 64, 1, 1, s=2.0),
+    WL.custom("gemv_one_r16_k4096", 192, 4096, 1, 16, s=1.5),
+    WL.custom("gemv_one_r5_k960", 320, 960, 1, 5, s=0.5),
+    WL.custom("gemv_two_r17_k4096", 192, 4096, 1, 17, s=1.5),
     # at most 128 output tiles: the GEMM splits K over 2..4 workgroups per tile
     WL.custom("split_fwd", 512, 4096, 200, 16, s=2.0),       # fwd 2 tiles -> 4 splits
     WL.custom("split_bwd", 4096, 512, 130, 64, s=1.0),       # dX 2 tiles -> 4 splits, ragged tokens
