@@ -212,7 +212,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
     const bool pad = r != lw.r_pad;
     // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
     if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
-                                 A, d_in, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r,
+                                 A, d_in, false, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r,
                                  reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
     if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
@@ -401,12 +401,13 @@ int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const floa
     uint16_t* atpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
     uint16_t* bt = reinterpret_cast<uint16_t*>(ws + lw.adapt2);
     hipError_t e;
-    // B^T (the pre-pass needs K-contiguous rows of B^T)
-    if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
+    // the pre-pass reads B itself (k-major) where it can; else K-contiguous rows of B^T
+    const bool km = qn::prepass_takes_kmajor(r);
+    if (!km && (e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (B^T)");
     // dequant W_hat^T + U = s (dY B) + A^T padded to r_pad columns, in one launch
     if ((e = qn::launch_prologue(codes, bc, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
-                                 bt, d_out, r, s, u, lw.r_pad, 2, A, atpad, r, d_in,
+                                 km ? B : bt, d_out, km, r, s, u, lw.r_pad, 2, A, atpad, r, d_in,
                                  reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (prologue)");
     if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
@@ -518,14 +519,15 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const
     hipError_t e;
     // T' = bf16(s X A^T): the forward's pre-pass, without the dequantisation
     if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, X, d_in, d_seq,
-                                 d_in, A, d_in, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0,
+                                 d_in, A, d_in, false, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0,
                                  reinterpret_cast<float*>(ws + gw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (X A^T)");
-    // U' = bf16(s dY B): the input gradient's pre-pass on B^T
-    if ((e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
+    // U' = bf16(s dY B): the input gradient's pre-pass, on B itself where it can, else on B^T
+    const bool km = qn::prepass_takes_kmajor(r);
+    if (!km && (e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (B^T)");
     if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, dY, d_out,
-                                 d_seq, d_out, bt, d_out, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0,
+                                 d_seq, d_out, km ? B : bt, d_out, km, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0,
                                  reinterpret_cast<float*>(ws + gw.ppart), st)) !=
         hipSuccess)
         return hip_fail(e, "qlora_lora_grads (dY B)");

@@ -89,9 +89,13 @@ PrepassSplit prepass_split(int64_t M, int64_t K);
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
-                           const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
-                           int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
+                           const uint16_t* R, int64_t ldr, bool r_kmajor, int r, float s, uint16_t* OUT,
+                           int r_pad, int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
                            int64_t acols, float* ppart, hipStream_t st);
+// The pre-pass can take R k-major, as B [K, r] itself (r % 8 == 0 and r <= 32: one
+// 32-rank MFMA tile, whose transposing reads keep the kernel's occupancy), which spares
+// the input gradient a transpose of B.
+inline bool prepass_takes_kmajor(int r) { return r % 8 == 0 && r <= 32; }
 // dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);

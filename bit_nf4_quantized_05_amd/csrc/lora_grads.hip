@@ -75,11 +75,6 @@ __device__ __forceinline__ void grad_issue(GradTile& t, const GradJob& jb, const
     load_lds16(jb.T + mg * g.r_pad + j0 + 8 * ((lane & 7) ^ swz(row)), &t.T[wave * 64]);
 }
 
-// LDS byte address of a pointer into a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
-}
-
 // All transposing reads of one 32-token step in one asm block that ends with its own
 // wait (so no read is in flight when the block ends). The swizzle depends on the row
 // only through row % 4, so the reads of a lane differ by constant row offsets: 4 rows

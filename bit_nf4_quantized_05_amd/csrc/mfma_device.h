@@ -30,6 +30,11 @@ static __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
     return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
+// LDS byte address of a pointer into a __shared__ object
+static __device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+
 // s_waitcnt vmcnt(n) (n < 64; vmcnt is bits [3:0] and [15:14]), other counters untouched
 #define QN_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 0x3) << 14) | (0x7 << 4) | (0xF << 8))
 

@@ -31,7 +31,7 @@ struct PrologueArgs {
     int transposed;                 // dequant to W_hat^T [d_in, d_out] instead of W_hat
     uint16_t* what;
     const uint16_t* P; int64_t ldp; int M, K;
-    const uint16_t* R; int64_t ldr; int r; float s;
+    const uint16_t* R; int64_t ldr; int r; float s;   // R [r, K] row stride ldr, or k-major [K, r]
     uint16_t* OUT; int r_pad;
     int adapt_mode;                 // 0 none, 1 pad columns, 2 transpose + pad
     const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
@@ -52,13 +52,19 @@ constexpr int kTP = 64 + 8;                      // LDS pitch (bf16) of the tran
 // the 32-row MFMA fragment reads free of bank conflicts. D = R P^T per 32x32 tile:
 // rank rows, token columns. Rows of R past r and tokens past M are clamped into the
 // arrays; their results are not stored (ranks past r are written as 0).
+// With R given k-major (R^T = B [K, r] of the input gradient, r % 8 == 0, r <= 32),
+// the chunk is fetched as 64 k-rows of 32 NT ranks (pieces past r repeat a valid
+// address; their ranks are not stored) and each lane's fragment of 8 consecutive k is
+// gathered by ds_read_b64_tr_b16, which hands lane p of a 16-lane group column p of
+// a 4 x 16 block: two reads give rows k .. k + 7. This replaces a separate transpose
+// of B before the launch.
 template <int NT>
 struct PreStage {
     uint4 x[128 * 8];               // 128 token rows
     uint4 r[32 * NT * 8];           // 32 NT rank rows
 };
 
-template <int NT>
+template <int NT, bool KM>
 __device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& a, int wave, int lane, int m0,
                                           int kc) {
     const int64_t k0 = static_cast<int64_t>(kc) * 64;
@@ -70,32 +76,77 @@ __device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& 
         __builtin_amdgcn_global_load_lds((global_ptr)(a.P + m * a.ldp + k0 + 8 * c),
                                          (lds_ptr)(&st.x[(32 * wave + 8 * u) * 8]), 16, 0, 0);
     }
+    if constexpr (KM) {
+        // piece q = 64 (4 i + w) + lane of the [64 k][32 NT ranks] chunk: k-row q / (4 NT),
+        // ranks 8 (q % (4 NT)) .. +7 (pieces past r re-read the last valid one)
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {                     // R rows 8 (4 i + w) .. +7
-        const int row = 8 * (4 * i + wave) + (lane >> 3);
-        const int c = (lane & 7) ^ ((row >> 1) & 7);
-        const int64_t j = min(row, a.r - 1);
-        __builtin_amdgcn_global_load_lds((global_ptr)(a.R + j * a.ldr + k0 + 8 * c),
-                                         (lds_ptr)(&st.r[8 * (4 * i + wave) * 8]), 16, 0, 0);
+        for (int i = 0; i < NT; ++i) {
+            const int q = 64 * (4 * i + wave) + lane;
+            const int64_t k = k0 + q / (4 * NT);
+            const int pj = min(q % (4 * NT), a.r / 8 - 1);
+            __builtin_amdgcn_global_load_lds((global_ptr)(a.R + k * a.r + 8 * pj),
+                                             (lds_ptr)(&st.r[64 * (4 * i + wave)]), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {                 // R rows 8 (4 i + w) .. +7
+            const int row = 8 * (4 * i + wave) + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const int64_t j = min(row, a.r - 1);
+            __builtin_amdgcn_global_load_lds((global_ptr)(a.R + j * a.ldr + k0 + 8 * c),
+                                             (lds_ptr)(&st.r[8 * (4 * i + wave) * 8]), 16, 0, 0);
+        }
     }
 }
 
-template <int NT>
+#define QN_TR(d, a, off) "ds_read_b64_tr_b16 %" #d ", %" #a " offset:" #off "\n\t"
+
+// k-major R (one rank tile): the lane's fragments for the four k16 steps u, rows
+// k = 16 u + 8 (g4 / 2) + 4 h .. +3 (h = 0, 1) of ranks 16 (g4 % 2) + 4 (lane % 4) .. +3 per
+// address, all eight reads in one asm block ending with its own wait. The row pitch is
+// 32 ranks = 64 bytes, so the offsets are (16 u + 4 h) 64 bytes.
+__device__ __forceinline__ void pre_r_fragments(const PreStage<1>& st, int lane, uint4 (&rf)[4]) {
+    const int g4 = lane >> 4;
+    const uint32_t base = lds_addr(st.r) +
+        2 * ((8 * (g4 >> 1) + ((lane >> 2) & 3)) * 32 + 16 * (g4 & 1) + 4 * (lane & 3));
+    unsigned long long v[8];
+    asm volatile(QN_TR(0, 8, 0) QN_TR(1, 8, 256) QN_TR(2, 8, 1024) QN_TR(3, 8, 1280)
+                 QN_TR(4, 8, 2048) QN_TR(5, 8, 2304) QN_TR(6, 8, 3072) QN_TR(7, 8, 3328)
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+                   "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+                 : "v"(base)
+                 : "memory");
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const unsigned long long lo = v[2 * u], hi = v[2 * u + 1];
+        rf[u] = uint4{static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                      static_cast<uint32_t>(hi), static_cast<uint32_t>(hi >> 32)};
+    }
+}
+#undef QN_TR
+
+template <int NT, bool KM>
 __device__ __forceinline__ void pre_compute(const PreStage<NT>& st, int wave, int lane, f32x16 (&acc)[NT]) {
     const int frow = lane & 31;
     const int sw = (frow >> 1) & 7;                    // rows 32 w + frow and 32 t + frow share it
+    uint4 rf[4];
+    if constexpr (KM) {
+        static_assert(NT == 1, "k-major R: at most 32 ranks");
+        pre_r_fragments(st, lane, rf);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int c = (2 * u + (lane >> 5)) ^ sw;
         const uint4 xf = st.x[(32 * wave + frow) * 8 + c];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] = mfma32(st.r[(32 * t + frow) * 8 + c], xf, acc[t]);
+        for (int t = 0; t < NT; ++t) acc[t] = mfma32(KM ? rf[u] : st.r[(32 * t + frow) * 8 + c], xf, acc[t]);
     }
 }
 
 #define QN_PRE_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
-template <int NT>
+template <int NT, bool KM>
 __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreStage<NT>& s0, PreStage<NT>& s1) {
     constexpr int kLoads = 4 + NT;                     // direct loads per wave and stage
     const int lane = threadIdx.x & 63;
@@ -110,18 +161,18 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreSta
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     // The barriers wait for LDS traffic only; each wave first waits for its own loads
     // of the stage about to be read (loads complete in issue order).
-    pre_issue<NT>(s0, a, wave, lane, m0, kb);
+    pre_issue<NT, KM>(s0, a, wave, lane, m0, kb);
     for (int kc = kb; kc < ke; kc += 2) {
-        if (kc + 1 < ke) { pre_issue<NT>(s1, a, wave, lane, m0, kc + 1); QN_WAIT_VM(kLoads); }
+        if (kc + 1 < ke) { pre_issue<NT, KM>(s1, a, wave, lane, m0, kc + 1); QN_WAIT_VM(kLoads); }
         else QN_WAIT_VM(0);
         QN_PRE_BARRIER();
-        pre_compute<NT>(s0, wave, lane, acc);
+        pre_compute<NT, KM>(s0, wave, lane, acc);
         QN_PRE_BARRIER();
         if (kc + 1 >= ke) break;
-        if (kc + 2 < ke) { pre_issue<NT>(s0, a, wave, lane, m0, kc + 2); QN_WAIT_VM(kLoads); }
+        if (kc + 2 < ke) { pre_issue<NT, KM>(s0, a, wave, lane, m0, kc + 2); QN_WAIT_VM(kLoads); }
         else QN_WAIT_VM(0);
         QN_PRE_BARRIER();
-        pre_compute<NT>(s1, wave, lane, acc);
+        pre_compute<NT, KM>(s1, wave, lane, acc);
         QN_PRE_BARRIER();
     }
     // D of tile t: lane l holds ranks 32 t + 8 (v / 4) + 4 (l / 32) + v % 4 of token l % 32
@@ -301,14 +352,14 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
     }
 }
 
-template <int NT>
+template <int NT, bool KM>
 __global__ __launch_bounds__(256)
 void prologue_kernel(PrologueArgs a, NF4Tables tab) {
     __shared__ PreStage<NT> s0, s1;
     char* lds = reinterpret_cast<char*>(s1.x);             // 16 KB of scratch for the other jobs
     const int b = blockIdx.x;
     if (b < a.n_pre) {
-        prepass_job<NT>(a, b, s0, s1);
+        prepass_job<NT, KM>(a, b, s0, s1);
         return;
     }
     if (b < a.n_pre + a.n_adapt) {
@@ -358,8 +409,8 @@ PrepassSplit prepass_split(int64_t M, int64_t K) {
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
-                           const uint16_t* R, int64_t ldr, int r, float s, uint16_t* OUT, int r_pad,
-                           int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
+                           const uint16_t* R, int64_t ldr, bool r_kmajor, int r, float s, uint16_t* OUT,
+                           int r_pad, int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
                            int64_t acols, float* ppart, hipStream_t st) {
     PrologueArgs a;
     a.codes = codes; a.bc = bc;
@@ -384,13 +435,18 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
     static_assert(64 + 1024 + 64 * kTP * sizeof(uint16_t) <= sizeof(PreStage<1>::x), "dequant scratch fits a stage");
     const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
     const NF4Tables& tab = tables();
-    switch (NT) {
+    if (r_kmajor) {
+        if (!prepass_takes_kmajor(r)) return hipErrorInvalidValue;
+        QN_LAUNCH("prologue_kernel", st, (prologue_kernel<1, true>), grid, dim3(256), 0, st, a, tab);
+    } else {
+        switch (NT) {
 #define QN_PRO_CASE(T) \
-        case T: QN_LAUNCH("prologue_kernel", st, prologue_kernel<T>, grid, dim3(256), 0, st, a, tab); break;
-        QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
-        QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
+            case T: QN_LAUNCH("prologue_kernel", st, (prologue_kernel<T, false>), grid, dim3(256), 0, st, a, tab); break;
+            QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
+            QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
 #undef QN_PRO_CASE
-        default: return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;
+        }
     }
     if (a.psplits > 1) {
         const int64_t total = M * (r_pad / 4);

@@ -21,6 +21,8 @@ CASES = [
     WL.custom("tall", 576, 128, 513, 64, s=1.0),       # odd token count: a last unpaired token
     WL.custom("one_token", 192, 320, 1, 8, s=2.0),
     WL.custom("r33", 256, 448, 77, 33, s=0.75),
+    WL.custom("r24", 320, 256, 129, 24, s=1.25),       # U' pre-pass reads B itself (r % 8 == 0, r <= 32)
+    WL.custom("r32", 128, 192, 64, 32, s=0.5),
     WL.CONFIGS["prefill"],
     WL.CONFIGS["mlp_up"],
 ]

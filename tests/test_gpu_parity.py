@@ -176,6 +176,10 @@ LINEAR_SMALL = [
     WL.custom("split_fwd", 512, 4096, 200, 16, s=2.0),       # fwd 2 tiles -> 4 splits
     WL.custom("split_bwd", 4096, 512, 130, 64, s=1.0),       # dX 2 tiles -> 4 splits, ragged tokens
     WL.custom("split_both", 1536, 1536, 300, 33, s=1.5),     # 12 tiles each way -> 3 splits
+    # the dX pre-pass reads B itself when r % 8 == 0 and r <= 32, else a transpose of B
+    WL.custom("bmajor_r24", 256, 320, 100, 24, s=1.5),
+    WL.custom("bmajor_r32", 192, 448, 77, 32, s=0.75),
+    WL.custom("btrans_r40", 192, 448, 77, 40, s=0.75),
 ]
 
 
