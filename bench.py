@@ -323,6 +323,36 @@ def main():
     dprof = qn.profile_read()
     qn.profile_enable(False)
     nbytes = decode_bytes(dcfg)
+    # the same calls captured once in a HIP graph and replayed (a serving loop without host
+    # launch cost): GPU time per call including the gaps between launches
+    log("[bench] decode: the calls over all copies in one HIP graph")
+
+    def decode_all():
+        for i in range(len(copies)):
+            qn.linear_fwd(copies[i], A, B, dcfg.s, x1, out=y1, workspace=dws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_all()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_reps = max(1, args.decode_iters // len(copies))
+    e0.record()
+    for _ in range(g_reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_call_us = 1e3 * e0.elapsed_time(e1) / (g_reps * len(copies))
+    del graph
+
     # one launch when A fits one segment (this layer); else the A x slice kernel runs first
     dk = {k: 1e3 * ms / n for k, (n, ms) in dprof.items() if k in ("gemv_nf4_kernel", "lora_ax_partial_kernel")}
     gv_n, gv_ms = dprof["gemv_nf4_kernel"]
@@ -331,6 +361,7 @@ def main():
               "unit": "GB/s", "bytes_per_call": nbytes, "kernel_us": round(kern_us, 3),
               "gemv_kernel_us": round(1e3 * gv_ms / gv_n, 3),
               "call_us_back_to_back": round(1e6 * d_elapsed / args.decode_iters, 3),
+              "call_us_graph_replay": round(graph_call_us, 3),
               "copies": len(copies),
               "roofline": {"bound": "hbm", "kernel": " + ".join(sorted(dk)),
                            "achieved": round(nbytes / (kern_us * 1e-6) / 1e9, 1), "peak": PEAK_HBM_GBPS,
