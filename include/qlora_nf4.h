@@ -27,6 +27,9 @@
  *    enqueues work on that stream and returns; outputs are ready once the
  *    stream has reached the enqueued work. Outputs are overwritten, never
  *    accumulated into.
+ *  - Every call enqueues kernel launches only (no memset, copy, allocation or
+ *    host synchronisation), so a call may be captured in a HIP graph; a replay
+ *    reads whatever the captured input buffers hold at that time.
  *  - Quantised format (one NF4 + DQ weight):
  *      n   = d_out * d_in,  n_b = ceil(n / 64) blocks,  n_g = ceil(n_b / 256) groups
  *      codes  uint8 [n_b * 32] : 4-bit code of flat element 2i in the low nibble of
