@@ -30,6 +30,8 @@
 #include "internal.h"
 #include "nf4_device.h"
 
+#include <algorithm>
+
 namespace qn {
 namespace {
 
@@ -216,25 +218,32 @@ __device__ __forceinline__ float mean_from_limbs(const unsigned long long* colsu
 
 // ---------------------------------------------------------------------------
 // Level 2. A workgroup of 1024 threads forms mu (waves 0..9 add one limb column
-// each over the quant_blocks workgroups), then encodes kDqGroups groups of 256
-// block constants, one per 4 waves.
+// each over the quant_blocks workgroups; one thread then divides), then encodes
+// `passes` consecutive spans of kDqGroups groups of 256 block constants, one group
+// per 4 waves. mu is the serial part of a workgroup, so a large weight gives each
+// workgroup several spans (their constants are loaded before mu is formed).
 // ---------------------------------------------------------------------------
 constexpr int kDqThreads = 1024;
 constexpr int kDqGroups = kDqThreads / kGroup;
+constexpr int kDqMaxPasses = 16;
 
 __global__ __launch_bounds__(kDqThreads)
 void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned long long* __restrict__ limb_part,
-               int parts, int fmt, float* __restrict__ qmean, int8_t* __restrict__ qconst,
+               int parts, int passes, int fmt, float* __restrict__ qmean, int8_t* __restrict__ qconst,
                float* __restrict__ qscale) {
     __shared__ unsigned long long s_col[kLimbs];
     __shared__ float s_mu;
-    __shared__ uint32_t s_max[kDqThreads / 64];
+    __shared__ uint32_t s_max[2][kDqThreads / 64];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * kDqThreads + tid;
-    const bool valid = j < n_b;
-    const float a = valid ? absmax[j] : 0.0f;
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * passes * kDqThreads + tid;
+    float av[kDqMaxPasses];
+#pragma unroll
+    for (int p = 0; p < kDqMaxPasses; ++p) {
+        const int64_t j = j0 + static_cast<int64_t>(p) * kDqThreads;
+        av[p] = p < passes && j < n_b ? absmax[j] : 0.0f;
+    }
     if (wave < kLimbs) {
         unsigned long long acc = 0ull;
         for (int g = lane; g < parts; g += 64) acc += limb_part[static_cast<int64_t>(wave) * parts + g];
@@ -256,30 +265,38 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned lon
     }
     __syncthreads();
     const float mu = s_mu;
-    const float d = valid ? a - mu : 0.0f;
-    uint32_t m = __float_as_uint(d) & 0x7FFFFFFFu;
-    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
-    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16)));
-    m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 8)));
-    m = max8(m);
-    if (lane == 0) s_max[wave] = m;
-    __syncthreads();
     const int g0 = (wave >> 2) << 2;             // the 4 waves of this thread's group
-    const uint32_t mb = max(max(s_max[g0], s_max[g0 + 1]), max(s_max[g0 + 2], s_max[g0 + 3]));
-    const float b = __uint_as_float(mb);
-    if (valid) {
-        int8_t q = 0;
-        if (mb != 0) {
-            const float r = d / b;                                  // in [-1, 1]
-            if (fmt == kDqFp8)
-                q = static_cast<int8_t>(e4m3_encode(r * static_cast<float>(kE4m3Max)));
-            else
-                q = static_cast<int8_t>(static_cast<int>(rintf(r * static_cast<float>(kInt8Step))));
+#pragma unroll
+    for (int p = 0; p < kDqMaxPasses; ++p) {
+        if (p >= passes) break;
+        const int64_t j = j0 + static_cast<int64_t>(p) * kDqThreads;
+        const bool valid = j < n_b;
+        const float d = valid ? av[p] - mu : 0.0f;
+        uint32_t m = __float_as_uint(d) & 0x7FFFFFFFu;
+        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32)));
+        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16)));
+        m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 8)));
+        m = max8(m);
+        // s_max alternates between two buffers, so one barrier per span suffices
+        if (lane == 0) s_max[p & 1][wave] = m;
+        __syncthreads();
+        const uint32_t* sm = s_max[p & 1];
+        const uint32_t mb = max(max(sm[g0], sm[g0 + 1]), max(sm[g0 + 2], sm[g0 + 3]));
+        const float b = __uint_as_float(mb);
+        if (valid) {
+            int8_t q = 0;
+            if (mb != 0) {
+                const float r = d / b;                              // in [-1, 1]
+                if (fmt == kDqFp8)
+                    q = static_cast<int8_t>(e4m3_encode(r * static_cast<float>(kE4m3Max)));
+                else
+                    q = static_cast<int8_t>(static_cast<int>(rintf(r * static_cast<float>(kInt8Step))));
+            }
+            qconst[j] = q;
         }
-        qconst[j] = q;
+        const int64_t grp = (j0 - tid) / kGroup + static_cast<int64_t>(p) * kDqGroups + (wave >> 2);
+        if ((tid & (kGroup - 1)) == 0 && grp * kGroup < n_b) qscale[grp] = b;
     }
-    const int64_t grp = static_cast<int64_t>(blockIdx.x) * kDqGroups + (wave >> 2);
-    if ((tid & (kGroup - 1)) == 0 && grp * kGroup < n_b) qscale[grp] = b;
 }
 
 // ---------------------------------------------------------------------------
@@ -332,9 +349,12 @@ hipError_t launch_quantize(const float* W, int64_t n, int64_t n_b, int64_t n_g, 
     QN_LAUNCH("quant_blocks", st, quant_blocks, dim3(grid), dim3(kQuantThreads), 0, st, W, n, n_b,
               reinterpret_cast<uint32_t*>(codes), absmax, ws_limbs, tab);
     if (fmt != kDqNone) {
-        const int64_t dq_grid = (n_g + kDqGroups - 1) / kDqGroups;
+        // spans of kDqGroups groups: about 256 workgroups, at most kDqMaxPasses spans each
+        const int64_t spans = (n_g + kDqGroups - 1) / kDqGroups;
+        const int passes = static_cast<int>(std::min<int64_t>(kDqMaxPasses, std::max<int64_t>(1, spans / 256)));
+        const int64_t dq_grid = (spans + passes - 1) / passes;
         QN_LAUNCH("dq_encode", st, dq_encode, dim3(static_cast<unsigned>(dq_grid)), dim3(kDqThreads), 0, st,
-                  ws_absmax, n_b, ws_limbs, grid, fmt, qmean, qconst, qscale);
+                  ws_absmax, n_b, ws_limbs, grid, passes, fmt, qmean, qconst, qscale);
     }
     return hipGetLastError();
 }
