@@ -226,7 +226,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
 // workspace of qlora_lora_grads
 namespace {
 struct GradWs {
-    int64_t tp, up, bt, part, ppart, bytes;
+    int64_t tp, up, bt, part, ppart, ppart1, bytes;
     int r_pad;
 };
 
@@ -238,8 +238,8 @@ GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
     w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
     w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
-    w.ppart = off; off += align_up(std::max(prepass_part_bytes(d_seq, d_in, r), prepass_part_bytes(d_seq, d_out, r)),
-                                   256);                                            // pre-pass K-split partials
+    w.ppart = off; off += align_up(prepass_part_bytes(d_seq, d_in, r), 256);       // X A^T K-split partials
+    w.ppart1 = off; off += align_up(prepass_part_bytes(d_seq, d_out, r), 256);     // dY B K-split partials
     w.bytes = off;
     return w;
 }
@@ -517,20 +517,16 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const
     uint16_t* bt = reinterpret_cast<uint16_t*>(ws + gw.bt);
     float* part = reinterpret_cast<float*>(ws + gw.part);
     hipError_t e;
-    // T' = bf16(s X A^T): the forward's pre-pass, without the dequantisation
-    if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, X, d_in, d_seq,
-                                 d_in, A, d_in, false, r, s, tp, gw.r_pad, 0, nullptr, nullptr, 0, 0,
-                                 reinterpret_cast<float*>(ws + gw.ppart), st)) != hipSuccess)
-        return hip_fail(e, "qlora_lora_grads (X A^T)");
-    // U' = bf16(s dY B): the input gradient's pre-pass, on B itself where it can, else on B^T
+    // T' = bf16(s X A^T) and U' = bf16(s dY B): the forward's and the input gradient's
+    // pre-passes (without the dequantisation) in one launch; U' on B itself where it can
     const bool km = qn::prepass_takes_kmajor(r);
     if (!km && (e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (B^T)");
-    if ((e = qn::launch_prologue(nullptr, qn::BlockConsts{}, d_out, d_in, false, nullptr, dY, d_out,
-                                 d_seq, d_out, km ? B : bt, d_out, km, r, s, up, gw.r_pad, 0, nullptr, nullptr, 0, 0,
-                                 reinterpret_cast<float*>(ws + gw.ppart), st)) !=
+    if ((e = qn::launch_prepass_pair(X, d_in, d_in, A, d_in, tp, reinterpret_cast<float*>(ws + gw.ppart),
+                                     dY, d_out, d_out, km ? B : bt, d_out, km, up,
+                                     reinterpret_cast<float*>(ws + gw.ppart1), d_seq, r, s, gw.r_pad, st)) !=
         hipSuccess)
-        return hip_fail(e, "qlora_lora_grads (dY B)");
+        return hip_fail(e, "qlora_lora_grads (X A^T, dY B)");
     if ((e = qn::launch_lora_grads(X, dY, tp, up, d_out, d_in, d_seq, r, gw.r_pad, part, dA, dB, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (reduction)");
     return 0;

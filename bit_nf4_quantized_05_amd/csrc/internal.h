@@ -92,6 +92,14 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
                            const uint16_t* R, int64_t ldr, bool r_kmajor, int r, float s, uint16_t* OUT,
                            int r_pad, int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
                            int64_t acols, float* ppart, hipStream_t st);
+// Two LoRA pre-passes over the same M tokens in one launch (and one reduction):
+// OUT0 = bf16(s P0 R0^T) with R0 [r, K0] row stride ldr0, and OUT1 = bf16(s P1 R1^T)
+// with R1 [r, K1] (or k-major [K1, r] when r1_kmajor). ppart0 / ppart1 hold each job's
+// K-slice partials (prepass_split), or are null for one slice.
+hipError_t launch_prepass_pair(const uint16_t* P0, int64_t ldp0, int64_t K0, const uint16_t* R0, int64_t ldr0,
+                               uint16_t* OUT0, float* ppart0, const uint16_t* P1, int64_t ldp1, int64_t K1,
+                               const uint16_t* R1, int64_t ldr1, bool r1_kmajor, uint16_t* OUT1, float* ppart1,
+                               int64_t M, int r, float s, int r_pad, hipStream_t st);
 // The pre-pass can take R k-major, as B [K, r] itself (r % 8 == 0 and r <= 32: one
 // 32-rank MFMA tile, whose transposing reads keep the kernel's occupancy), which spares
 // the input gradient a transpose of B.

@@ -25,20 +25,28 @@ namespace {
 //   [.., +n_deq)          double dequantisation to bf16: W_hat row-major
 //                         (forward) or W_hat^T through 64x64 LDS tiles (dX).
 // ---------------------------------------------------------------------------
+// One LoRA pre-pass OUT = bf16(s P R^T); a launch takes up to two (the adapter
+// gradients need X A^T and dY B together; M, r, s and r_pad are shared).
+struct PreJob {
+    const uint16_t* P; int64_t ldp; int K;
+    const uint16_t* R; int64_t ldr;  // R [r, K] row stride ldr, or k-major [K, r]
+    uint16_t* OUT;
+    float* ppart;                    // [psplits][M][32 NT] fp32 partials when psplits > 1
+    int psplits, kper;               // K-slices and 64-wide K-chunks per slice
+    int n;                           // workgroups of this job
+};
+
 struct PrologueArgs {
     const uint8_t* codes; BlockConsts bc;
     int64_t d_out, d_in;
     int transposed;                 // dequant to W_hat^T [d_in, d_out] instead of W_hat
     uint16_t* what;
-    const uint16_t* P; int64_t ldp; int M, K;
-    const uint16_t* R; int64_t ldr; int r; float s;   // R [r, K] row stride ldr, or k-major [K, r]
-    uint16_t* OUT; int r_pad;
+    PreJob pre[2];
+    int M, r, r_pad; float s;
     int adapt_mode;                 // 0 none, 1 pad columns, 2 transpose + pad
     const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
-    int n_pre, n_adapt, n_deq;
-    int psplits, kper;              // pre-pass K-slices and 64-wide K-chunks per slice
+    int n_pre, n_adapt, n_deq;      // n_pre = pre[0].n + pre[1].n
     int trans_tiles;                // 64 x 64 tiles per transposed-dequant workgroup (1..4)
-    float* ppart;                   // [psplits][M][32 NT] fp32 partials when psplits > 1
 };
 
 constexpr int kDeqPerWG = 8192;                  // weights per row-major dequant workgroup (128 blocks)
@@ -65,15 +73,15 @@ struct PreStage {
 };
 
 template <int NT, bool KM>
-__device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& a, int wave, int lane, int m0,
-                                          int kc) {
+__device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PreJob& j, const PrologueArgs& a, int wave,
+                                          int lane, int m0, int kc) {
     const int64_t k0 = static_cast<int64_t>(kc) * 64;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {                      // P rows 32 w + 8 u .. +7
         const int row = 32 * wave + 8 * u + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         const int64_t m = min(m0 + row, a.M - 1);
-        __builtin_amdgcn_global_load_lds((global_ptr)(a.P + m * a.ldp + k0 + 8 * c),
+        __builtin_amdgcn_global_load_lds((global_ptr)(j.P + m * j.ldp + k0 + 8 * c),
                                          (lds_ptr)(&st.x[(32 * wave + 8 * u) * 8]), 16, 0, 0);
     }
     if constexpr (KM) {
@@ -84,7 +92,7 @@ __device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& 
             const int q = 64 * (4 * i + wave) + lane;
             const int64_t k = k0 + q / (4 * NT);
             const int pj = min(q % (4 * NT), a.r / 8 - 1);
-            __builtin_amdgcn_global_load_lds((global_ptr)(a.R + k * a.r + 8 * pj),
+            __builtin_amdgcn_global_load_lds((global_ptr)(j.R + k * a.r + 8 * pj),
                                              (lds_ptr)(&st.r[64 * (4 * i + wave)]), 16, 0, 0);
         }
     } else {
@@ -92,8 +100,8 @@ __device__ __forceinline__ void pre_issue(PreStage<NT>& st, const PrologueArgs& 
         for (int i = 0; i < NT; ++i) {                 // R rows 8 (4 i + w) .. +7
             const int row = 8 * (4 * i + wave) + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
-            const int64_t j = min(row, a.r - 1);
-            __builtin_amdgcn_global_load_lds((global_ptr)(a.R + j * a.ldr + k0 + 8 * c),
+            const int64_t jr = min(row, a.r - 1);
+            __builtin_amdgcn_global_load_lds((global_ptr)(j.R + jr * j.ldr + k0 + 8 * c),
                                              (lds_ptr)(&st.r[8 * (4 * i + wave) * 8]), 16, 0, 0);
         }
     }
@@ -147,29 +155,30 @@ __device__ __forceinline__ void pre_compute(const PreStage<NT>& st, int wave, in
 #define QN_PRE_BARRIER() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 template <int NT, bool KM>
-__device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreStage<NT>& s0, PreStage<NT>& s1) {
+__device__ __forceinline__ void prepass_job(const PreJob& j, const PrologueArgs& a, int b, PreStage<NT>& s0,
+                                            PreStage<NT>& s1) {
     constexpr int kLoads = 4 + NT;                     // direct loads per wave and stage
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int tiles = (a.M + 127) / 128;
     const int tile = b % tiles, sp = b / tiles;
     const int m0 = tile * 128;
-    const int kb = sp * a.kper;
-    const int ke = min(kb + a.kper, a.K / 64);
+    const int kb = sp * j.kper;
+    const int ke = min(kb + j.kper, j.K / 64);
     f32x16 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     // The barriers wait for LDS traffic only; each wave first waits for its own loads
     // of the stage about to be read (loads complete in issue order).
-    pre_issue<NT, KM>(s0, a, wave, lane, m0, kb);
+    pre_issue<NT, KM>(s0, j, a, wave, lane, m0, kb);
     for (int kc = kb; kc < ke; kc += 2) {
-        if (kc + 1 < ke) { pre_issue<NT, KM>(s1, a, wave, lane, m0, kc + 1); QN_WAIT_VM(kLoads); }
+        if (kc + 1 < ke) { pre_issue<NT, KM>(s1, j, a, wave, lane, m0, kc + 1); QN_WAIT_VM(kLoads); }
         else QN_WAIT_VM(0);
         QN_PRE_BARRIER();
         pre_compute<NT, KM>(s0, wave, lane, acc);
         QN_PRE_BARRIER();
         if (kc + 1 >= ke) break;
-        if (kc + 2 < ke) { pre_issue<NT, KM>(s0, a, wave, lane, m0, kc + 2); QN_WAIT_VM(kLoads); }
+        if (kc + 2 < ke) { pre_issue<NT, KM>(s0, j, a, wave, lane, m0, kc + 2); QN_WAIT_VM(kLoads); }
         else QN_WAIT_VM(0);
         QN_PRE_BARRIER();
         pre_compute<NT, KM>(s1, wave, lane, acc);
@@ -178,8 +187,8 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreSta
     // D of tile t: lane l holds ranks 32 t + 8 (v / 4) + 4 (l / 32) + v % 4 of token l % 32
     const int m = m0 + 32 * wave + (lane & 31);
     if (m >= a.M) return;
-    if (a.psplits == 1) {
-        uint16_t* orow = a.OUT + static_cast<int64_t>(m) * a.r_pad;
+    if (j.psplits == 1) {
+        uint16_t* orow = j.OUT + static_cast<int64_t>(m) * a.r_pad;
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -195,7 +204,7 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreSta
             *reinterpret_cast<uint2*>(orow + n) = uint2{0u, 0u};
         return;
     }
-    float* prow = a.ppart + (static_cast<int64_t>(sp) * a.M + m) * (32 * NT);
+    float* prow = j.ppart + (static_cast<int64_t>(sp) * a.M + m) * (32 * NT);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -209,26 +218,30 @@ __device__ __forceinline__ void prepass_job(const PrologueArgs& a, int b, PreSta
 #undef QN_PRE_BARRIER
 
 // OUT[m, j] = bf16(s * sum of the slice partials in slice order) for j < r, 0 for
-// r <= j < r_pad; a thread takes 4 consecutive columns.
+// r <= j < r_pad; a thread takes 4 consecutive columns. The first `blocks0` workgroups
+// reduce job 0, the rest job 1.
+struct ReduceJob { const float* part; uint16_t* OUT; int splits; };
+
 __global__ __launch_bounds__(256)
-void prepass_reduce(const float* __restrict__ part, int splits, int M, int ncols, int r, int r_pad, float s,
-                    uint16_t* __restrict__ OUT) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+void prepass_reduce(ReduceJob j0, ReduceJob j1, int blocks0, int M, int ncols, int r, int r_pad, float s) {
+    const bool second = static_cast<int>(blockIdx.x) >= blocks0;
+    const ReduceJob& jb = second ? j1 : j0;
+    const int64_t idx = static_cast<int64_t>(second ? blockIdx.x - blocks0 : blockIdx.x) * 256 + threadIdx.x;
     const int q4 = r_pad / 4;
     if (idx >= static_cast<int64_t>(M) * q4) return;
     const int64_t m = idx / q4;
     const int j = static_cast<int>(idx % q4) * 4;
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (j < ncols) {
-        const float* p = part + m * ncols + j;
-        for (int sp = 0; sp < splits; ++sp) {
+        const float* p = jb.part + m * ncols + j;
+        for (int sp = 0; sp < jb.splits; ++sp) {
             const float4 t = *reinterpret_cast<const float4*>(p + static_cast<int64_t>(sp) * M * ncols);
             v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
         }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = j + e < r ? s * v[e] : 0.0f;
-    *reinterpret_cast<uint2*>(OUT + m * r_pad + j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<uint2*>(jb.OUT + m * r_pad + j) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
 // Adapter layouts; destination is [rows, r_pad] (pad) or [acols, r_pad] (transpose).
@@ -352,14 +365,19 @@ __device__ __forceinline__ void dequant_transposed_job(const PrologueArgs& a, in
     }
 }
 
-template <int NT, bool KM>
+// KM0, KM1: whether pre-pass job 0 / 1 takes its R k-major
+template <int NT, bool KM0, bool KM1>
 __global__ __launch_bounds__(256)
 void prologue_kernel(PrologueArgs a, NF4Tables tab) {
     __shared__ PreStage<NT> s0, s1;
     char* lds = reinterpret_cast<char*>(s1.x);             // 16 KB of scratch for the other jobs
     const int b = blockIdx.x;
+    if (b < a.pre[0].n) {
+        prepass_job<NT, KM0>(a.pre[0], a, b, s0, s1);
+        return;
+    }
     if (b < a.n_pre) {
-        prepass_job<NT, KM>(a, b, s0, s1);
+        prepass_job<NT, KM1>(a.pre[1], a, b - a.pre[0].n, s0, s1);
         return;
     }
     if (b < a.n_pre + a.n_adapt) {
@@ -406,23 +424,68 @@ PrepassSplit prepass_split(int64_t M, int64_t K) {
     return ps;
 }
 
+namespace {
+
+PreJob make_job(const uint16_t* P, int64_t ldp, int64_t M, int64_t K, const uint16_t* R, int64_t ldr,
+                uint16_t* OUT, float* ppart) {
+    PreJob j;
+    j.P = P; j.ldp = ldp; j.K = static_cast<int>(K); j.R = R; j.ldr = ldr; j.OUT = OUT; j.ppart = ppart;
+    const PrepassSplit ps = prepass_split(M, K);
+    j.psplits = ppart == nullptr ? 1 : ps.splits;
+    j.kper = j.psplits == 1 ? static_cast<int>(K / 64) : ps.kper;
+    j.n = static_cast<int>((M + 127) / 128) * j.psplits;
+    return j;
+}
+
+// Launch the prologue for a (pre[0].n, pre[1].n set; the dequant and adapter fields
+// set by the caller), then one reduction of the split pre-pass jobs.
+hipError_t launch_prologue_args(PrologueArgs& a, bool km0, bool km1, hipStream_t st) {
+    a.n_pre = a.pre[0].n + a.pre[1].n;
+    const int NT = (a.r + 31) / 32;
+    const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
+    const NF4Tables& tab = tables();
+    if (km0 || km1) {
+        if (!prepass_takes_kmajor(a.r) || (km0 && km1)) return hipErrorInvalidValue;
+        if (km0) QN_LAUNCH("prologue_kernel", st, (prologue_kernel<1, true, false>), grid, dim3(256), 0, st, a, tab);
+        else QN_LAUNCH("prologue_kernel", st, (prologue_kernel<1, false, true>), grid, dim3(256), 0, st, a, tab);
+    } else {
+        switch (NT) {
+#define QN_PRO_CASE(T) \
+            case T: QN_LAUNCH("prologue_kernel", st, (prologue_kernel<T, false, false>), grid, dim3(256), 0, st, \
+                              a, tab); break;
+            QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
+            QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
+#undef QN_PRO_CASE
+            default: return hipErrorInvalidValue;
+        }
+    }
+    const int64_t per_job = (static_cast<int64_t>(a.M) * (a.r_pad / 4) + 255) / 256;
+    const int blocks0 = a.pre[0].n > 0 && a.pre[0].psplits > 1 ? static_cast<int>(per_job) : 0;
+    const int blocks1 = a.pre[1].n > 0 && a.pre[1].psplits > 1 ? static_cast<int>(per_job) : 0;
+    if (blocks0 + blocks1 > 0) {
+        const ReduceJob r0{a.pre[0].ppart, a.pre[0].OUT, a.pre[0].psplits};
+        const ReduceJob r1{a.pre[1].ppart, a.pre[1].OUT, a.pre[1].psplits};
+        QN_LAUNCH("prepass_reduce", st, prepass_reduce, dim3(static_cast<unsigned>(blocks0 + blocks1)), dim3(256), 0,
+                  st, r0, r1, blocks0, a.M, 32 * NT, a.r, a.r_pad, a.s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            bool transposed,
                            uint16_t* what, const uint16_t* P, int64_t ldp, int64_t M, int64_t K,
                            const uint16_t* R, int64_t ldr, bool r_kmajor, int r, float s, uint16_t* OUT,
                            int r_pad, int adapt_mode, const uint16_t* asrc, uint16_t* adst, int64_t arows,
                            int64_t acols, float* ppart, hipStream_t st) {
-    PrologueArgs a;
+    PrologueArgs a{};
     a.codes = codes; a.bc = bc;
     a.d_out = d_out; a.d_in = d_in; a.transposed = transposed ? 1 : 0; a.what = what;
-    a.P = P; a.ldp = ldp; a.M = static_cast<int>(M); a.K = static_cast<int>(K);
-    a.R = R; a.ldr = ldr; a.r = r; a.s = s; a.OUT = OUT; a.r_pad = r_pad;
+    a.pre[0] = make_job(P, ldp, M, K, R, ldr, OUT, ppart);
+    a.pre[1] = PreJob{};
+    a.M = static_cast<int>(M); a.r = r; a.s = s; a.r_pad = r_pad;
     a.adapt_mode = adapt_mode; a.asrc = asrc; a.adst = adst; a.arows = arows; a.acols = acols;
-    const PrepassSplit ps = prepass_split(M, K);
-    a.psplits = ppart == nullptr ? 1 : ps.splits;
-    a.kper = a.psplits == 1 ? static_cast<int>(K / 64) : ps.kper;
-    a.ppart = ppart;
-    a.n_pre = static_cast<int>((M + 127) / 128) * a.psplits;
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
     a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
@@ -431,29 +494,20 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
                               : static_cast<int>(transposed ? (d_in / 64 + a.trans_tiles - 1) / a.trans_tiles *
                                                                   ((d_out + 63) / 64)
                                                             : (n + kDeqPerWG - 1) / kDeqPerWG);
-    const int NT = (r + 31) / 32;
     static_assert(64 + 1024 + 64 * kTP * sizeof(uint16_t) <= sizeof(PreStage<1>::x), "dequant scratch fits a stage");
-    const dim3 grid(static_cast<unsigned>(a.n_pre + a.n_adapt + a.n_deq));
-    const NF4Tables& tab = tables();
-    if (r_kmajor) {
-        if (!prepass_takes_kmajor(r)) return hipErrorInvalidValue;
-        QN_LAUNCH("prologue_kernel", st, (prologue_kernel<1, true>), grid, dim3(256), 0, st, a, tab);
-    } else {
-        switch (NT) {
-#define QN_PRO_CASE(T) \
-            case T: QN_LAUNCH("prologue_kernel", st, (prologue_kernel<T, false>), grid, dim3(256), 0, st, a, tab); break;
-            QN_PRO_CASE(1) QN_PRO_CASE(2) QN_PRO_CASE(3) QN_PRO_CASE(4)
-            QN_PRO_CASE(5) QN_PRO_CASE(6) QN_PRO_CASE(7) QN_PRO_CASE(8)
-#undef QN_PRO_CASE
-            default: return hipErrorInvalidValue;
-        }
-    }
-    if (a.psplits > 1) {
-        const int64_t total = M * (r_pad / 4);
-        QN_LAUNCH("prepass_reduce", st, prepass_reduce, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-                  st, ppart, a.psplits, static_cast<int>(M), 32 * NT, r, r_pad, s, OUT);
-    }
-    return hipGetLastError();
+    return launch_prologue_args(a, r_kmajor, false, st);
+}
+
+hipError_t launch_prepass_pair(const uint16_t* P0, int64_t ldp0, int64_t K0, const uint16_t* R0, int64_t ldr0,
+                               uint16_t* OUT0, float* ppart0, const uint16_t* P1, int64_t ldp1, int64_t K1,
+                               const uint16_t* R1, int64_t ldr1, bool r1_kmajor, uint16_t* OUT1, float* ppart1,
+                               int64_t M, int r, float s, int r_pad, hipStream_t st) {
+    PrologueArgs a{};
+    a.pre[0] = make_job(P0, ldp0, M, K0, R0, ldr0, OUT0, ppart0);
+    a.pre[1] = make_job(P1, ldp1, M, K1, R1, ldr1, OUT1, ppart1);
+    a.M = static_cast<int>(M); a.r = r; a.s = s; a.r_pad = r_pad;
+    a.n_adapt = 0; a.n_deq = 0; a.trans_tiles = 1;
+    return launch_prologue_args(a, false, r1_kmajor, st);
 }
 
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
