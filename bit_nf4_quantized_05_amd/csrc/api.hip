@@ -1,6 +1,6 @@
 // extern "C" entry points of libqlora_nf4: argument checks, workspace layout and
 // kernel sequencing. Every step of the layer runs in the kernels of quantize.hip,
-// prologue.hip, gemm_nt.hip, gemv.hip, skinny.hip and lora_grads.hip; this file does
+// prologue.hip, gemm_nt.hip, gemv.hip, skinny.hip, lora_grads.hip and factors.hip; this file does
 // no arithmetic on the data.
 #include <hip/hip_runtime.h>
 
@@ -98,7 +98,7 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.what = off;   off += align_up(2 * d_out * d_in, 256);                        // W_hat or W_hat^T
     w.lora = off;   off += align_up(2 * d_seq * w.r_pad, 256);                     // s(XA^T) or s(dY B)
     w.adapt = off;  off += align_up(2 * (d_out > d_in ? d_out : d_in) * w.r_pad, 256);  // B padded or A^T padded
-    w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T
+    w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T (unless the pre-pass reads B)
     w.t = off;      off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);  // GEMV: partial A x
     w.part = off;                                                                // small batch: K-split partials
     if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
@@ -236,7 +236,7 @@ GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     int64_t off = 0;
     w.tp = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // T' = bf16(s X A^T)
     w.up = off;   off += align_up(2 * d_seq * w.r_pad, 256);                        // U' = bf16(s dY B)
-    w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T
+    w.bt = off;   off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);        // B^T (unless the pre-pass reads B)
     w.part = off; off += align_up(4 * qn::lora_grads_partials(d_out, d_in, d_seq, r), 256);
     w.ppart = off; off += align_up(prepass_part_bytes(d_seq, d_in, r), 256);       // X A^T K-split partials
     w.ppart1 = off; off += align_up(prepass_part_bytes(d_seq, d_out, r), 256);     // dY B K-split partials

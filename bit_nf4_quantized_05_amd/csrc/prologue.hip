@@ -1,7 +1,8 @@
 // Prologue of a QLoRA linear call on gfx950: the LoRA pre-pass (rank-r product of
-// the activations with A or B^T), the adapter layouts and the double dequantisation
-// of the NF4 weight to bf16 W_hat or W_hat^T, in one launch; plus the small
-// transpose of B used by the input gradient.
+// the activations with A or B^T; up to two such products per launch), the adapter
+// layouts and the double dequantisation of the NF4 weight to bf16 W_hat or W_hat^T,
+// in one launch; the reduction of K-split pre-pass partials; and the small transpose
+// of B that the input gradient uses when the pre-pass cannot read B itself.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
