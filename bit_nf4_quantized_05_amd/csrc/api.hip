@@ -102,7 +102,7 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     w.t = off;      off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);  // GEMV: partial A x
     w.part = off;                                                                // small batch: K-split partials
     if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
-        off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * (d_out + w.r_pad), 256);
+        off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in, d_seq)) * d_seq * (d_out + w.r_pad), 256);
     w.gpart = off;                                                               // GEMM K-split partials (few tiles)
     off += align_up(4 * std::max(d_seq > qn::kSkinnyMaxTokens ? qn::gemm_split_part_floats(d_seq, d_out, d_in) : 0,
                                  qn::gemm_split_part_floats(d_seq, d_in, d_out)), 256);
@@ -200,7 +200,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
     if (d_seq <= qn::kSkinnyMaxTokens) {
         // few tokens: the codes streamed once, A x in the same launch
         float* part = reinterpret_cast<float*>(ws + lw.part);
-        float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in)) * d_seq * d_out;
+        float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in, d_seq)) * d_seq * d_out;
         if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
                                        part, part_a, Y, st)) != hipSuccess)
             return hip_fail(e, "qlora_linear_fwd (small batch)");

@@ -117,11 +117,11 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
 
 // ---- skinny.hip ----
 // Small-batch forward, 2 <= d_seq <= 64: Y = dequant(W) X + bf16(s X A^T) B^T from the
-// packed codes, A x formed in the same launch. part must hold skinny_splits(d_in) *
-// d_seq * d_out floats, part_a skinny_splits(d_in) * d_seq * r_pad. d_out % 64 == 0,
+// packed codes, A x formed in the same launch. part must hold skinny_splits(d_in, d_seq) *
+// d_seq * d_out floats, part_a skinny_splits(d_in, d_seq) * d_seq * r_pad. d_out % 64 == 0,
 // d_in % 64 == 0.
 constexpr int kSkinnyMaxTokens = 64;
-int skinny_splits(int64_t d_in);
+int skinny_splits(int64_t d_in, int64_t d_seq);
 hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                              const uint16_t* X, int64_t d_seq,
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,

@@ -36,6 +36,7 @@ constexpr int kSkRows = 64;         // rows of W per workgroup (16 per wave)
 constexpr int kSkBlk = 8;           // 64-weight blocks per K-slice
 constexpr int kSkTok = 64;          // tokens at most
 constexpr int kSkSplits = 8;        // K-split partials at most
+constexpr int kSkSplitTokens = 32;  // above this many tokens, at most 4 K-splits
 
 struct SkArgs {
     const uint8_t* codes; BlockConsts bc;
@@ -277,9 +278,12 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
 
 }  // namespace
 
-int skinny_splits(int64_t d_in) {
+int skinny_splits(int64_t d_in, int64_t d_seq) {
+    // up to 8 K-splits; with more than 32 tokens the fp32 partials (splits x d_seq x d_out)
+    // cost more than the extra workgroups gain, so at most 4
     const int64_t nslices = (d_in / 64 + kSkBlk - 1) / kSkBlk;
-    return static_cast<int>(std::min<int64_t>(kSkSplits, nslices));
+    const int64_t cap = d_seq > kSkSplitTokens ? 4 : kSkSplits;
+    return static_cast<int>(std::min<int64_t>(cap, nslices));
 }
 
 hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
@@ -289,7 +293,7 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
     SkArgs a;
     a.codes = codes; a.bc = bc;
     a.d_out = static_cast<int>(d_out); a.d_in = static_cast<int>(d_in); a.d_seq = static_cast<int>(d_seq);
-    a.splits = skinny_splits(d_in);
+    a.splits = skinny_splits(d_in, d_seq);
     a.r = r; a.r_pad = r_pad;
     a.X = X; a.A = A; a.part = part; a.part_a = part_a;
     const int blocks = static_cast<int>(d_out / kSkRows) + (r + kSkRows - 1) / kSkRows;
