@@ -209,7 +209,9 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 // Y[t, o] = bf16( sum_split part + sum_j T'[t, j] B[o, j] ) for kRdRows rows o per
 // workgroup, T'[t, j] = bf16(s * sum_split part_a). Thread tid takes the (token, row)
 // pairs tid + 256 q; the rank sums go through LDS in chunks of 64 rank entries (rows
-// of odd pitch, so a row of B and a row of T' fall in different banks).
+// of odd pitch, so a row of B and a row of T' fall in different banks). Every load of
+// a chunk is issued before any of them is used (split indices past `splits` re-read
+// the last split and are masked out), so a chunk costs one memory round trip.
 constexpr int kRdRows = 16;
 
 __global__ __launch_bounds__(256)
@@ -217,45 +219,61 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
                    int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y) {
     constexpr int kJ = 64, kP = kJ + 1;
     constexpr int kPairs = kSkTok * kRdRows / 256;   // pairs per thread at most
+    constexpr int kBPer = kRdRows * kJ / 256;        // B entries per thread and chunk
     __shared__ float s_b[kRdRows * kP];
     __shared__ float s_t[kSkTok * kP];
     const int tid = threadIdx.x;
     const int o0 = static_cast<int>(blockIdx.x) * kRdRows;
     const int npairs = d_seq * kRdRows;
-    float acc[kPairs];
+    float pv[kPairs][kSkSplits];
 #pragma unroll
     for (int q = 0; q < kPairs; ++q) {
-        const int e = tid + 256 * q;
-        float v = 0.0f;
-        if (e < npairs) {
-            // all split loads issued before the ordered sum
-            const int64_t idx = static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows;
-            float pv[kSkSplits];
+        const int e = min(tid + 256 * q, npairs - 1);
+        const int64_t idx = static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows;
 #pragma unroll
-            for (int sp = 0; sp < kSkSplits; ++sp)
-                pv[sp] = sp < splits ? part[static_cast<int64_t>(sp) * d_seq * d_out + idx] : 0.0f;
-#pragma unroll
-            for (int sp = 0; sp < kSkSplits; ++sp) v += pv[sp];
-        }
-        acc[q] = v;
+        for (int sp = 0; sp < kSkSplits; ++sp)
+            pv[q][sp] = part[static_cast<int64_t>(min(sp, splits - 1)) * d_seq * d_out + idx];
     }
+    float acc[kPairs];
+#pragma unroll
+    for (int q = 0; q < kPairs; ++q) acc[q] = 0.0f;
     for (int j0 = 0; j0 < r; j0 += kJ) {
         const int nj = min(kJ, r - j0);
-        __syncthreads();
-        for (int e = tid; e < kRdRows * nj; e += 256) {
-            const int ro = e / nj, j = e % nj;
-            s_b[ro * kP + j] = __uint_as_float(static_cast<uint32_t>(B[static_cast<int64_t>(o0 + ro) * r + j0 + j]) << 16);
+        // this chunk's loads: kBPer entries of B, then one (token, rank) entry of T' per
+        // pass (all splits); the sums follow once they are in flight
+        uint16_t bv[kBPer];
+#pragma unroll
+        for (int i = 0; i < kBPer; ++i) {
+            const int e = min(tid + 256 * i, kRdRows * nj - 1);
+            bv[i] = B[static_cast<int64_t>(o0 + e / nj) * r + j0 + e % nj];
         }
-        for (int e = tid; e < d_seq * nj; e += 256) {
+        const int nt = d_seq * nj;
+        __syncthreads();                                  // the previous chunk's LDS reads are done
+        for (int e0 = 0; e0 < nt; e0 += 256) {
+            const int e = min(e0 + tid, nt - 1);
             const int t = e / nj, j = e % nj;
-            float pv[kSkSplits];
+            float av[kSkSplits];
 #pragma unroll
             for (int sp = 0; sp < kSkSplits; ++sp)
-                pv[sp] = sp < splits ? part_a[(static_cast<int64_t>(sp) * d_seq + t) * r_pad + j0 + j] : 0.0f;
-            float v = 0.0f;
+                av[sp] = part_a[(static_cast<int64_t>(min(sp, splits - 1)) * d_seq + t) * r_pad + j0 + j];
+            if (e0 + tid < nt) {
+                float v = 0.0f;
 #pragma unroll
-            for (int sp = 0; sp < kSkSplits; ++sp) v += pv[sp];
-            s_t[t * kP + j] = __uint_as_float(static_cast<uint32_t>(bf16_bits(s * v)) << 16);
+                for (int sp = 0; sp < kSkSplits; ++sp) v += sp < splits ? av[sp] : 0.0f;
+                s_t[t * kP + j] = __uint_as_float(static_cast<uint32_t>(bf16_bits(s * v)) << 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kBPer; ++i) {
+            const int e = tid + 256 * i;
+            if (e < kRdRows * nj) s_b[(e / nj) * kP + e % nj] = __uint_as_float(static_cast<uint32_t>(bv[i]) << 16);
+        }
+        if (j0 == 0) {
+#pragma unroll
+            for (int q = 0; q < kPairs; ++q) {
+#pragma unroll
+                for (int sp = 0; sp < kSkSplits; ++sp) acc[q] += sp < splits ? pv[q][sp] : 0.0f;
+            }
         }
         __syncthreads();
 #pragma unroll
