@@ -26,6 +26,7 @@
 
 #include "internal.h"
 #include "mfma_device.h"
+#include "nf4_device.h"
 
 #include <algorithm>
 
@@ -200,20 +201,14 @@ void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __re
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     const int64_t nB = d_out * r;
     if (idx < nB) {                                   // dB[n, j], n = idx / r
-        float v = 0.0f;
-#pragma unroll 8
-        for (int s = 0; s < SB; ++s) v += partB[static_cast<int64_t>(s) * nB + idx];
-        dB[idx] = v;
+        dB[idx] = ordered_sum<16>(partB + idx, nB, SB);
         return;
     }
     const int64_t k = idx - nB;                       // dA[j, n], n fastest
     if (k >= d_in * r) return;
     const int64_t j = k / d_in, n = k % d_in;
     const int64_t nA = d_in * r;
-    float v = 0.0f;
-#pragma unroll 8
-    for (int s = 0; s < SA; ++s) v += partA[static_cast<int64_t>(s) * nA + n * r + j];
-    dA[k] = v;
+    dA[k] = ordered_sum<16>(partA + n * r + j, nA, SA);
 }
 
 // token slices (multiples of kGK) for N columns: about kGSlices workgroups in all

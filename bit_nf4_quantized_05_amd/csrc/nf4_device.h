@@ -45,6 +45,41 @@ __device__ __forceinline__ float block_constant(int fmt, int8_t q, float b, floa
     return mu + prod;
 }
 
+// Ordered sums over K-split partials: v = p[0] + p[stride] + ... + p[(n-1) stride], float32
+// adds from +0.0 in that order. The loads are issued B at a time (slices past n re-read
+// the last one and are masked to +0.0, which leaves a sum that started at +0.0
+// unchanged), so n slices cost ceil(n / B) memory round trips instead of n.
+template <int Bt>
+__device__ __forceinline__ float ordered_sum(const float* __restrict__ p, int64_t stride, int n) {
+    float v = 0.0f;
+    for (int s0 = 0; s0 < n; s0 += Bt) {
+        float t[Bt];
+#pragma unroll
+        for (int i = 0; i < Bt; ++i) t[i] = p[static_cast<int64_t>(min(s0 + i, n - 1)) * stride];
+#pragma unroll
+        for (int i = 0; i < Bt; ++i) v += s0 + i < n ? t[i] : 0.0f;
+    }
+    return v;
+}
+
+template <int Bt>
+__device__ __forceinline__ float4 ordered_sum4(const float* __restrict__ p, int64_t stride, int n) {
+    float4 v = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < n; s0 += Bt) {
+        float4 t[Bt];
+#pragma unroll
+        for (int i = 0; i < Bt; ++i)
+            t[i] = *reinterpret_cast<const float4*>(p + static_cast<int64_t>(min(s0 + i, n - 1)) * stride);
+#pragma unroll
+        for (int i = 0; i < Bt; ++i) {
+            const bool ok = s0 + i < n;
+            v.x += ok ? t[i].x : 0.0f; v.y += ok ? t[i].y : 0.0f;
+            v.z += ok ? t[i].z : 0.0f; v.w += ok ? t[i].w : 0.0f;
+        }
+    }
+    return v;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     const __bf16 a = static_cast<__bf16>(lo);    // round to nearest even (v_cvt_pk_bf16_f32)
     const __bf16 b = static_cast<__bf16>(hi);

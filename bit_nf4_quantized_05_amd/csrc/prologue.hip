@@ -234,11 +234,8 @@ void prepass_reduce(ReduceJob j0, ReduceJob j1, int blocks0, int M, int ncols, i
     const int j = static_cast<int>(idx % q4) * 4;
     float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (j < ncols) {
-        const float* p = jb.part + m * ncols + j;
-        for (int sp = 0; sp < jb.splits; ++sp) {
-            const float4 t = *reinterpret_cast<const float4*>(p + static_cast<int64_t>(sp) * M * ncols);
-            v[0] += t.x; v[1] += t.y; v[2] += t.z; v[3] += t.w;
-        }
+        const float4 t = ordered_sum4<8>(jb.part + m * ncols + j, static_cast<int64_t>(M) * ncols, jb.splits);
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = j + e < r ? s * v[e] : 0.0f;
