@@ -77,3 +77,32 @@ def test_largest_accepted_layer():
     cols = (cblk[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
     got = bf16_f64(dx[:, torch.from_numpy(cols).to(dev())])
     check_close(got, O.linear_bwd_x(ol.col_blocks(cblk), a[:, cols], b, S, dy), "bwd_x max size")
+
+
+def test_long_sequence():
+    """131072 tokens on a 1024 x 1024 layer (r = 16): the pre-pass runs 1024 token
+    tiles unsplit, the GEMMs 512 x 4 tiles, the adapter gradients many token slices;
+    forward, input gradient and adapter gradients on sampled tokens (incl. the last)."""
+    cfg = WL.custom("long", 1024, 1024, 131072, 16, s=1.5)
+    _say(f"[long sequence] {cfg.d_out}x{cfg.d_in}, {cfg.d_seq} tokens")
+    w = WL.make_weight(cfg)
+    q = qn.quantize(torch.from_numpy(w).to(dev()))
+    ol = OracleLayer(w)
+    a, b = WL.make_lora(cfg)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    x, dy = WL.make_x(cfg), WL.make_dy(cfg)
+    X, dY = to_gpu_bf16(x), to_gpu_bf16(dy)
+    y = qn.linear_fwd(q, A, B, cfg.s, X)
+    dx = qn.linear_bwd_x(q, A, B, cfg.s, dY)
+    dA, dB = qn.lora_grads(A, B, cfg.s, X, dY)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    toks = np.unique(np.concatenate([[0, 127, 128, cfg.d_seq - 129, cfg.d_seq - 1], rng.choice(cfg.d_seq, 59, replace=False)]))
+    tt = torch.from_numpy(toks).to(dev())
+    wh = ol.rows(np.arange(cfg.d_out))
+    check_close(bf16_f64(y[tt]), O.linear_fwd(wh, a, b, cfg.s, x[toks]), "fwd long sequence (sampled tokens)")
+    check_close(bf16_f64(dx[tt]), O.linear_bwd_x(wh, a, b, cfg.s, dy[toks]), "bwd_x long sequence (sampled tokens)")
+    # adapter gradients sum over every token: checked in full against the oracle
+    rA, rB = O.lora_grads(a, b, cfg.s, x, dy)
+    check_close(dA.cpu().numpy().astype(np.float64), rA, "dA long sequence")
+    check_close(dB.cpu().numpy().astype(np.float64), rB, "dB long sequence")
