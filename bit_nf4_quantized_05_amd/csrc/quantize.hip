@@ -20,9 +20,10 @@
 //                    per-workgroup sum of the constants as 32-bit-limb integers.
 //   dq_encode      - each workgroup first forms mu itself: it adds the per-workgroup
 //                    limb sums (integers, so the order is free and every workgroup gets
-//                    the same bits), divides by n_b with integer long division and rounds
-//                    once to float32; then, for its kDqGroups groups of 256 constants:
-//                    centre, absmax, INT8.
+//                    the same bits) and rounds their exact mean once to float32 (a float64
+//                    estimate decides unless it is too close to a rounding midpoint, then
+//                    integer long division); then, for its kDqGroups groups of 256
+//                    constants: centre, absmax, INT8.
 //   dequant_rows   - double dequantisation to bf16 (the standalone entry point; the
 //                    linear calls dequantise inside their prologue launch).
 #include <hip/hip_runtime.h>
@@ -215,6 +216,26 @@ __device__ __forceinline__ float mean_from_limbs(const unsigned long long* colsu
     return __uint_as_float(bits);
 }
 
+// The same mu, usually without the long division: the column totals summed in float64
+// (each limb scaled by its power of two) and divided by n_b give the exact mean within
+// a relative 20 * 2^-53 (19 roundings of positive terms, one division). Rounding that
+// estimate to float32 gives the float nearest the exact mean unless the estimate lies
+// within x 2^-46 of a midpoint between neighbouring floats (sums of two adjacent floats
+// are exact in float64); only then does the integer division above decide.
+__device__ __forceinline__ float mean_of_columns(const unsigned long long* colsum, int64_t n_b) {
+    double s = 0.0;
+#pragma unroll
+    for (int L = kLimbs - 1; L >= 0; --L) s += ldexp(static_cast<double>(colsum[L]), 32 * L - 149);
+    const double x = s / static_cast<double>(n_b);
+    const float f = static_cast<float>(x);
+    const uint32_t fb = __float_as_uint(f);
+    const double up = (static_cast<double>(f) + static_cast<double>(__uint_as_float(fb + 1u))) * 0.5;
+    const double dn = fb ? (static_cast<double>(f) + static_cast<double>(__uint_as_float(fb - 1u))) * 0.5 : -1.0;
+    const double tol = x * 0x1p-46;
+    if (up - x > tol && x - dn > tol) return f;
+    return mean_from_limbs(colsum, n_b);
+}
+
 
 // ---------------------------------------------------------------------------
 // Level 2. A workgroup of 1024 threads forms mu (waves 0..9 add one limb column
@@ -226,6 +247,7 @@ __device__ __forceinline__ float mean_from_limbs(const unsigned long long* colsu
 constexpr int kDqThreads = 1024;
 constexpr int kDqGroups = kDqThreads / kGroup;
 constexpr int kDqMaxPasses = 16;
+constexpr int kLimbBatch = 4;
 
 __global__ __launch_bounds__(kDqThreads)
 void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned long long* __restrict__ limb_part,
@@ -246,7 +268,14 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned lon
     }
     if (wave < kLimbs) {
         unsigned long long acc = 0ull;
-        for (int g = lane; g < parts; g += 64) acc += limb_part[static_cast<int64_t>(wave) * parts + g];
+        const unsigned long long* colp = limb_part + static_cast<int64_t>(wave) * parts;
+        for (int g0 = 0; g0 < parts; g0 += 64 * kLimbBatch) {   // kLimbBatch loads in flight per lane
+            unsigned long long v[kLimbBatch];
+#pragma unroll
+            for (int b = 0; b < kLimbBatch; ++b) v[b] = colp[min(g0 + 64 * b + lane, parts - 1)];
+#pragma unroll
+            for (int b = 0; b < kLimbBatch; ++b) acc += g0 + 64 * b + lane < parts ? v[b] : 0ull;
+        }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const uint32_t lo = static_cast<uint32_t>(__shfl_xor(static_cast<int>(acc & 0xFFFFFFFFull), off));
@@ -260,7 +289,7 @@ void dq_encode(const float* __restrict__ absmax, int64_t n_b, const unsigned lon
         unsigned long long col[kLimbs];
 #pragma unroll
         for (int L = 0; L < kLimbs; ++L) col[L] = s_col[L];
-        s_mu = mean_from_limbs(col, n_b);
+        s_mu = mean_of_columns(col, n_b);
         if (blockIdx.x == 0) qmean[0] = s_mu;
     }
     __syncthreads();

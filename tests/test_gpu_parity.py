@@ -98,6 +98,37 @@ def test_quantize_and_dequant_bit_exact_small(name, make):
     assert np.array_equal(bf16_bits(wh), want)
 
 
+_F = np.float32
+MEAN_CASES = [   # block absmax values, the float32 nearest their mean (ties to even)
+    ([2.0, 2.0 ** -23], 1.0),                                     # exactly halfway: 1 + 2^-24
+    ([2.0 + 2.0 ** -22, 2.0 ** -23], 1.0 + 2.0 ** -22),           # halfway between 1 + 2^-23 and 1 + 2^-22
+    ([2.0, 2.0 ** -23 + 2.0 ** -46], 1.0 + 2.0 ** -23),           # 2^-47 above halfway
+    ([2.0, 2.0 ** -23 - 2.0 ** -47], 1.0),                        # 2^-48 below halfway
+    ([1.0, 1.0, 1.0 + 2.0 ** -23], 1.0),                          # a third of an ulp above 1
+    ([2.0 ** -149, 0.0], 0.0),                                    # subnormal: halfway between 0 and 2^-149
+    ([3 * 2.0 ** -149, 0.0], 2.0 ** -148),                        # halfway between 2^-149 and 2^-148
+    ([2.0 ** -149] * 3 + [0.0], 2.0 ** -149),
+    ([float(np.finfo(np.float32).max)] * 2, float(np.finfo(np.float32).max)),
+]
+
+
+@pytest.mark.parametrize("k", range(len(MEAN_CASES)))
+def test_mean_rounding_at_midpoints(k):
+    """The mean of the block constants at, and within far less than an ulp of, float32
+    rounding midpoints (normal and subnormal), where the kernel cannot decide from a
+    float64 estimate and has to divide the exact integer sum."""
+    absmax, want = MEAN_CASES[k]
+    pattern = np.linspace(-0.9, 0.9, 64).astype(np.float32)
+    pattern[5] = 1.0
+    w = np.stack([(pattern * _F(a)).astype(np.float32) for a in absmax])
+    assert [float(np.abs(r).max()) for r in w] == [float(_F(a)) for a in absmax]
+    _say(f"[mean] case {k}: {len(absmax)} blocks")
+    q = _gpu_quantize(w)
+    ref = O.quantize(w)
+    assert ref["qmean"].view(np.uint32)[0] == np.array([want], np.float32).view(np.uint32)[0]
+    _assert_quant_equal(q, ref)
+
+
 def test_quantize_is_deterministic_and_reusable():
     w = _normal((777, 320), 11)
     q1 = _gpu_quantize(w)
