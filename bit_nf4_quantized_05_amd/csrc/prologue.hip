@@ -19,8 +19,12 @@ namespace {
 // jobs, all memory-bound, so they overlap on the chip:
 //   [0, n_pre)            LoRA pre-pass  OUT[M, r_pad] = bf16(s * P[M,K] R[r,K]^T):
 //                         128 tokens (32 per wave) and one K-slice per workgroup;
-//                         with one slice it writes OUT (columns r..r_pad-1 as 0),
-//                         else fp32 partials that prepass_reduce adds in slice order.
+//                         with one slice it writes OUT (columns r..r_pad-1 as 0);
+//                         with several, either each slice writes bf16(s partial) to
+//                         its own r columns of OUT (when the adapter is laid out in
+//                         the same launch and the slices fit in r_pad: the adapter
+//                         repeats once per slice, so the GEMM adds the partials), or
+//                         fp32 partials that prepass_reduce adds in slice order.
 //   [n_pre, +n_adapt)     adapter layout: B padded to r_pad columns (forward) or
 //                         A^T padded to r_pad columns (input gradient).
 //   [.., +n_deq)          double dequantisation to bf16: W_hat row-major
@@ -32,8 +36,9 @@ struct PreJob {
     const uint16_t* P; int64_t ldp; int K;
     const uint16_t* R; int64_t ldr;  // R [r, K] row stride ldr, or k-major [K, r]
     uint16_t* OUT;
-    float* ppart;                    // [psplits][M][32 NT] fp32 partials when psplits > 1
+    float* ppart;                    // [psplits][M][32 NT] fp32 partials when psplits > 1 and !cat
     int psplits, kper;               // K-slices and 64-wide K-chunks per slice
+    int cat;                         // slice sp writes its own bf16 partial to OUT columns sp r .. sp r + r - 1
     int n;                           // workgroups of this job
 };
 
@@ -45,6 +50,7 @@ struct PrologueArgs {
     PreJob pre[2];
     int M, r, r_pad; float s;
     int adapt_mode;                 // 0 none, 1 pad columns, 2 transpose + pad
+    int reps;                       // copies of the adapter's r columns side by side (one per slice of a cat job)
     const uint16_t* asrc; uint16_t* adst; int64_t arows, acols;
     int n_pre, n_adapt, n_deq;      // n_pre = pre[0].n + pre[1].n
     int trans_tiles;                // 64 x 64 tiles per transposed-dequant workgroup (1..4)
@@ -188,6 +194,25 @@ __device__ __forceinline__ void prepass_job(const PreJob& j, const PrologueArgs&
     // D of tile t: lane l holds ranks 32 t + 8 (v / 4) + 4 (l / 32) + v % 4 of token l % 32
     const int m = m0 + 32 * wave + (lane & 31);
     if (m >= a.M) return;
+    if (j.cat) {
+        // r % 4 == 0: each group of 4 ranks is wholly below r or wholly past it
+        uint16_t* orow = j.OUT + static_cast<int64_t>(m) * a.r_pad;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = t * 32 + 8 * gq + 4 * (lane >> 5);
+                if (n < a.r)
+                    *reinterpret_cast<uint2*>(orow + sp * a.r + n) =
+                        uint2{pack_bf16x2(a.s * acc[t][4 * gq], a.s * acc[t][4 * gq + 1]),
+                              pack_bf16x2(a.s * acc[t][4 * gq + 2], a.s * acc[t][4 * gq + 3])};
+            }
+        }
+        if (sp == j.psplits - 1)
+            for (int n = j.psplits * a.r + 4 * (lane >> 5); n < a.r_pad; n += 8)   // padding columns
+                *reinterpret_cast<uint2*>(orow + n) = uint2{0u, 0u};
+        return;
+    }
     if (j.psplits == 1) {
         uint16_t* orow = j.OUT + static_cast<int64_t>(m) * a.r_pad;
 #pragma unroll
@@ -254,16 +279,19 @@ __device__ __forceinline__ void adapt_job(const PrologueArgs& a, int b) {
     const int j0 = static_cast<int>(c % cpr) * 8;
     uint16_t v[8];
     if (a.adapt_mode == 1) {                                       // B [arows, r] -> [arows, r_pad]
-        if (j0 + 8 <= a.acols && (a.acols & 7) == 0) {
-            const uint4 w = *reinterpret_cast<const uint4*>(a.asrc + i * a.acols + j0);
+        const int r = static_cast<int>(a.acols), span = r * a.reps;
+        if (j0 + 8 <= span && (r & 7) == 0) {
+            const uint4 w = *reinterpret_cast<const uint4*>(a.asrc + i * r + j0 % r);
             *reinterpret_cast<uint4*>(a.adst + c * 8) = w;
             return;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = j0 + e < a.acols ? a.asrc[i * a.acols + j0 + e] : uint16_t{0};
+        for (int e = 0; e < 8; ++e) v[e] = j0 + e < span ? a.asrc[i * r + (j0 + e) % r] : uint16_t{0};
     } else {                                                       // A [r, acols] -> A^T [acols, r_pad]
+        const int r = static_cast<int>(a.arows), span = r * a.reps;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = j0 + e < a.arows ? a.asrc[static_cast<int64_t>(j0 + e) * a.acols + i] : uint16_t{0};
+        for (int e = 0; e < 8; ++e)
+            v[e] = j0 + e < span ? a.asrc[static_cast<int64_t>((j0 + e) % r) * a.acols + i] : uint16_t{0};
     }
     *reinterpret_cast<uint4*>(a.adst + c * 8) =
         uint4{v[0] | (static_cast<uint32_t>(v[1]) << 16), v[2] | (static_cast<uint32_t>(v[3]) << 16),
@@ -424,13 +452,24 @@ PrepassSplit prepass_split(int64_t M, int64_t K) {
 
 namespace {
 
+// cat_max > 1: up to cat_max K-slices, each writing its bf16 partial into its own
+// column block of OUT (no reduction); otherwise fp32 partials in ppart (if given).
 PreJob make_job(const uint16_t* P, int64_t ldp, int64_t M, int64_t K, const uint16_t* R, int64_t ldr,
-                uint16_t* OUT, float* ppart) {
+                uint16_t* OUT, float* ppart, int cat_max = 0) {
     PreJob j;
     j.P = P; j.ldp = ldp; j.K = static_cast<int>(K); j.R = R; j.ldr = ldr; j.OUT = OUT; j.ppart = ppart;
     const PrepassSplit ps = prepass_split(M, K);
-    j.psplits = ppart == nullptr ? 1 : ps.splits;
-    j.kper = j.psplits == 1 ? static_cast<int>(K / 64) : ps.kper;
+    j.cat = 0;
+    if (cat_max > 1 && ps.splits > 1) {
+        const int64_t nk = K / 64;
+        const int64_t want = std::min<int64_t>(ps.splits, cat_max);
+        j.kper = static_cast<int>((nk + want - 1) / want);
+        j.psplits = static_cast<int>((nk + j.kper - 1) / j.kper);
+        j.cat = j.psplits > 1 ? 1 : 0;
+    } else {
+        j.psplits = ppart == nullptr ? 1 : ps.splits;
+        j.kper = j.psplits == 1 ? static_cast<int>(K / 64) : ps.kper;
+    }
     j.n = static_cast<int>((M + 127) / 128) * j.psplits;
     return j;
 }
@@ -458,8 +497,8 @@ hipError_t launch_prologue_args(PrologueArgs& a, bool km0, bool km1, hipStream_t
         }
     }
     const int64_t per_job = (static_cast<int64_t>(a.M) * (a.r_pad / 4) + 255) / 256;
-    const int blocks0 = a.pre[0].n > 0 && a.pre[0].psplits > 1 ? static_cast<int>(per_job) : 0;
-    const int blocks1 = a.pre[1].n > 0 && a.pre[1].psplits > 1 ? static_cast<int>(per_job) : 0;
+    const int blocks0 = a.pre[0].n > 0 && a.pre[0].psplits > 1 && !a.pre[0].cat ? static_cast<int>(per_job) : 0;
+    const int blocks1 = a.pre[1].n > 0 && a.pre[1].psplits > 1 && !a.pre[1].cat ? static_cast<int>(per_job) : 0;
     if (blocks0 + blocks1 > 0) {
         const ReduceJob r0{a.pre[0].ppart, a.pre[0].OUT, a.pre[0].psplits};
         const ReduceJob r1{a.pre[1].ppart, a.pre[1].OUT, a.pre[1].psplits};
@@ -480,10 +519,15 @@ hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t 
     PrologueArgs a{};
     a.codes = codes; a.bc = bc;
     a.d_out = d_out; a.d_in = d_in; a.transposed = transposed ? 1 : 0; a.what = what;
-    a.pre[0] = make_job(P, ldp, M, K, R, ldr, OUT, ppart);
+    // With the adapter laid out here (r < r_pad), the K-slices of the pre-pass can each
+    // take r of the r_pad columns and the adapter repeat once per slice: the GEMM's
+    // LoRA K-steps then add the slice partials, and no reduction pass is needed.
+    const int cat_max = adapt_mode != 0 && r % 4 == 0 ? r_pad / r : 0;
+    a.pre[0] = make_job(P, ldp, M, K, R, ldr, OUT, ppart, cat_max);
     a.pre[1] = PreJob{};
     a.M = static_cast<int>(M); a.r = r; a.s = s; a.r_pad = r_pad;
     a.adapt_mode = adapt_mode; a.asrc = asrc; a.adst = adst; a.arows = arows; a.acols = acols;
+    a.reps = a.pre[0].cat ? a.pre[0].psplits : 1;
     const int64_t adapt_elems = adapt_mode == 0 ? 0 : (adapt_mode == 1 ? arows : acols) * r_pad;
     a.n_adapt = static_cast<int>((adapt_elems / 8 + 255) / 256);    // one 8-entry chunk per thread
     const int64_t n = d_out * d_in;
@@ -504,7 +548,7 @@ hipError_t launch_prepass_pair(const uint16_t* P0, int64_t ldp0, int64_t K0, con
     a.pre[0] = make_job(P0, ldp0, M, K0, R0, ldr0, OUT0, ppart0);
     a.pre[1] = make_job(P1, ldp1, M, K1, R1, ldr1, OUT1, ppart1);
     a.M = static_cast<int>(M); a.r = r; a.s = s; a.r_pad = r_pad;
-    a.n_adapt = 0; a.n_deq = 0; a.trans_tiles = 1;
+    a.n_adapt = 0; a.n_deq = 0; a.trans_tiles = 1; a.reps = 1;
     return launch_prologue_args(a, false, r1_kmajor, st);
 }
 
