@@ -5,8 +5,8 @@
 // the loss gradient dY (torch layout, one token per row):
 //     dB [d_out, r] = s dY^T (X A^T) = dY^T T',   T' = bf16(s X A^T)
 //     dA [r, d_in]  = s (dY B)^T X   = U'^T X,    U' = bf16(s dY B)
-// T' and U' come from the linear layer's LoRA pre-pass (the same bf16 operands the
-// forward and input-gradient GEMMs use). What remains is a reduction over the
+// T' and U' come from the LoRA pre-pass of the linear calls (here with its K-slice
+// partials added before the rounding to bf16). What remains is a reduction over the
 // d_seq tokens, out[n, j] = sum_m P[m, n] T[m, j] with P = dY or X: tall and skinny
 // (N = 4096 columns, r = 16 rank entries, K = d_seq), bound by the single read of P.
 //

@@ -254,9 +254,10 @@ int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_
  *    with respect to A and B]
  *   With T = X A^T and U = dY B ([d_seq, r]):
  *     dA [r, d_in]  = s U^T X,     dB [d_out, r] = s dY^T T,
- *   computed from the bf16 operands U' = bf16(s U) and T' = bf16(s T) (the same ones
- *   the forward and input-gradient GEMMs consume), float32 accumulation, float32
- *   outputs (overwritten). The quantised weight is not needed.
+ *   computed from the bf16 operands U' = bf16(s U) and T' = bf16(s T) (the linear
+ *   calls' GEMMs consume the same products, rounded to bf16 once or once per K-slice
+ *   of their pre-pass), float32 accumulation, float32 outputs (overwritten). The
+ *   quantised weight is not needed.
  *   A [r, d_in], B [d_out, r], X [d_seq, d_in], dY [d_seq, d_out] bf16 (device);
  *   dA, dB float32 (device).
  *   Same shape rules as qlora_linear_fwd (d_in, d_out multiples of 64, 1 <= r <= 256,
