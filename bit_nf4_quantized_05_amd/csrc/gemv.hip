@@ -73,9 +73,11 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
 // loads by one wave each and passed through LDS: the x segment (waves 0..7), the
 // A x slice partials (waves 10..13) and the 16 rows of B (wave 14). The block
 // constants are per row: lane l loads block l's 8-bit code (or a_j) and scale with
-// its code words. Every wave issues the loads it must wait for before its code
-// loads, so that wait never covers the codes, and the next segment's loads go out
-// before the current one is computed.
+// its code words. The first segment's code loads go out only after the first
+// barrier (x, B and the tables in LDS): issued at once with x they filled the
+// memory queues ahead of it and every wave started later (one-launch decode on a
+// 4096 x 4096 layer: 7.3 -> 6.7 us median). The next segment's loads go out before
+// the current one is computed.
 // A lane forms a_hat of block l and hands it to the two lanes owning the block's
 // halves by a cross-lane read. Each code byte (two weights) is looked up as a pair
 // of bf16 code values and dotted with the bf16 x pair (v_dot2_f32_bf16); a_hat
@@ -163,7 +165,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
         }
     };
 
-    // ---- loads: staged data first, then the codes
+    // ---- loads: staged data first (the codes follow the first barrier)
     uint4 st = uint4{0, 0, 0, 0};
     stage_issue(st, 0);
     const int nval = nparts * r;                  // <= 1024
@@ -190,10 +192,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
         for (int i = 0; i < 8; ++i)
             if (64 * i < nbv) bst[i] = b4[min(lane + 64 * i, nbv - 1)];
     }
-    __builtin_amdgcn_sched_barrier(0);
     GvRowSeg g0, g1;
-    seg_issue(g0, 0);
-    __builtin_amdgcn_sched_barrier(0);
 
     // ---- tables and staged data to LDS; the barriers wait for LDS writes only
     if (tid < 256) {
@@ -218,6 +217,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
             if (lane + 64 * i < nbv) bs[lane + 64 * i] = bst[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    seg_issue(g0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (kAx) {
         // s (A x) of rank row `wave`: 8 chunk dot products per lane, then a fixed xor tree
         float t = 0.0f;
