@@ -81,9 +81,13 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
 // an adapter layout job (adapt_mode 1: B [arows, acols] -> [arows, r_pad] zero-padded;
 // 2: A [arows, acols] -> A^T [acols, r_pad] zero-padded; 0: none), and the double
 // dequantisation to W_hat [d_out, d_in] or W_hat^T [d_in, d_out] (transposed; none if
-// what is null). The pre-pass splits K over prepass_split(M, K).splits workgroups per
-// 128 tokens, whose fp32 partials go to ppart (splits * M * 32 ceil(r/32) floats) and
-// are added by a second small launch; a null ppart runs it unsplit.
+// what is null). The pre-pass splits K over up to prepass_split(M, K).splits workgroups
+// per 128 tokens. With an adapter job, r % 4 == 0 and at least two slices of r columns
+// fitting in r_pad, slice s writes bf16(s * its partial) to OUT columns s r .. s r + r - 1
+// (the rest zero) and the adapter layout repeats its r columns once per slice, so the
+// GEMM adds the partials; otherwise the fp32 partials go to ppart (splits * M *
+// 32 ceil(r/32) floats) and are added by a second small launch; a null ppart runs it
+// unsplit.
 struct PrepassSplit { int splits, kper; };
 PrepassSplit prepass_split(int64_t M, int64_t K);
 hipError_t launch_prologue(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
