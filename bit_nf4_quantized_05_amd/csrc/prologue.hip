@@ -453,17 +453,21 @@ PrepassSplit prepass_split(int64_t M, int64_t K) {
 namespace {
 
 // cat_max > 1: up to cat_max K-slices, each writing its bf16 partial into its own
-// column block of OUT (no reduction); otherwise fp32 partials in ppart (if given).
+// column block of OUT (no reduction), unless that makes a slice much longer than the
+// split it replaces (more than max(16, that split's) 64-wide K-chunks: the pre-pass
+// would outlast the rest of the launch); otherwise fp32 partials in ppart (if given).
 PreJob make_job(const uint16_t* P, int64_t ldp, int64_t M, int64_t K, const uint16_t* R, int64_t ldr,
                 uint16_t* OUT, float* ppart, int cat_max = 0) {
     PreJob j;
     j.P = P; j.ldp = ldp; j.K = static_cast<int>(K); j.R = R; j.ldr = ldr; j.OUT = OUT; j.ppart = ppart;
     const PrepassSplit ps = prepass_split(M, K);
+    const int64_t nk = K / 64;
+    const int64_t cat_kper = cat_max > 1 ? (nk + std::min<int64_t>(ps.splits, cat_max) - 1) /
+                                               std::min<int64_t>(ps.splits, cat_max)
+                                         : 0;
     j.cat = 0;
-    if (cat_max > 1 && ps.splits > 1) {
-        const int64_t nk = K / 64;
-        const int64_t want = std::min<int64_t>(ps.splits, cat_max);
-        j.kper = static_cast<int>((nk + want - 1) / want);
+    if (cat_max > 1 && ps.splits > 1 && cat_kper <= std::max(16, ps.kper)) {
+        j.kper = static_cast<int>(cat_kper);
         j.psplits = static_cast<int>((nk + j.kper - 1) / j.kper);
         j.cat = j.psplits > 1 ? 1 : 0;
     } else {

@@ -211,6 +211,12 @@ LINEAR_SMALL = [
     WL.custom("bmajor_r24", 256, 320, 100, 24, s=1.5),
     WL.custom("bmajor_r32", 192, 448, 77, 32, s=0.75),
     WL.custom("btrans_r40", 192, 448, 77, 40, s=0.75),
+    # pre-pass K-slices: side by side in the LoRA columns (r = 16, 4 slices; r = 12, 5
+    # slices and 4 zero columns), or fp32 partials plus a reduction when 4 slices of a
+    # long K would each be far longer than the split they replace (d_in = 16384 fwd)
+    WL.custom("slices_cat_r16", 1024, 4096, 256, 16, s=1.25),
+    WL.custom("slices_cat_r12", 512, 2048, 160, 12, s=0.5),
+    WL.custom("slices_long_k", 512, 16384, 128, 16, s=2.0),
 ]
 
 
