@@ -108,7 +108,8 @@ hipError_t launch_prepass_pair(const uint16_t* P0, int64_t ldp0, int64_t K0, con
 // 32-rank MFMA tile, whose transposing reads keep the kernel's occupancy), which spares
 // the input gradient a transpose of B.
 inline bool prepass_takes_kmajor(int r) { return r % 8 == 0 && r <= 32; }
-// dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols.
+// dst[j, i] = i < rows ? src[i, j] : 0, for j < cols, i < ld_dst. src is rows x cols,
+// 16-byte aligned; 1 <= cols <= 256, ld_dst >= rows and ld_dst % 8 == 0 (else an error).
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);
 

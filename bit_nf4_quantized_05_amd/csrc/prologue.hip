@@ -428,12 +428,71 @@ void prologue_kernel(PrologueArgs a, NF4Tables tab) {
 // ---------------------------------------------------------------------------
 // Small layout helpers for the adapter matrices.
 // ---------------------------------------------------------------------------
-__global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
-                                     uint16_t* __restrict__ dst, int64_t ld_dst) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (idx >= cols * ld_dst) return;
-    const int64_t j = idx / ld_dst, i = idx % ld_dst;
-    dst[idx] = i < rows ? src[i * cols + j] : static_cast<uint16_t>(0);
+// src [rows, cols] -> dst [cols, ld_dst] = src^T, zero in columns rows..ld_dst-1
+// (cols <= 256, ld_dst % 8 == 0, src 16-byte aligned). A workgroup takes 64 source rows,
+// one contiguous span of 64 cols elements starting 128 cols bytes into src, so 16-byte
+// aligned: it is read with 16-byte loads (all issued before any is used) into LDS, then
+// written as cols destination segments of 64 elements, 16 bytes per thread.
+constexpr int kTpRows = 64;
+constexpr int kTpMaxCols = 256;
+constexpr int kTpPer = kTpRows * kTpMaxCols / 8 / 256;      // 16-byte pieces per thread at most
+
+__global__ __launch_bounds__(256)
+void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
+                          uint16_t* __restrict__ dst, int64_t ld_dst) {
+    __shared__ uint16_t t[kTpRows * (kTpMaxCols + 2)];
+    const int tid = threadIdx.x;
+    const int nc = static_cast<int>(cols);
+    const int pitch = nc + 2;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kTpRows;
+    const int nrow = static_cast<int>(std::min<int64_t>(kTpRows, std::max<int64_t>(0, rows - i0)));
+    const int total = nrow * nc;                                  // elements of the span
+    const uint16_t* sp = src + i0 * cols;
+    uint4 v[kTpPer];
+#pragma unroll
+    for (int k = 0; k < kTpPer; ++k) {
+        const int e0 = 8 * (tid + 256 * k);
+        v[k] = uint4{0, 0, 0, 0};
+        if (e0 + 8 <= total) {
+            v[k] = *reinterpret_cast<const uint4*>(sp + e0);
+        } else if (e0 < total) {                                  // the span's last, partial piece
+            uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (e0 + q < total) w[q >> 1] |= static_cast<uint32_t>(sp[e0 + q]) << (16 * (q & 1));
+            v[k] = uint4{w[0], w[1], w[2], w[3]};
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kTpPer; ++k) {
+        const int e0 = 8 * (tid + 256 * k);
+        if (e0 < total) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int e = e0 + q;
+                if (e < total) t[(e / nc) * pitch + e % nc] = static_cast<uint16_t>(w[q >> 1] >> (16 * (q & 1)));
+            }
+        }
+    }
+    __syncthreads();
+    // destination piece p: row j = p / 8 of dst, elements i0 + 8 (p % 8) .. + 7
+#pragma unroll
+    for (int k = 0; k < kTpPer; ++k) {
+        const int p = tid + 256 * k;
+        const int j = p >> 3, q8 = 8 * (p & 7);
+        if (j < nc && i0 + q8 < ld_dst) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int a = q8 + 2 * h, b = a + 1;
+                const uint32_t lo = a < nrow ? t[a * pitch + j] : 0u;
+                const uint32_t hi = b < nrow ? t[b * pitch + j] : 0u;
+                w[h] = lo | (hi << 16);
+            }
+            *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(j) * ld_dst + i0 + q8) = uint4{w[0], w[1], w[2], w[3]};
+        }
+    }
 }
 
 }  // namespace
@@ -558,9 +617,10 @@ hipError_t launch_prepass_pair(const uint16_t* P0, int64_t ldp0, int64_t K0, con
 
 hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st) {
-    const int64_t total = cols * ld_dst;
-    QN_LAUNCH("transpose_pad_kernel", st, transpose_pad_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
-                       src, rows, cols, dst, ld_dst);
+    if (cols < 1 || cols > kTpMaxCols || ld_dst % 8 != 0 || ld_dst < rows) return hipErrorInvalidValue;
+    QN_LAUNCH("transpose_pad_kernel", st, transpose_pad_kernel,
+              dim3(static_cast<unsigned>((ld_dst + kTpRows - 1) / kTpRows)), dim3(256), 0, st, src, rows, cols, dst,
+              ld_dst);
     return hipGetLastError();
 }
 
