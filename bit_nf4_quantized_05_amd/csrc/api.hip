@@ -185,14 +185,15 @@ void prof_end(void* token, const char* name, hipStream_t st) {
 
 namespace {
 
-// The forward once the arguments are checked: d_seq == 1 streams the codes (GEMV),
-// d_seq <= 64 runs the small-batch kernel, otherwise dequantise + pre-pass + GEMM.
+// The forward once the arguments are checked: d_seq == 1 (and up to 3 tokens when r <= 16
+// and d_in <= 4096) streams the codes (GEMV), d_seq <= 64 runs the small-batch kernel,
+// otherwise dequantise + pre-pass + GEMM.
 int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_out, int64_t d_in,
                    const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t d_seq,
                    uint16_t* Y, char* ws, const LinWs& lw, hipStream_t st) {
     hipError_t e;
-    if (d_seq == 1) {
-        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, Y,
+    if (qn::gemv_takes_tokens(d_seq, d_in, r)) {
+        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, d_seq, Y,
                                 reinterpret_cast<float*>(ws + lw.t), st);
         if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
         return 0;

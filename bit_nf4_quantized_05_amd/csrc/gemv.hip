@@ -117,14 +117,19 @@ __device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv,
 // chunks 4 l .. 4 l + 3; their order is XORed with bits 2..3 of l
 __device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c >> 4) & 3)); }
 
-template <bool kAx>
+// T tokens (1, 2 or 3; the ntok <= T real ones first, x rows past ntok read as zero and
+// their outputs not stored): each code-pair lookup serves all T tokens. T > 1 only with
+// the one-launch form (kAx); 4 tokens would need more than the 128 registers a lane has
+// at 16 waves per CU.
+template <int T, bool kAx>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
-                     int d_out, int d_in, const uint16_t* __restrict__ x,
+                     int d_out, int d_in, const uint16_t* __restrict__ x, int ntok,
                      const uint16_t* __restrict__ B, int r, float s, const float* __restrict__ part,
                      int nparts, const uint16_t* __restrict__ A, uint16_t* __restrict__ y, NF4Tables tab) {
+    static_assert(T == 1 || kAx, "several tokens only in the one-launch form");
     __shared__ uint4 lut4[256 * kLutCopies / 4];
-    __shared__ uint4 xs[2][kGvSeg / 8];
+    __shared__ uint4 xs[2][T][kGvSeg / 8];
     __shared__ float tvs[1024];
     __shared__ uint4 bs[kGvWaves * 256 * 2 / 16];     // the 16 rows of B (r <= 256)
     __shared__ float qlut[256];
@@ -138,19 +143,25 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     const int row = min(row0 + wave, d_out - 1);
     const int nbpr = d_in / 64;
     const int upr = d_in / 32;                    // 16-byte code words per row
-    const int nseg = (d_in + kGvSeg - 1) / kGvSeg;
+    const int nseg = kAx ? 1 : (d_in + kGvSeg - 1) / kGvSeg;   // the one-launch form takes d_in <= kGvSeg
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
     const int64_t row_u = static_cast<int64_t>(row) * upr;
 
-    // the x segment: waves 0..7, one 16-byte chunk per lane
-    auto stage_issue = [&](uint4& g, int S) {
+    // the x segment of each token: waves 0..7, one 16-byte chunk per lane and token
+    auto stage_issue = [&](uint4 (&g)[T], int S) {
         if (wave < 8) {
             const int col = S * kGvSeg + 8 * tid;
-            g = x4[min(col, d_in - 8) / 8];
+#pragma unroll
+            for (int k = 0; k < T; ++k)
+                g[k] = x4[(static_cast<int64_t>(min(k, ntok - 1)) * d_in + min(col, d_in - 8)) / 8];
         }
     };
-    auto stage_store = [&](const uint4& g, int S) {
-        if (wave < 8) xs[S & 1][gv_xpos(tid)] = S * kGvSeg + 8 * tid < d_in ? g : uint4{0, 0, 0, 0};
+    auto stage_store = [&](const uint4 (&g)[T], int S) {
+        if (wave < 8) {
+#pragma unroll
+            for (int k = 0; k < T; ++k)
+                xs[S & 1][k][gv_xpos(tid)] = S * kGvSeg + 8 * tid < d_in && k < ntok ? g[k] : uint4{0, 0, 0, 0};
+        }
     };
     auto seg_issue = [&](GvRowSeg& k, int S) {
         {
@@ -166,7 +177,9 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     };
 
     // ---- loads: staged data first (the codes follow the first barrier)
-    uint4 st = uint4{0, 0, 0, 0};
+    uint4 st[T];
+#pragma unroll
+    for (int k = 0; k < T; ++k) st[k] = uint4{0, 0, 0, 0};
     stage_issue(st, 0);
     const int nval = nparts * r;                  // <= 1024
     uint4 tst = uint4{0, 0, 0, 0};
@@ -220,24 +233,31 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     seg_issue(g0, 0);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (kAx) {
-        // s (A x) of rank row `wave`: 8 chunk dot products per lane, then a fixed xor tree
-        float t = 0.0f;
+        // s (A x) of rank row `wave` for each token: 8 chunk dot products per lane, then
+        // a fixed xor tree; token k's entries at s_t[16 k + rank]
+        // (one token at a time: the scheduling barrier keeps the x reads of the next
+        // token from being hoisted, which would need 32 registers per token)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = lane + 64 * e;
-            if (c < nch) {
-                const uint4 xv = xs[0][gv_xpos(c)];
-                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int k = 0; k < T; ++k) {
+            float t = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
-                                                        __builtin_bit_cast(bf16x2, xw[q]), t, false);
+            for (int e = 0; e < 8; ++e) {
+                const int c = lane + 64 * e;
+                if (c < nch) {
+                    const uint4 xv = xs[0][k][gv_xpos(c)];
+                    const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                            __builtin_bit_cast(bf16x2, xw[q]), t, false);
+                }
             }
-        }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
-        if (lane == 0 && wave < r) s_t[wave] = s * t;
+            for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+            if (lane == 0 && wave < r) s_t[16 * k + wave] = s * t;
+            if constexpr (T > 1) __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         // s (A x), summed per rank row in slice order
         if (tid < r) {
@@ -251,19 +271,49 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     const uint32_t* lut = reinterpret_cast<const uint32_t*>(lut4);
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kLutCopies - 1));
     const float mu = bc.mean[0];
-    float acc = 0.0f;
-    auto compute = [&](const GvRowSeg& k, int S) {
+    float acc[T];
+#pragma unroll
+    for (int k = 0; k < T; ++k) acc[k] = 0.0f;
+    auto compute = [&](const GvRowSeg& g, int S) {
         const int kb = S & 1;
         const bool bok = S * 64 + lane < nbpr;
-        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? k.sv : mu + k.sv * qlut[k.qv + 128];
-        const uint4* xb = xs[kb];
+        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? g.sv : mu + g.sv * qlut[g.qv + 128];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const float a = __shfl(ah, h * 32 + (lane >> 1));
-            uint4 xv[4];
+            if constexpr (T == 1) {
+                uint4 xv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xv[e] = xb[h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
-            acc += a * gemv_half_block(k.cw[h], xv, lut, lane_off);
+                for (int e = 0; e < 4; ++e) xv[e] = xs[kb][0][h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
+                acc[0] += a * gemv_half_block(g.cw[h], xv, lut, lane_off);
+            } else {
+                // one code-pair lookup per byte for all tokens; per token the same dot
+                // order as the single-token form
+                const uint32_t cw[4] = {g.cw[h].x, g.cw[h].y, g.cw[h].z, g.cw[h].w};
+                float part[T];
+#pragma unroll
+                for (int k = 0; k < T; ++k) part[k] = 0.0f;
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    uint4 xv[T];
+#pragma unroll
+                    for (int k = 0; k < T; ++k) xv[k] = xs[kb][k][h * 256 + 4 * lane + (w4 ^ ((lane >> 2) & 3))];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
+                        const bf16x2 lv = __builtin_bit_cast(bf16x2, lut[byte * kLutCopies + lane_off]);
+#pragma unroll
+                        for (int k = 0; k < T; ++k) {
+                            const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+                            part[k] = __builtin_amdgcn_fdot2_f32_bf16(lv, __builtin_bit_cast(bf16x2, xw[b]), part[k],
+                                                                      false);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int k = 0; k < T; ++k) acc[k] += a * part[k];
+            }
         }
     };
     // segment S+1's loads go out before segment S is computed; its staged data is
@@ -289,23 +339,38 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 
     // ---- rank-r term of this wave's row, row sum, store
     const uint16_t* brow = reinterpret_cast<const uint16_t*>(bs) + wave * r;
-    for (int k = lane; k < r; k += 64) acc += bf16_to_f32(brow[k]) * s_t[k];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0 && row0 + wave < d_out) y[row0 + wave] = bf16_bits(acc);
+    for (int k = 0; k < T; ++k) {
+        float v = acc[k];
+        for (int j = lane; j < r; j += 64) v += bf16_to_f32(brow[j]) * s_t[16 * k + j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0 && row0 + wave < d_out && k < ntok) y[static_cast<int64_t>(k) * d_out + row0 + wave] = bf16_bits(v);
+    }
 }
 
 }  // namespace
 
+bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r) {
+    return d_seq == 1 || (d_seq <= kGemvMaxTokens && r <= kGvWaves && d_in <= kGvSeg);
+}
+
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
-                           const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st) {
+                           const uint16_t* x, int64_t d_seq, uint16_t* y, float* ws_part, hipStream_t st) {
+    if (!gemv_takes_tokens(d_seq, d_in, r)) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
+    const int nt = static_cast<int>(d_seq);
     if (r <= kGvWaves && d_in <= kGvSeg) {
         // one launch: every workgroup forms s A x from A (r x d_in <= 16 x 4096 bf16)
-        QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<true>, grid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B,
-                  r, s, ws_part, 0, A, y, tables());
+#define QN_GV_LAUNCH(TT) \
+        QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<TT, true>), grid, dim3(64 * kGvWaves), 0, st, \
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, nt, \
+                  B, r, s, ws_part, 0, A, y, tables())
+        if (nt == 1) QN_GV_LAUNCH(1);
+        else if (nt == 2) QN_GV_LAUNCH(2);
+        else QN_GV_LAUNCH(3);
+#undef QN_GV_LAUNCH
         return hipGetLastError();
     }
     // slices of A x: at most 16, and nparts * r <= 1024 partials in all
@@ -315,8 +380,8 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     const int nparts = (nb64 + per - 1) / per;   // <= want
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
-    QN_LAUNCH("gemv_nf4_kernel", st, gemv_nf4_kernel<false>, grid, dim3(64 * kGvWaves), 0, st,
-              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B,
+    QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<1, false>), grid, dim3(64 * kGvWaves), 0, st,
+              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, 1, B,
               r, s, ws_part, nparts, A, y, tables());
     return hipGetLastError();
 }

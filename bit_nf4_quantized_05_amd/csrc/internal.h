@@ -114,11 +114,15 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
                                 uint16_t* dst, int64_t ld_dst, hipStream_t st);
 
 // ---- gemv.hip ----
-// y[o] = sum_i w_hat[o,i] x[i] + s * sum_k B[o,k] (A x)[k], streaming the packed codes;
-// ws_part holds at most d_in/64 x r floats of partial A x sums.
+// y[t, o] = sum_i w_hat[o,i] x[t, i] + s * sum_k B[o,k] (A x_t)[k], streaming the packed
+// codes, for d_seq = 1, or for 2 <= d_seq <= kGemvMaxTokens tokens when r <= 16 and
+// d_in <= 4096 (gemv_takes_tokens); ws_part holds at most d_in/64 x r floats of partial
+// A x sums (d_seq = 1 only).
+constexpr int kGemvMaxTokens = 3;
+bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r);
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
-                           const uint16_t* x, uint16_t* y, float* ws_part, hipStream_t st);
+                           const uint16_t* x, int64_t d_seq, uint16_t* y, float* ws_part, hipStream_t st);
 
 // ---- skinny.hip ----
 // Small-batch forward, 2 <= d_seq <= 64: Y = dequant(W) X + bf16(s X A^T) B^T from the

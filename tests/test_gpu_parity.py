@@ -203,6 +203,10 @@ LINEAR_SMALL = [
     WL.custom("gemv_one_r16_k4096", 192, 4096, 1, 16, s=1.5),
     WL.custom("gemv_one_r5_k960", 320, 960, 1, 5, s=0.5),
     WL.custom("gemv_two_r17_k4096", 192, 4096, 1, 17, s=1.5),
+    # 2 and 3 tokens with r <= 16 and d_in <= 4096 take the GEMV (one code lookup for all tokens)
+    WL.custom("gemv_tok2_r16_k4096", 1024, 4096, 2, 16, s=1.5),
+    WL.custom("gemv_tok3_r5_k960", 320, 960, 3, 5, s=0.5),
+    WL.custom("gemv_tok3_r16_k64", 64, 64, 3, 16, s=2.0),
     # at most 128 output tiles: the GEMM splits K over 2..4 workgroups per tile
     WL.custom("split_fwd", 512, 4096, 200, 16, s=2.0),       # fwd 2 tiles -> 4 splits
     WL.custom("split_bwd", 4096, 512, 130, 64, s=1.0),       # dX 2 tiles -> 4 splits, ragged tokens
