@@ -163,9 +163,10 @@ int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq,
  *   (float32 accumulation, one final round to nearest even).
  *   s is the LoRA scale (float32).
  * Requires d_in % 64 == 0 and d_out % 64 == 0 (-2 otherwise), 1 <= r <= 256,
- * d_seq >= 1. d_seq == 1 runs a streaming GEMV over the packed codes; 2 <= d_seq <= 64
- * streams the codes once into small MFMA tiles; larger d_seq dequantises W to bf16 in
- * the workspace and runs the MFMA GEMM with the LoRA branch as extra K-steps.
+ * d_seq >= 1. d_seq == 1 (and d_seq = 2, 3 when r <= 16 and d_in <= 4096) runs a
+ * streaming GEMV over the packed codes; other d_seq <= 64 stream the codes once into
+ * small MFMA tiles; larger d_seq dequantises W to bf16 in the workspace and runs the
+ * MFMA GEMM with the LoRA branch as extra K-steps.
  */
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                      const float* qmean, int64_t d_out, int64_t d_in,
