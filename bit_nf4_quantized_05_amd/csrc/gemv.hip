@@ -12,10 +12,11 @@ namespace qn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// d_seq = 1 (decode). When all of A fits one 4096-column segment with r <= 16
-// (A <= 128 KB, read from L2 by every workgroup), one launch: each gemv_nf4
-// workgroup forms s A x itself, wave j the dot product of row j of A with the x
-// segment it has staged in LDS anyway. Otherwise two launches:
+// d_seq = 1 (decode), and 2 or 3 tokens. When all of A fits one 4096-column segment
+// with r <= 16 (A <= 128 KB, read from L2 by every workgroup), one launch: each
+// gemv_nf4 workgroup forms s A x itself, wave j the dot product of row j of A with the
+// x segment (of each token) it has staged in LDS anyway. Otherwise (one token only)
+// two launches:
 //   lora_ax_partial: the 64-column blocks of x are split into nparts contiguous
 //     slices (nparts * r <= 1024); workgroup w writes, for every rank row j, the dot
 //     product of A[j] and x over slice w to part[w][j] (fixed summation order).
@@ -85,7 +86,8 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
 // over its block). The lookup table is replicated kLutCopies times with copy c in
 // bank c, so a half-wave never collides, and the x chunks are XOR-swizzled so the
 // 16-byte reads of 16 lanes hit 16 distinct bank groups. s (A x) is formed before
-// the weight loop, so each wave finishes on its own.
+// the weight loop, so each wave finishes on its own (formed after it, the A loads
+// would have longer to land, but the call measured 7.6 against 6.9 us).
 constexpr int kGvWaves = 16;
 constexpr int kGvSeg = 4096;
 constexpr int kLutCopies = 32;
