@@ -4,9 +4,10 @@
 // equal probability steps, with a separate negative half (7 values) and positive
 // half (8 values) that share one exact zero, normalised so the ends are -1 and +1
 // (learn.ifs.name QLoRA deck, cards 2-3; whoami-wesleyyou.top "1. NF4"; the printed
-// quant book of jjjymmm.cn "4-bit NormalFloat(NF4)"). The outermost probability is
-// the midpoint of the half-bin offsets of a 15-level and a 16-level scheme,
-// 1 - 1/30 and 1 - 1/32, which keeps the infinite quantile at p = 1 out.
+// quant book of jjjymmm.cn "4-bit NormalFloat(NF4)"). The outermost probability,
+// which keeps the infinite quantile at p = 1 out, is 0.967704: the printed 4-decimal
+// book holds for offsets in [0.9677024, 0.9677083] only, and this value keeps each
+// of the 16 entries farthest inside the rounding interval of its printed digits.
 //
 // Quantiles are found by bisection on the normal CDF written with erfc, in double;
 // the float32 rounding of each value has a wide margin to that error.
@@ -47,7 +48,7 @@ float round_down_f32(double v) {
 
 NF4Tables build() {
     NF4Tables t{};
-    const double top = 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0));
+    const double top = 0.967704;
     const double norm = normal_quantile(top);
     double v[16];
     // negative half, most negative first: probabilities 1-top ... stepping to 1/2

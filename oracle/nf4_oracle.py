@@ -53,12 +53,16 @@ DQ_FORMATS = ("int8", "fp8", "none")
 def nf4_offset() -> float:
     """Probability of the outermost code.
 
-    Equal-probability bins place the outermost sample half a bin inside the
-    open end of the CDF, avoiding the infinite quantile at p = 1 [P1 分位数采样与
-    端点问题]. With 2^k = 16 levels that offset is 1 - 1/32, with the 15 levels of
-    a symmetric scheme it is 1 - 1/30; the code book uses their midpoint (the
-    pages give no value; this one reproduces the printed table)."""
-    return 0.5 * ((1.0 - 1.0 / 30.0) + (1.0 - 1.0 / 32.0))
+    Equal-probability bins place the outermost sample inside the open end of the
+    CDF, avoiding the infinite quantile at p = 1 [P1 分位数采样与端点问题]; the pages
+    do not say how far inside. It is the one free parameter of the construction,
+    and the printed quant book [P4 4-bit NormalFloat(NF4)] fixes it: the 16 values
+    round to the printed 4 decimals exactly for offsets in [0.9677024, 0.9677083]
+    and for no other. The offset used is 0.967704, the six-decimal value that keeps
+    every entry farthest inside the rounding interval of its printed digits (at
+    least 2.0e-6 from either edge). It lies between the half-bin offsets of a
+    15-level and a 16-level scheme, 1 - 1/30 and 1 - 1/32."""
+    return 0.967704
 
 
 def codebook_f64(inv_cdf=None) -> np.ndarray:

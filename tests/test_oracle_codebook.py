@@ -24,14 +24,12 @@ def printed(golden_dir):
 
 def test_matches_printed_table_to_4dp(printed):
     c = O.codebook_f64()
-    # A 4-decimal print is within half a unit of the 4th place of the true value.
-    # Entry 6 (-0.091049976) sits 2.4e-8 past that half unit from the printed
-    # -0.0911, hence the 3e-8 slack.
-    assert np.all(np.abs(c - printed) <= 5e-5 + 3e-8), np.abs(c - printed)
-    # all but that one entry round to exactly the printed digits
-    rounded = np.round(c, 4)
-    mism = np.nonzero(rounded != printed)[0]
-    assert set(mism.tolist()) <= {6}
+    # a 4-decimal print is within half a unit of the 4th place of the true value,
+    # on every one of the 16 entries
+    assert np.all(np.abs(c - printed) <= 5e-5), np.abs(c - printed)
+    assert np.array_equal(np.round(c, 4), printed)
+    # the float32 book the layer uses rounds to the same digits
+    assert np.array_equal(np.round(O.codebook().astype(np.float64), 4), printed)
 
 
 def test_structure_exact_zero_and_ends():
@@ -63,12 +61,46 @@ def test_equal_probability_steps_on_each_half():
     assert np.allclose(np.diff(neg), (d - 0.5) / 7, atol=1e-12, rtol=0)
 
 
-def test_outer_offset_is_between_the_15_and_16_level_half_bins():
+def _book_for(d):
+    """The asymmetric book for outer probabilities d (scalar or 1-D array), written
+    with scipy's ndtri (a different inverse-CDF routine from the oracle's)."""
+    d = np.atleast_1d(np.asarray(d, np.float64))[:, None]
+    pos = ndtri(d - np.arange(8)[None, :] * (d - 0.5) / 8)
+    neg = -ndtri(d - np.arange(7)[None, :] * (d - 0.5) / 7)
+    v = np.concatenate([neg, np.zeros((d.shape[0], 1)), pos], axis=1)
+    return np.squeeze(np.sort(v, axis=1) / ndtri(d))
+
+
+def test_offset_lies_inside_the_interval_the_printed_book_allows(printed):
+    # Scan the outer probability over (0.55, 1) in steps of 2.2e-7: the offsets whose
+    # book rounds to all 16 printed digits form one short interval, and the oracle's
+    # offset is inside it with room on both sides.
+    grid = np.linspace(0.55, 0.99999, 2_000_001)
+    ok = np.nonzero(np.all(np.round(_book_for(grid), 4) == printed[None, :], axis=1))[0]
+    assert ok.size > 0, "no offset reproduces the printed book"
+    assert ok[-1] - ok[0] + 1 == ok.size, "the matching offsets are not one interval"
+    lo, hi = grid[ok[0]], grid[ok[-1]]
+    assert hi - lo < 1e-5
     d = O.nf4_offset()
+    assert lo < d < hi
+
+    def fits(x):
+        return np.array_equal(np.round(_book_for(x), 4), printed)
+
+    # the interval's edges, to 1e-9 by bisection from the scanned points
+    def edge(good, bad):
+        for _ in range(40):
+            mid = 0.5 * (good + bad)
+            good, bad = (mid, bad) if fits(mid) else (good, mid)
+        return good
+
+    lo_e, hi_e = edge(d, d - 1e-4), edge(d, d + 1e-4)
+    assert fits(d) and hi_e - lo_e > 5e-6
+    assert lo_e + 1e-6 < d < hi_e - 1e-6
+    # every entry at least 2e-6 inside its printed rounding interval
+    assert np.min(5e-5 - np.abs(_book_for(d) - printed)) >= 2e-6
+    # and between the half-bin offsets of 15 and 16 equal-probability levels
     assert 1 - 1 / 30 < d < 1 - 1 / 32
-    # the interval of offsets whose book rounds to the printed digits
-    # (except the borderline entry 6) contains this value
-    assert abs(d - 0.96770833) < 1e-8
 
 
 def test_page1_literal_sample_formula_is_not_the_printed_book(printed):
