@@ -32,25 +32,28 @@ SIGNATURES = {
     "nf4_quantize": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "nf4_double_dequant": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "qlora_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "qlora_linear_fwd_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "qlora_linear_bwd_x_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
     "qlora_linear_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_float,
-                                  _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+                                  _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_float,
-                                    _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+                                    _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_lora_grads_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
-    "qlora_lora_grads": (_c_int, [_c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
-                                  _c_vp, _c_i64, _c_vp]),
+    "qlora_lora_grads": (_c_int, [_c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_i64, _c_vp, _c_i64, _c_i64, _c_i64,
+                                  _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "qn_nf4_sizes_ex": (_c_int, [_c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp]),
     "nf4_quantize_ex": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "nf4_double_dequant_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
     "qlora_linear_fwd_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
-                                     _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+                                     _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
-                                       _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+                                       _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "int8_quantize": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "int8_dequant": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp]),
     "qlr_linear_workspace_bytes": (_c_i64, [_c_i64, _c_i64, _c_i64, _c_int]),
     "qlr_linear_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_int,
-                                _c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_vp]),
+                                _c_vp, _c_vp, _c_int, _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64,
+                                _c_vp]),
     "qn_profile_enable": (_c_int, [_c_int]),
     "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
 }
@@ -92,6 +95,24 @@ def _stream(dev: torch.device) -> int:
 
 def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
+
+
+def _rows(t: torch.Tensor, dtype, shape, name: str, device) -> int:
+    """Checks a [rows, cols] activation that may be a view into a wider array: unit
+    column stride, any row stride >= cols; returns the row stride (elements)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 2 or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    rows, cols = shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: the columns must be contiguous")
+    ld = t.stride(0) if rows > 1 else cols
+    if ld < cols:
+        raise ValueError(f"{name}: row stride {ld} is smaller than the row length {cols}")
+    return ld
 
 
 def _need(t: torch.Tensor, dtype, shape, name: str, device) -> None:
@@ -157,7 +178,16 @@ def quantize_workspace_bytes(d_out: int, d_in: int) -> int:
 
 
 def linear_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
+    """Bytes enough for both the forward and the input-gradient call."""
     return lib().qlora_linear_workspace_bytes(d_out, d_in, d_seq, r)
+
+
+def linear_fwd_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
+    return lib().qlora_linear_fwd_workspace_bytes(d_out, d_in, d_seq, r)
+
+
+def linear_bwd_x_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
+    return lib().qlora_linear_bwd_x_workspace_bytes(d_out, d_in, d_seq, r)
 
 
 def alloc_weight(d_out: int, d_in: int, device, dq: str = "int8") -> NF4Weight:
@@ -197,7 +227,8 @@ def double_dequant(q: NF4Weight, out: torch.Tensor | None = None) -> torch.Tenso
 
 
 def _linear(fn_name: str, q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, inp: torch.Tensor,
-            in_dim: int, out_dim: int, out: torch.Tensor | None, workspace: torch.Tensor | None) -> torch.Tensor:
+            in_dim: int, out_dim: int, out: torch.Tensor | None, workspace: torch.Tensor | None,
+            ws_bytes_fn) -> torch.Tensor:
     dev = q.device
     r = A.shape[0]
     _need(A, torch.bfloat16, (r, q.d_in), "A", dev)
@@ -205,28 +236,32 @@ def _linear(fn_name: str, q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: flo
     if inp.dim() != 2 or inp.shape[1] != in_dim:
         raise ValueError(f"input must be [d_seq, {in_dim}]")
     d_seq = inp.shape[0]
-    _need(inp, torch.bfloat16, (d_seq, in_dim), "input", dev)
+    ld_in = _rows(inp, torch.bfloat16, (d_seq, in_dim), "input", dev)
     o = out if out is not None else torch.empty(d_seq, out_dim, dtype=torch.bfloat16, device=dev)
-    _need(o, torch.bfloat16, (d_seq, out_dim), "out", dev)
-    need = linear_workspace_bytes(q.d_out, q.d_in, d_seq, r)
+    ld_out = _rows(o, torch.bfloat16, (d_seq, out_dim), "out", dev)
+    need = ws_bytes_fn(q.d_out, q.d_in, d_seq, r)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = getattr(lib(), fn_name)(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
-                                 _dq_code(q.dq), _ptr(A), _ptr(B), r, float(s), _ptr(inp), d_seq, _ptr(o), _ptr(ws),
-                                 ws.numel() * ws.element_size(), _stream(dev))
+                                 _dq_code(q.dq), _ptr(A), _ptr(B), r, float(s), _ptr(inp), ld_in, d_seq, _ptr(o),
+                                 ld_out, _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, fn_name)
     return o
 
 
 def linear_fwd(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """qlora_linear_fwd: Y [d_seq, d_out] = X W_hat^T + s (X A^T) B^T."""
-    return _linear("qlora_linear_fwd_ex", q, A, B, s, X, q.d_in, q.d_out, out, workspace)
+    """qlora_linear_fwd: Y [d_seq, d_out] = X W_hat^T + s (X A^T) B^T. X and out may be
+    row views of wider arrays (unit column stride)."""
+    return _linear("qlora_linear_fwd_ex", q, A, B, s, X, q.d_in, q.d_out, out, workspace,
+                   linear_fwd_workspace_bytes)
 
 
 def linear_bwd_x(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, dY: torch.Tensor,
                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """qlora_linear_bwd_x: dX [d_seq, d_in] = dY W_hat + s (dY B) A."""
-    return _linear("qlora_linear_bwd_x_ex", q, A, B, s, dY, q.d_out, q.d_in, out, workspace)
+    """qlora_linear_bwd_x: dX [d_seq, d_in] = dY W_hat + s (dY B) A. dY and out may be row
+    views of wider arrays."""
+    return _linear("qlora_linear_bwd_x_ex", q, A, B, s, dY, q.d_out, q.d_in, out, workspace,
+                   linear_bwd_x_workspace_bytes)
 
 
 def lora_grads_workspace_bytes(d_out: int, d_in: int, d_seq: int, r: int) -> int:
@@ -245,15 +280,15 @@ def lora_grads(A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor, dY: 
     if X.dim() != 2 or dY.dim() != 2 or X.shape[0] != dY.shape[0]:
         raise ValueError("X [d_seq, d_in] and dY [d_seq, d_out] must share d_seq")
     d_seq = X.shape[0]
-    _need(X, torch.bfloat16, (d_seq, d_in), "X", dev)
-    _need(dY, torch.bfloat16, (d_seq, d_out), "dY", dev)
+    ldx = _rows(X, torch.bfloat16, (d_seq, d_in), "X", dev)
+    lddy = _rows(dY, torch.bfloat16, (d_seq, d_out), "dY", dev)
     ga = dA if dA is not None else torch.empty(r, d_in, dtype=torch.float32, device=dev)
     gb = dB if dB is not None else torch.empty(d_out, r, dtype=torch.float32, device=dev)
     _need(ga, torch.float32, (r, d_in), "dA", dev)
     _need(gb, torch.float32, (d_out, r), "dB", dev)
     need = lora_grads_workspace_bytes(d_out, d_in, d_seq, r)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    rc = lib().qlora_lora_grads(_ptr(A), _ptr(B), r, float(s), _ptr(X), _ptr(dY), d_out, d_in, d_seq,
+    rc = lib().qlora_lora_grads(_ptr(A), _ptr(B), r, float(s), _ptr(X), ldx, _ptr(dY), lddy, d_out, d_in, d_seq,
                                 _ptr(ga), _ptr(gb), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "qlora_lora_grads")
     return ga, gb
@@ -353,14 +388,14 @@ def qlr_linear_fwd(q: NF4Weight, Af: QFactor, Bf: QFactor, s: float, X: torch.Te
     if X.dim() != 2 or X.shape[1] != q.d_in:
         raise ValueError(f"input must be [d_seq, {q.d_in}]")
     d_seq = X.shape[0]
-    _need(X, torch.bfloat16, (d_seq, q.d_in), "input", dev)
+    ldx = _rows(X, torch.bfloat16, (d_seq, q.d_in), "input", dev)
     o = out if out is not None else torch.empty(d_seq, q.d_out, dtype=torch.bfloat16, device=dev)
-    _need(o, torch.bfloat16, (d_seq, q.d_out), "out", dev)
+    ldy = _rows(o, torch.bfloat16, (d_seq, q.d_out), "out", dev)
     need = qlr_linear_workspace_bytes(q.d_out, q.d_in, d_seq, r)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     rc = lib().qlr_linear_fwd(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out, q.d_in,
                               _dq_code(q.dq), Af.bits, _ptr(Af.codes), _ptr(Af.scale), Bf.bits, _ptr(Bf.codes),
-                              _ptr(Bf.scale), r, float(s), _ptr(X), d_seq, _ptr(o), _ptr(ws),
+                              _ptr(Bf.scale), r, float(s), _ptr(X), ldx, d_seq, _ptr(o), ldy, _ptr(ws),
                               ws.numel() * ws.element_size(), _stream(dev))
     _check(rc, "qlr_linear_fwd")
     return o

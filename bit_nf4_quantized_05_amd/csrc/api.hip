@@ -91,36 +91,53 @@ int64_t prepass_part_bytes(int64_t M, int64_t K, int r) {
     return ps.splits > 1 ? 4 * static_cast<int64_t>(ps.splits) * M * 32 * ((r + 31) / 32) : 0;
 }
 
-LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+// Workspace layout of one linear call. The forward with d_seq <= kSkinnyMaxTokens streams
+// the packed codes (GEMV or small batch) and needs only its partial sums; every other
+// call dequantises W into the workspace and runs the GEMM. Regions a call does not use
+// have size 0.
+LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r, bool bwd) {
     LinWs w{};
     w.r_pad = static_cast<int>(align_up(r, 64));
+    const bool streams = !bwd && d_seq <= qn::kSkinnyMaxTokens;
+    const bool gemm = !streams;
     int64_t off = 0;
-    w.what = off;   off += align_up(2 * d_out * d_in, 256);                        // W_hat or W_hat^T
-    w.lora = off;   off += align_up(2 * d_seq * w.r_pad, 256);                     // s(XA^T) or s(dY B)
-    w.adapt = off;  off += align_up(2 * (d_out > d_in ? d_out : d_in) * w.r_pad, 256);  // B padded or A^T padded
-    w.adapt2 = off; off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);     // B^T (unless the pre-pass reads B)
-    w.t = off;      off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);  // GEMV: partial A x
-    w.part = off;                                                                // small batch: K-split partials
-    if (d_seq >= 2 && d_seq <= qn::kSkinnyMaxTokens)
+    w.what = off;   if (gemm) off += align_up(2 * d_out * d_in, 256);                        // W_hat or W_hat^T
+    w.lora = off;   if (gemm) off += align_up(2 * d_seq * w.r_pad, 256);                     // s(XA^T) or s(dY B)
+    w.adapt = off;  if (gemm) off += align_up(2 * (bwd ? d_in : d_out) * w.r_pad, 256);      // B padded or A^T padded
+    w.adapt2 = off;                                                                          // B^T (unless the pre-pass reads B)
+    if (bwd && !qn::prepass_takes_kmajor(r)) off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);
+    w.t = off;                                                                               // GEMV: partial A x
+    if (streams && qn::gemv_takes_tokens(d_seq, d_in, r)) off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);
+    w.part = off;                                                                            // small batch: K-split partials
+    if (streams && !qn::gemv_takes_tokens(d_seq, d_in, r))
         off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in, d_seq)) * d_seq * (d_out + w.r_pad), 256);
-    w.gpart = off;                                                               // GEMM K-split partials (few tiles)
-    off += align_up(4 * std::max(d_seq > qn::kSkinnyMaxTokens ? qn::gemm_split_part_floats(d_seq, d_out, d_in) : 0,
-                                 qn::gemm_split_part_floats(d_seq, d_in, d_out)), 256);
-    w.ppart = off;                                                               // pre-pass K-split partials
-    off += align_up(std::max(d_seq > qn::kSkinnyMaxTokens ? prepass_part_bytes(d_seq, d_in, r) : 0,
-                             prepass_part_bytes(d_seq, d_out, r)), 256);
+    w.gpart = off;                                                                           // GEMM K-split partials (few tiles)
+    if (gemm) off += align_up(4 * (bwd ? qn::gemm_split_part_floats(d_seq, d_in, d_out)
+                                       : qn::gemm_split_part_floats(d_seq, d_out, d_in)), 256);
+    w.ppart = off;                                                                           // pre-pass K-split partials
+    if (gemm) off += align_up(bwd ? prepass_part_bytes(d_seq, d_out, r) : prepass_part_bytes(d_seq, d_in, r), 256);
     w.bytes = off;
     return w;
 }
 
+bool linear_sizes_ok(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    return d_out >= 1 && d_in >= 1 && d_seq >= 1 && r >= 1 && r <= 256 && d_out <= (int64_t{1} << 40) / d_in &&
+           d_seq <= INT32_MAX;
+}
+
+// Checks of a linear call; `in` [d_seq, in_cols] with row stride ldi, `out` [d_seq, out_cols]
+// with row stride ldo (in elements).
 int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean, int dq,
                  int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r,
-                 const uint16_t* in, int64_t d_seq, uint16_t* out, void* ws, int64_t ws_bytes,
-                 LinWs* lw, qn::BlockConsts* bc) {
+                 const uint16_t* in, int64_t ldi, int64_t d_seq, uint16_t* out, int64_t ldo, bool bwd, void* ws,
+                 int64_t ws_bytes, LinWs* lw, qn::BlockConsts* bc) {
     if (int rc = make_consts(dq, codes, qconst, qscale, qmean, bc)) return rc;
     if (!A || !B || !in || !out || !ws) return fail(-1, "null pointer argument");
     if (d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1");
     if (r < 1 || r > 256) return fail(-1, "r must be in [1, 256]");
+    const int64_t in_cols = bwd ? d_out : d_in, out_cols = bwd ? d_in : d_out;
+    if (ldi < in_cols || ldo < out_cols) return fail(-1, "a leading dimension is smaller than its row");
+    if (ldi % 8 != 0 || ldo % 8 != 0) return fail(-1, "leading dimensions must be multiples of 8 elements");
     if (!aligned(codes, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(in, 16) ||
         !aligned(out, 16) || !aligned(ws, 256))
         return fail(-1, "misaligned pointer (16 B for arrays, 256 B for the workspace)");
@@ -130,9 +147,9 @@ int check_linear(const uint8_t* codes, const int8_t* qconst, const float* qscale
     if (!nf4_counts(d_out, d_in, &n, &n_b, &n_g)) return fail(-2, "weight too large");
     // the GEMM addresses each operand with 32-bit byte offsets
     const int64_t kMaxBytes = int64_t{1} << 32;
-    if (2 * n >= kMaxBytes || 2 * d_seq * (d_out > d_in ? d_out : d_in) >= kMaxBytes)
+    if (2 * n >= kMaxBytes || 2 * d_seq * std::max(ldi, ldo) >= kMaxBytes)
         return fail(-2, "an operand reaches 4 GiB");
-    *lw = linear_ws(d_out, d_in, d_seq, r);
+    *lw = linear_ws(d_out, d_in, d_seq, r, bwd);
     if (ws_bytes < lw->bytes) return fail(-3, "workspace too small");
     return 0;
 }
@@ -189,11 +206,11 @@ namespace {
 // and d_in <= 4096) streams the codes (GEMV), d_seq <= 64 runs the small-batch kernel,
 // otherwise dequantise + pre-pass + GEMM.
 int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_out, int64_t d_in,
-                   const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t d_seq,
-                   uint16_t* Y, char* ws, const LinWs& lw, hipStream_t st) {
+                   const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t ldx,
+                   int64_t d_seq, uint16_t* Y, int64_t ldy, char* ws, const LinWs& lw, hipStream_t st) {
     hipError_t e;
     if (qn::gemv_takes_tokens(d_seq, d_in, r)) {
-        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, d_seq, Y,
+        e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy,
                                 reinterpret_cast<float*>(ws + lw.t), st);
         if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");
         return 0;
@@ -202,8 +219,8 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
         // few tokens: the codes streamed once, A x in the same launch
         float* part = reinterpret_cast<float*>(ws + lw.part);
         float* part_a = part + static_cast<int64_t>(qn::skinny_splits(d_in, d_seq)) * d_seq * d_out;
-        if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, d_seq, A, B, r, lw.r_pad, s,
-                                       part, part_a, Y, st)) != hipSuccess)
+        if ((e = qn::launch_skinny_nf4(codes, bc, d_out, d_in, X, ldx, d_seq, A, B, r, lw.r_pad, s,
+                                       part, part_a, Y, ldy, st)) != hipSuccess)
             return hip_fail(e, "qlora_linear_fwd (small batch)");
         return 0;
     }
@@ -212,12 +229,12 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
     uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
     const bool pad = r != lw.r_pad;
     // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
-    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, d_in, d_seq, d_in,
+    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, ldx, d_seq, d_in,
                                  A, d_in, false, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r,
                                  reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
-    if ((e = qn::launch_gemm_nt(X, d_in, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
-                                d_out, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
+    if ((e = qn::launch_gemm_nt(X, ldx, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
+                                ldy, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (gemm)");
     return 0;
 }
@@ -361,39 +378,49 @@ int nf4_double_dequant(const uint8_t* codes, const int8_t* qconst, const float* 
 }
 
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
-    if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
-    return linear_ws(d_out, d_in, d_seq, r).bytes;
+    if (!linear_sizes_ok(d_out, d_in, d_seq, r)) return 0;
+    return std::max(linear_ws(d_out, d_in, d_seq, r, false).bytes, linear_ws(d_out, d_in, d_seq, r, true).bytes);
+}
+
+int64_t qlora_linear_fwd_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    if (!linear_sizes_ok(d_out, d_in, d_seq, r)) return 0;
+    return linear_ws(d_out, d_in, d_seq, r, false).bytes;
+}
+
+int64_t qlora_linear_bwd_x_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
+    if (!linear_sizes_ok(d_out, d_in, d_seq, r)) return 0;
+    return linear_ws(d_out, d_in, d_seq, r, true).bytes;
 }
 
 int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
                         int64_t d_out, int64_t d_in, int dq, const uint16_t* A, const uint16_t* B, int r, float s,
-                        const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
+                        const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy, void* workspace,
                         int64_t workspace_bytes, void* stream) {
     LinWs lw;
     qn::BlockConsts bc;
-    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, X, d_seq, Y, workspace,
-                          workspace_bytes, &lw, &bc);
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, X, ldx, d_seq, Y, ldy, false,
+                          workspace, workspace_bytes, &lw, &bc);
     if (rc) return rc;
-    return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, d_seq, Y, static_cast<char*>(workspace), lw,
-                          static_cast<hipStream_t>(stream));
+    return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy, static_cast<char*>(workspace),
+                          lw, static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
                      int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
-                     const uint16_t* X, int64_t d_seq, uint16_t* Y, void* workspace,
+                     const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy, void* workspace,
                      int64_t workspace_bytes, void* stream) {
-    return qlora_linear_fwd_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, X, d_seq, Y,
-                               workspace, workspace_bytes, stream);
+    return qlora_linear_fwd_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, X, ldx, d_seq, Y,
+                               ldy, workspace, workspace_bytes, stream);
 }
 
 int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
                           int64_t d_out, int64_t d_in, int dq, const uint16_t* A, const uint16_t* B, int r,
-                          float s, const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
-                          int64_t workspace_bytes, void* stream) {
+                          float s, const uint16_t* dY, int64_t lddy, int64_t d_seq, uint16_t* dX, int64_t lddx,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
     LinWs lw;
     qn::BlockConsts bc;
-    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, dY, d_seq, dX, workspace,
-                          workspace_bytes, &lw, &bc);
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, dY, lddy, d_seq, dX, lddx, true,
+                          workspace, workspace_bytes, &lw, &bc);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
@@ -407,22 +434,22 @@ int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const floa
     if (!km && (e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (B^T)");
     // dequant W_hat^T + U = s (dY B) + A^T padded to r_pad columns, in one launch
-    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, true, whatT, dY, d_out, d_seq, d_out,
+    if ((e = qn::launch_prologue(codes, bc, d_out, d_in, true, whatT, dY, lddy, d_seq, d_out,
                                  km ? B : bt, d_out, km, r, s, u, lw.r_pad, 2, A, atpad, r, d_in,
                                  reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (prologue)");
-    if ((e = qn::launch_gemm_nt(dY, d_out, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
-                                d_in, d_seq, d_in, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
+    if ((e = qn::launch_gemm_nt(dY, lddy, whatT, d_out, d_out, u, lw.r_pad, atpad, lw.r_pad, lw.r_pad, dX,
+                                lddx, d_seq, d_in, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_bwd_x (gemm)");
     return 0;
 }
 
 int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
                        int64_t d_out, int64_t d_in, const uint16_t* A, const uint16_t* B, int r, float s,
-                       const uint16_t* dY, int64_t d_seq, uint16_t* dX, void* workspace,
+                       const uint16_t* dY, int64_t lddy, int64_t d_seq, uint16_t* dX, int64_t lddx, void* workspace,
                        int64_t workspace_bytes, void* stream) {
-    return qlora_linear_bwd_x_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, dY, d_seq, dX,
-                                 workspace, workspace_bytes, stream);
+    return qlora_linear_bwd_x_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, dY, lddy, d_seq,
+                                 dX, lddx, workspace, workspace_bytes, stream);
 }
 
 // ---- quantised low-rank factors (W ~ Q + L R) --------------------------------
@@ -447,29 +474,30 @@ int int8_dequant(const int8_t* q, const float* absmax, int64_t rows, int64_t col
 }
 
 int64_t qlr_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
-    if (d_out < 1 || d_in < 1 || d_seq < 1 || r < 1 || r > 256) return 0;
-    return linear_ws(d_out, d_in, d_seq, r).bytes + align_up(2 * r * d_in, 256) + align_up(2 * d_out * r, 256);
+    if (!linear_sizes_ok(d_out, d_in, d_seq, r)) return 0;
+    return linear_ws(d_out, d_in, d_seq, r, false).bytes + align_up(2 * r * d_in, 256) + align_up(2 * d_out * r, 256);
 }
 
 int qlr_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
                    int64_t d_out, int64_t d_in, int dq, int a_bits, const void* a_codes, const float* a_scale,
                    int b_bits, const void* b_codes, const float* b_scale, int r, float s, const uint16_t* X,
-                   int64_t d_seq, uint16_t* Y, void* workspace, int64_t workspace_bytes, void* stream) {
+                   int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
     if ((a_bits != 4 && a_bits != 8) || (b_bits != 4 && b_bits != 8)) return fail(-1, "factor bits must be 4 or 8");
     if (!a_codes || !a_scale || !b_codes || !b_scale) return fail(-1, "null pointer argument");
     if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4))
         return fail(-1, "misaligned pointer");
-    if (r < 1 || r > 256 || d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1, r <= 256");
-    // the dequantised factors sit after the linear workspace (A [r, d_in], then B [d_out, r])
-    const LinWs lw0 = linear_ws(d_out, d_in, d_seq, r);
+    if (!linear_sizes_ok(d_out, d_in, d_seq, r)) return fail(-1, "sizes must be >= 1, r <= 256");
+    // the dequantised factors sit after the forward's workspace (A [r, d_in], then B [d_out, r])
+    const LinWs lw0 = linear_ws(d_out, d_in, d_seq, r, false);
     if (workspace_bytes < qlr_linear_workspace_bytes(d_out, d_in, d_seq, r)) return fail(-3, "workspace too small");
     char* ws = static_cast<char*>(workspace);
     uint16_t* a_hat = reinterpret_cast<uint16_t*>(ws + lw0.bytes);
     uint16_t* b_hat = reinterpret_cast<uint16_t*>(ws + lw0.bytes + align_up(2 * r * d_in, 256));
     LinWs lw;
     qn::BlockConsts bc;
-    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, a_hat, b_hat, r, X, d_seq, Y, workspace,
-                          workspace_bytes, &lw, &bc);
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, a_hat, b_hat, r, X, ldx, d_seq, Y, ldy,
+                          false, workspace, workspace_bytes, &lw, &bc);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
@@ -487,7 +515,7 @@ int qlr_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qsca
         }
         if (e != hipSuccess) return hip_fail(e, "qlr_linear_fwd (factors)");
     }
-    return linear_fwd_run(codes, bc, d_out, d_in, a_hat, b_hat, r, s, X, d_seq, Y, ws, lw, st);
+    return linear_fwd_run(codes, bc, d_out, d_in, a_hat, b_hat, r, s, X, ldx, d_seq, Y, ldy, ws, lw, st);
 }
 
 // ---- adapter gradients ----------------------------------------------------
@@ -497,18 +525,20 @@ int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_
     return grad_ws(d_out, d_in, d_seq, r).bytes;
 }
 
-int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X,
-                     const uint16_t* dY, int64_t d_out, int64_t d_in, int64_t d_seq, float* dA, float* dB,
-                     void* workspace, int64_t workspace_bytes, void* stream) {
+int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t ldx,
+                     const uint16_t* dY, int64_t lddy, int64_t d_out, int64_t d_in, int64_t d_seq, float* dA,
+                     float* dB, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!A || !B || !X || !dY || !dA || !dB || !workspace) return fail(-1, "null pointer argument");
     if (d_out < 1 || d_in < 1 || d_seq < 1) return fail(-1, "sizes must be >= 1");
     if (r < 1 || r > 256) return fail(-1, "r must be in [1, 256]");
+    if (ldx < d_in || lddy < d_out) return fail(-1, "a leading dimension is smaller than its row");
+    if (ldx % 8 != 0 || lddy % 8 != 0) return fail(-1, "leading dimensions must be multiples of 8 elements");
     if (!aligned(A, 16) || !aligned(B, 16) || !aligned(X, 16) || !aligned(dY, 16) || !aligned(dA, 16) ||
         !aligned(dB, 16) || !aligned(workspace, 256))
         return fail(-1, "misaligned pointer (16 B for arrays, 256 B for the workspace)");
     if (d_in % 64 != 0 || d_out % 64 != 0) return fail(-2, "d_in and d_out must be multiples of 64");
     if (d_in > INT32_MAX || d_out > INT32_MAX || d_seq > INT32_MAX) return fail(-2, "dimension too large");
-    if (2 * d_seq * (d_out > d_in ? d_out : d_in) >= (int64_t{1} << 32)) return fail(-2, "an operand reaches 4 GiB");
+    if (2 * d_seq * std::max(ldx, lddy) >= (int64_t{1} << 32)) return fail(-2, "an operand reaches 4 GiB");
     const GradWs gw = grad_ws(d_out, d_in, d_seq, r);
     if (workspace_bytes < gw.bytes) return fail(-3, "workspace too small");
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -523,12 +553,13 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s, const
     const bool km = qn::prepass_takes_kmajor(r);
     if (!km && (e = qn::launch_transpose_pad(B, d_out, r, bt, d_out, st)) != hipSuccess)
         return hip_fail(e, "qlora_lora_grads (B^T)");
-    if ((e = qn::launch_prepass_pair(X, d_in, d_in, A, d_in, tp, reinterpret_cast<float*>(ws + gw.ppart),
-                                     dY, d_out, d_out, km ? B : bt, d_out, km, up,
+    if ((e = qn::launch_prepass_pair(X, ldx, d_in, A, d_in, tp, reinterpret_cast<float*>(ws + gw.ppart),
+                                     dY, lddy, d_out, km ? B : bt, d_out, km, up,
                                      reinterpret_cast<float*>(ws + gw.ppart1), d_seq, r, s, gw.r_pad, st)) !=
         hipSuccess)
         return hip_fail(e, "qlora_lora_grads (X A^T, dY B)");
-    if ((e = qn::launch_lora_grads(X, dY, tp, up, d_out, d_in, d_seq, r, gw.r_pad, part, dA, dB, st)) != hipSuccess)
+    if ((e = qn::launch_lora_grads(X, ldx, dY, lddy, tp, up, d_out, d_in, d_seq, r, gw.r_pad, part, dA, dB, st)) !=
+        hipSuccess)
         return hip_fail(e, "qlora_lora_grads (reduction)");
     return 0;
 }

@@ -126,9 +126,9 @@ __device__ __forceinline__ int gv_xpos(int c) { return (c & ~3) | ((c & 3) ^ ((c
 template <int T, bool kAx>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
-                     int d_out, int d_in, const uint16_t* __restrict__ x, int ntok,
+                     int d_out, int d_in, const uint16_t* __restrict__ x, int ldx, int ntok,
                      const uint16_t* __restrict__ B, int r, float s, const float* __restrict__ part,
-                     int nparts, const uint16_t* __restrict__ A, uint16_t* __restrict__ y, NF4Tables tab) {
+                     int nparts, const uint16_t* __restrict__ A, uint16_t* __restrict__ y, int ldy, NF4Tables tab) {
     static_assert(T == 1 || kAx, "several tokens only in the one-launch form");
     __shared__ uint4 lut4[256 * kLutCopies / 4];
     __shared__ uint4 xs[2][T][kGvSeg / 8];
@@ -155,7 +155,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
             const int col = S * kGvSeg + 8 * tid;
 #pragma unroll
             for (int k = 0; k < T; ++k)
-                g[k] = x4[(static_cast<int64_t>(min(k, ntok - 1)) * d_in + min(col, d_in - 8)) / 8];
+                g[k] = x4[(static_cast<int64_t>(min(k, ntok - 1)) * ldx + min(col, d_in - 8)) / 8];
         }
     };
     auto stage_store = [&](const uint4 (&g)[T], int S) {
@@ -347,7 +347,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
         for (int j = lane; j < r; j += 64) v += bf16_to_f32(brow[j]) * s_t[16 * k + j];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-        if (lane == 0 && row0 + wave < d_out && k < ntok) y[static_cast<int64_t>(k) * d_out + row0 + wave] = bf16_bits(v);
+        if (lane == 0 && row0 + wave < d_out && k < ntok) y[static_cast<int64_t>(k) * ldy + row0 + wave] = bf16_bits(v);
     }
 }
 
@@ -359,7 +359,8 @@ bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r) {
 
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
-                           const uint16_t* x, int64_t d_seq, uint16_t* y, float* ws_part, hipStream_t st) {
+                           const uint16_t* x, int64_t ldx, int64_t d_seq, uint16_t* y, int64_t ldy, float* ws_part,
+                           hipStream_t st) {
     if (!gemv_takes_tokens(d_seq, d_in, r)) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
     const int nt = static_cast<int>(d_seq);
@@ -367,8 +368,8 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
         // one launch: every workgroup forms s A x from A (r x d_in <= 16 x 4096 bf16)
 #define QN_GV_LAUNCH(TT) \
         QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<TT, true>), grid, dim3(64 * kGvWaves), 0, st, \
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, nt, \
-                  B, r, s, ws_part, 0, A, y, tables())
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, \
+                  static_cast<int>(ldx), nt, B, r, s, ws_part, 0, A, y, static_cast<int>(ldy), tables())
         if (nt == 1) QN_GV_LAUNCH(1);
         else if (nt == 2) QN_GV_LAUNCH(2);
         else QN_GV_LAUNCH(3);
@@ -383,8 +384,8 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
     QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<1, false>), grid, dim3(64 * kGvWaves), 0, st,
-              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, 1, B,
-              r, s, ws_part, nparts, A, y, tables());
+              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x,
+              static_cast<int>(ldx), 1, B, r, s, ws_part, nparts, A, y, static_cast<int>(ldy), tables());
     return hipGetLastError();
 }
 

@@ -116,25 +116,27 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
 // ---- gemv.hip ----
 // y[t, o] = sum_i w_hat[o,i] x[t, i] + s * sum_k B[o,k] (A x_t)[k], streaming the packed
 // codes, for d_seq = 1, or for 2 <= d_seq <= kGemvMaxTokens tokens when r <= 16 and
-// d_in <= 4096 (gemv_takes_tokens); ws_part holds at most d_in/64 x r floats of partial
-// A x sums (d_seq = 1 only).
+// d_in <= 4096 (gemv_takes_tokens); x rows at stride ldx, y rows at stride ldy (elements,
+// multiples of 8); ws_part holds at most d_in/64 x r floats of partial A x sums (d_seq = 1
+// only).
 constexpr int kGemvMaxTokens = 3;
 bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r);
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
-                           const uint16_t* x, int64_t d_seq, uint16_t* y, float* ws_part, hipStream_t st);
+                           const uint16_t* x, int64_t ldx, int64_t d_seq, uint16_t* y, int64_t ldy, float* ws_part,
+                           hipStream_t st);
 
 // ---- skinny.hip ----
 // Small-batch forward, 2 <= d_seq <= 64: Y = dequant(W) X + bf16(s X A^T) B^T from the
-// packed codes, A x formed in the same launch. part must hold skinny_splits(d_in, d_seq) *
-// d_seq * d_out floats, part_a skinny_splits(d_in, d_seq) * d_seq * r_pad. d_out % 64 == 0,
-// d_in % 64 == 0.
+// packed codes, A x formed in the same launch. X rows at stride ldx, Y rows at stride ldy
+// (elements, multiples of 8). part must hold skinny_splits(d_in, d_seq) * d_seq * d_out
+// floats, part_a skinny_splits(d_in, d_seq) * d_seq * r_pad. d_out % 64 == 0, d_in % 64 == 0.
 constexpr int kSkinnyMaxTokens = 64;
 int skinny_splits(int64_t d_in, int64_t d_seq);
 hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
-                             const uint16_t* X, int64_t d_seq,
+                             const uint16_t* X, int64_t ldx, int64_t d_seq,
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
-                             float* part_a, uint16_t* Y, hipStream_t st);
+                             float* part_a, uint16_t* Y, int64_t ldy, hipStream_t st);
 
 // ---- factors.hip ----
 // Symmetric absmax INT8 per block of 64 flat elements of W [n] (padded with +0.0):
@@ -147,9 +149,11 @@ hipError_t launch_int8_dequant(const int8_t* q, const float* absmax, int64_t n, 
 // gradients, then their fixed-order sum:
 //   dB [d_out, r] = dY^T T'   (P = dY, T = T' = bf16(s X A^T))
 //   dA [r, d_in]  = U'^T X     (P = X,  T = U' = bf16(s dY B))
-// T' and U' are [d_seq, r_pad] bf16. part must hold lora_grads_partials(...) floats.
+// T' and U' are [d_seq, r_pad] bf16; X and dY rows at strides ldx, lddy (elements,
+// multiples of 8). part must hold lora_grads_partials(...) floats.
 int64_t lora_grads_partials(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
-hipError_t launch_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* Tp, const uint16_t* Up,
+hipError_t launch_lora_grads(const uint16_t* X, int64_t ldx, const uint16_t* dY, int64_t lddy, const uint16_t* Tp,
+                             const uint16_t* Up,
                              int64_t d_out, int64_t d_in, int64_t d_seq, int r, int r_pad,
                              float* part, float* dA, float* dB, hipStream_t st);
 

@@ -40,6 +40,7 @@ constexpr int kGSlices = 512;     // target workgroups per gradient
 
 struct GradJob {
     const uint16_t* P; int64_t N;    // [d_seq, N]
+    int64_t ldp;                     // row stride of P (elements)
     const uint16_t* T;               // [d_seq, r_pad]
     float* part;                     // [S][N][r]
     int tiles, S, L;                 // column tiles, token slices, slice length (multiple of kGK)
@@ -69,7 +70,7 @@ __device__ __forceinline__ void grad_issue(GradTile& t, const GradJob& jb, const
         const int row = 4 * (2 * wave + q) + (lane >> 4);
         const int64_t mg = min(m + row, g.d_seq - 1);
         const int64_t ng = min(n0 + 8 * ((lane & 15) ^ swz(row)), jb.N - 8);
-        load_lds16(jb.P + mg * jb.N + ng, &t.P[(2 * wave + q) * 64]);
+        load_lds16(jb.P + mg * jb.ldp + ng, &t.P[(2 * wave + q) * 64]);
     }
     const int row = 8 * wave + (lane >> 3);
     const int64_t mg = min(m + row, g.d_seq - 1);
@@ -233,7 +234,8 @@ int64_t lora_grads_partials(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
     return nb + static_cast<int64_t>(S) * d_in * r;
 }
 
-hipError_t launch_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* Tp, const uint16_t* Up,
+hipError_t launch_lora_grads(const uint16_t* X, int64_t ldx, const uint16_t* dY, int64_t lddy, const uint16_t* Tp,
+                             const uint16_t* Up,
                              int64_t d_out, int64_t d_in, int64_t d_seq, int r, int r_pad,
                              float* part, float* dA, float* dB, hipStream_t st) {
     GradArgs g;
@@ -243,9 +245,9 @@ hipError_t launch_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16
     g.jchunks = jchunks_of(r);
     GradJob& jB = g.job[0];
     GradJob& jA = g.job[1];
-    jB.P = dY; jB.N = d_out; jB.T = Tp; jB.part = part;
+    jB.P = dY; jB.N = d_out; jB.ldp = lddy; jB.T = Tp; jB.part = part;
     slicing(d_out, d_seq, g.jchunks, &jB.tiles, &jB.S, &jB.L);
-    jA.P = X; jA.N = d_in; jA.T = Up; jA.part = part + static_cast<int64_t>(jB.S) * d_out * r;
+    jA.P = X; jA.N = d_in; jA.ldp = ldx; jA.T = Up; jA.part = part + static_cast<int64_t>(jB.S) * d_out * r;
     slicing(d_in, d_seq, g.jchunks, &jA.tiles, &jA.S, &jA.L);
     const dim3 grid(static_cast<unsigned>((jB.tiles * jB.S + jA.tiles * jA.S) * g.jchunks));
     if (r <= 32) {

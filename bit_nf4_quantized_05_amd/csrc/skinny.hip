@@ -41,6 +41,7 @@ constexpr int kSkSplitTokens = 32;  // above this many tokens, at most 4 K-split
 struct SkArgs {
     const uint8_t* codes; BlockConsts bc;
     int d_out, d_in, d_seq, splits, r, r_pad;
+    int64_t ldx;                    // row stride of X (elements)
     const uint16_t* X;              // [d_seq, d_in]
     const uint16_t* A;              // [r, d_in]
     float* part;                    // [splits][d_seq][d_out]
@@ -112,7 +113,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
         for (int j = 0; j < kXRows; ++j) {
             const int tok = wv + 4 * j;
             const int c = min(lane ^ (tok & 15), nbk * 8 - 1);
-            load_lds16(x4 + (static_cast<int64_t>(min(tok, a.d_seq - 1)) * a.d_in + b0 * 64) / 8 + c, xs + tok * 64);
+            load_lds16(x4 + (static_cast<int64_t>(min(tok, a.d_seq - 1)) * a.ldx + b0 * 64) / 8 + c, xs + tok * 64);
         }
         __builtin_amdgcn_sched_barrier(0);         // the row loads go out before the loads that follow
     };
@@ -216,7 +217,8 @@ constexpr int kRdRows = 16;
 
 __global__ __launch_bounds__(256)
 void skinny_reduce(const float* __restrict__ part, const float* __restrict__ part_a, int splits, float s,
-                   int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y) {
+                   int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y,
+                   int64_t ldy) {
     constexpr int kJ = 64, kP = kJ + 1;
     constexpr int kPairs = kSkTok * kRdRows / 256;   // pairs per thread at most
     constexpr int kBPer = kRdRows * kJ / 256;        // B entries per thread and chunk
@@ -290,7 +292,7 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
 #pragma unroll
     for (int q = 0; q < kPairs; ++q) {
         const int e = tid + 256 * q;
-        if (e < npairs) Y[static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows] = bf16_bits(acc[q]);
+        if (e < npairs) Y[static_cast<int64_t>(e / kRdRows) * ldy + o0 + e % kRdRows] = bf16_bits(acc[q]);
     }
 }
 
@@ -305,15 +307,15 @@ int skinny_splits(int64_t d_in, int64_t d_seq) {
 }
 
 hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
-                             const uint16_t* X, int64_t d_seq,
+                             const uint16_t* X, int64_t ldx, int64_t d_seq,
                              const uint16_t* A, const uint16_t* B, int r, int r_pad, float s, float* part,
-                             float* part_a, uint16_t* Y, hipStream_t st) {
+                             float* part_a, uint16_t* Y, int64_t ldy, hipStream_t st) {
     SkArgs a;
     a.codes = codes; a.bc = bc;
     a.d_out = static_cast<int>(d_out); a.d_in = static_cast<int>(d_in); a.d_seq = static_cast<int>(d_seq);
     a.splits = skinny_splits(d_in, d_seq);
     a.r = r; a.r_pad = r_pad;
-    a.X = X; a.A = A; a.part = part; a.part_a = part_a;
+    a.X = X; a.ldx = ldx; a.A = A; a.part = part; a.part_a = part_a;
     const int blocks = static_cast<int>(d_out / kSkRows) + (r + kSkRows - 1) / kSkRows;
     const dim3 grid(static_cast<unsigned>(blocks * a.splits));
     const NF4Tables& tab = tables();
@@ -325,7 +327,7 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
         default: return hipErrorInvalidValue;
     }
     QN_LAUNCH("skinny_reduce", st, skinny_reduce, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256), 0, st,
-              part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y);
+              part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y, ldy);
     return hipGetLastError();
 }
 

@@ -15,7 +15,11 @@
  *  - W0 is d_out x d_in, row-major (d_in contiguous), float32 on input.
  *  - Activations follow the pages' x in R^{d_in x d_seq} [P1 LoRA], stored as
  *    a torch-style [d_seq, d_in] row-major array: each token's d_in features
- *    are contiguous. Y and dY are [d_seq, d_out], dX is [d_seq, d_in].
+ *    are contiguous. Y and dY are [d_seq, d_out], dX is [d_seq, d_in]. Token t of
+ *    an activation starts ld elements after token t-1 (ldx, ldy, lddy, lddx): ld
+ *    is at least the row length (d_in or d_out) and a multiple of 8 (16-byte
+ *    rows); a larger ld reads or writes rows of a wider array in place. Elements
+ *    between the end of a row and the next row are neither read nor written.
  *  - A is r x d_in and B is d_out x r, both row-major [P1 LoRA shapes].
  *  - bf16 values are passed as uint16_t bit patterns.
  *  - Every pointer argument is a DEVICE pointer (memory of the current HIP
@@ -152,18 +156,26 @@ int nf4_double_dequant_ex(const uint8_t* codes, const int8_t* qconst, const floa
                           const float* qmean, int64_t d_out, int64_t d_in, int dq,
                           uint16_t* W_bf16, void* stream);
 
-/* Workspace bytes qlora_linear_fwd / qlora_linear_bwd_x need (0 on bad sizes). */
+/* Workspace bytes of qlora_linear_fwd(_ex) and of qlora_linear_bwd_x(_ex) for the given
+ * sizes (0 on bad sizes). The forward with d_seq <= 64 streams the packed codes and needs
+ * only partial sums (16 KB at d_seq = 1 with r = 16); every other call dequantises W
+ * into the workspace (2 bytes per weight). qlora_linear_workspace_bytes is the larger
+ * of the two, enough for either call. */
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+int64_t qlora_linear_fwd_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
+int64_t qlora_linear_bwd_x_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
 
 /*
  * qlora_linear_fwd - Y = dequant(W) X + s B (A X) with BF16 operands.
  *   [P1 LoRA: y = W0 x + s B(A x), sequence input x in R^{d_in x d_seq};
  *    P1 1. NF4: 4-bit -> dequant -> BF16 -> GEMM; P2 card 1]
- *   A [r, d_in], B [d_out, r], X [d_seq, d_in] bf16; Y [d_seq, d_out] bf16 output
- *   (float32 accumulation, one final round to nearest even).
- *   s is the LoRA scale (float32).
+ *   A [r, d_in], B [d_out, r], X [d_seq, d_in] bf16 with row stride ldx; Y [d_seq, d_out]
+ *   bf16 output with row stride ldy (float32 accumulation, one final round to nearest
+ *   even). s is the LoRA scale (float32). The workspace must hold
+ *   qlora_linear_fwd_workspace_bytes(d_out, d_in, d_seq, r) bytes.
  * Requires d_in % 64 == 0 and d_out % 64 == 0 (-2 otherwise), 1 <= r <= 256,
- * d_seq >= 1. d_seq == 1 (and d_seq = 2, 3 when r <= 16 and d_in <= 4096) runs a
+ * d_seq >= 1, ldx >= d_in and ldy >= d_out, both multiples of 8 (-1 otherwise).
+ * d_seq == 1 (and d_seq = 2, 3 when r <= 16 and d_in <= 4096) runs a
  * streaming GEMV over the packed codes; other d_seq <= 64 stream the codes once into
  * small MFMA tiles; larger d_seq dequantises W to bf16 in the workspace and runs the
  * MFMA GEMM with the LoRA branch as extra K-steps.
@@ -171,34 +183,35 @@ int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq,
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                      const float* qmean, int64_t d_out, int64_t d_in,
                      const uint16_t* A, const uint16_t* B, int r, float s,
-                     const uint16_t* X, int64_t d_seq, uint16_t* Y,
+                     const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /* qlora_linear_fwd for a weight quantised in format dq. */
 int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                         const float* qmean, int64_t d_out, int64_t d_in, int dq,
                         const uint16_t* A, const uint16_t* B, int r, float s,
-                        const uint16_t* X, int64_t d_seq, uint16_t* Y,
+                        const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy,
                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * qlora_linear_bwd_x - input gradient dX = dequant(W)^T dY + s A^T (B^T dY).
  *   [P2 card 1: gradients flow through the dequantised weights, only A and B
  *    are trained; the formula is the adjoint of the forward above]
- *   dY [d_seq, d_out] bf16; dX [d_seq, d_in] bf16 output. Same shape rules as
- *   qlora_linear_fwd.
+ *   dY [d_seq, d_out] bf16 with row stride lddy >= d_out; dX [d_seq, d_in] bf16 output
+ *   with row stride lddx >= d_in. Same shape rules as qlora_linear_fwd; the workspace
+ *   must hold qlora_linear_bwd_x_workspace_bytes(d_out, d_in, d_seq, r) bytes.
  */
 int qlora_linear_bwd_x(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                        const float* qmean, int64_t d_out, int64_t d_in,
                        const uint16_t* A, const uint16_t* B, int r, float s,
-                       const uint16_t* dY, int64_t d_seq, uint16_t* dX,
+                       const uint16_t* dY, int64_t lddy, int64_t d_seq, uint16_t* dX, int64_t lddx,
                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /* qlora_linear_bwd_x for a weight quantised in format dq. */
 int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                           const float* qmean, int64_t d_out, int64_t d_in, int dq,
                           const uint16_t* A, const uint16_t* B, int r, float s,
-                          const uint16_t* dY, int64_t d_seq, uint16_t* dX,
+                          const uint16_t* dY, int64_t lddy, int64_t d_seq, uint16_t* dX, int64_t lddx,
                           void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
@@ -242,8 +255,8 @@ int qlr_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qsca
                    const float* qmean, int64_t d_out, int64_t d_in, int dq,
                    int a_bits, const void* a_codes, const float* a_scale,
                    int b_bits, const void* b_codes, const float* b_scale,
-                   int r, float s, const uint16_t* X, int64_t d_seq, uint16_t* Y,
-                   void* workspace, int64_t workspace_bytes, void* stream);
+                   int r, float s, const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y,
+                   int64_t ldy, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes qlora_lora_grads needs (0 on bad sizes). */
 int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
@@ -259,14 +272,15 @@ int64_t qlora_lora_grads_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_
  *   calls' GEMMs consume the same products, rounded to bf16 once or once per K-slice
  *   of their pre-pass), float32 accumulation, float32 outputs (overwritten). The
  *   quantised weight is not needed.
- *   A [r, d_in], B [d_out, r], X [d_seq, d_in], dY [d_seq, d_out] bf16 (device);
- *   dA, dB float32 (device).
+ *   A [r, d_in], B [d_out, r], X [d_seq, d_in] (row stride ldx >= d_in), dY [d_seq, d_out]
+ *   (row stride lddy >= d_out) bf16 (device), strides multiples of 8; dA, dB float32
+ *   (device).
  *   Same shape rules as qlora_linear_fwd (d_in, d_out multiples of 64, 1 <= r <= 256,
  *   d_seq >= 1). The result is deterministic (fixed summation order).
  */
 int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s,
-                     const uint16_t* X, const uint16_t* dY, int64_t d_out, int64_t d_in,
-                     int64_t d_seq, float* dA, float* dB,
+                     const uint16_t* X, int64_t ldx, const uint16_t* dY, int64_t lddy,
+                     int64_t d_out, int64_t d_in, int64_t d_seq, float* dA, float* dB,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
 /*

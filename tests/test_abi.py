@@ -39,16 +39,28 @@ def test_version_and_sizes():
     assert qn.nf4_sizes(28672, 8192) == (28672 * 8192 // 2, 3670016, 14336)
     assert qn.quantize_workspace_bytes(4096, 4096) >= 262144 * 4
     assert qn.linear_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 4096 * 4096
-    # d_seq = 1: the forward streams the codes, but the input gradient still runs the
-    # dequantise + GEMM path, so one workspace size must cover both
-    assert qn.linear_workspace_bytes(4096, 4096, 1, 16) >= 2 * 4096 * 4096 + 4 * 64 * 16
+    # d_seq = 1: the forward streams the codes and needs only its A x partials, but the
+    # input gradient still runs the dequantise + GEMM path; the shared query covers both
+    assert qn.linear_fwd_workspace_bytes(4096, 4096, 1, 16) <= 64 * 1024
+    assert qn.linear_bwd_x_workspace_bytes(4096, 4096, 1, 16) >= 2 * 4096 * 4096
+    assert qn.linear_workspace_bytes(4096, 4096, 1, 16) == qn.linear_bwd_x_workspace_bytes(4096, 4096, 1, 16)
+    # small batch (2..64 tokens): the forward keeps fp32 K-split partials, no W_hat
+    assert qn.linear_fwd_workspace_bytes(28672, 8192, 64, 64) < 2 * 28672 * 8192 // 4
+    assert qn.linear_fwd_workspace_bytes(4096, 4096, 16, 16) >= 4 * 8 * 16 * 4096
+    # above 64 tokens both calls dequantise W into the workspace
+    assert qn.linear_fwd_workspace_bytes(4096, 4096, 65, 16) >= 2 * 4096 * 4096
     # few output tiles: the GEMM splits K and keeps fp32 partials in the workspace
     # (2 tiles of the 200 x 512 forward -> 4 splits; a small K -> no split)
-    base = qn.linear_workspace_bytes(512, 4096, 200, 16)
+    base = qn.linear_fwd_workspace_bytes(512, 4096, 200, 16)
     assert base >= 2 * 512 * 4096 + 4 * 200 * 512 * 4
     assert qn.linear_workspace_bytes(320, 192, 300, 100) < 2 * 320 * 192 + 4 * 300 * 320 * 4 + (1 << 20)
     assert qn.quantize_workspace_bytes(0, 5) == 0
     assert qn.linear_workspace_bytes(64, 64, 1, 0) == 0
+    assert qn.linear_fwd_workspace_bytes(64, 64, 0, 8) == 0
+    for d_seq in (1, 2, 3, 16, 64, 65, 4096):
+        both = qn.linear_workspace_bytes(1024, 2048, d_seq, 16)
+        assert both == max(qn.linear_fwd_workspace_bytes(1024, 2048, d_seq, 16),
+                           qn.linear_bwd_x_workspace_bytes(1024, 2048, d_seq, 16))
 
 
 def test_library_code_book_bits_equal_oracle():
@@ -70,38 +82,55 @@ def test_argument_validation_without_device_work():
     assert lib.nf4_quantize(FAKE + 4, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     # workspace too small -> -3
     assert lib.nf4_quantize(FAKE, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, 8, None) == -3
-    # linear: d_in not a multiple of 64 -> -2
-    args = [FAKE, FAKE, FAKE, FAKE, 64, 96, FAKE, FAKE, 8, 2.0, FAKE, 16, FAKE, FAKE, 1 << 30, None]
-    assert lib.qlora_linear_fwd(*args) == -2
-    assert lib.qlora_linear_bwd_x(*args) == -2
+    # linear: codes, qconst, qscale, qmean, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy, ws, ws_bytes, stream
+    def lin(**kw):
+        a = dict(d_out=64, d_in=64, r=8, ldx=64, d_seq=16, Y=FAKE, ldy=64, ws=1 << 30)
+        a.update(kw)
+        return [FAKE, FAKE, FAKE, FAKE, a["d_out"], a["d_in"], FAKE, FAKE, a["r"], 2.0, FAKE, a["ldx"], a["d_seq"],
+                a["Y"], a["ldy"], FAKE, a["ws"], None]
+    # d_in not a multiple of 64 -> -2
+    assert lib.qlora_linear_fwd(*lin(d_in=96, ldx=96)) == -2
+    assert lib.qlora_linear_bwd_x(*lin(d_in=96, ldy=96)) == -2
     # r out of range -> -1
-    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 0, 2.0, FAKE, 16, FAKE, FAKE, 1 << 30, None]
-    assert lib.qlora_linear_fwd(*args) == -1
-    args[8] = 257
-    assert lib.qlora_linear_fwd(*args) == -1
+    assert lib.qlora_linear_fwd(*lin(r=0)) == -1
+    assert lib.qlora_linear_fwd(*lin(r=257)) == -1
     # workspace too small -> -3
-    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, 16, FAKE, FAKE, 16, None]
-    assert lib.qlora_linear_fwd(*args) == -3
-    assert lib.qlora_linear_bwd_x(*args) == -3
+    assert lib.qlora_linear_fwd(*lin(ws=16)) == -3
+    assert lib.qlora_linear_bwd_x(*lin(ws=16)) == -3
     # null output -> -1
-    args = [FAKE, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, 16, None, FAKE, 1 << 30, None]
-    assert lib.qlora_linear_fwd(*args) == -1
+    assert lib.qlora_linear_fwd(*lin(Y=None)) == -1
+    # leading dimensions: smaller than the row, or not a multiple of 8 -> -1; wider is fine
+    assert lib.qlora_linear_fwd(*lin(ldx=56)) == -1
+    assert b"leading dimension" in lib.qn_last_error()
+    assert lib.qlora_linear_fwd(*lin(ldy=60)) == -1
+    assert lib.qlora_linear_fwd(*lin(ldx=68)) == -1
+    assert lib.qlora_linear_bwd_x(*lin(d_out=128, ldx=64)) == -1     # dY rows are d_out long
+    assert lib.qlora_linear_bwd_x(*lin(d_in=128, ldy=64)) == -1      # dX rows are d_in long
+    assert lib.qlora_linear_fwd(*lin(ldx=72, ldy=8192, ws=16)) == -3    # passes the ld checks
+    # an operand reaching 4 GiB through its leading dimension -> -2
+    assert lib.qlora_linear_fwd(*lin(d_seq=1 << 16, ldx=1 << 16)) == -2
     assert lib.nf4_double_dequant(FAKE, FAKE, FAKE, FAKE, 64, 64, None, None) == -1
-    # adapter gradients: A, B, r, s, X, dY, d_out, d_in, d_seq, dA, dB, ws, ws_bytes, stream
-    g = [FAKE, FAKE, 8, 2.0, FAKE, FAKE, 64, 64, 16, FAKE, FAKE, FAKE, 1 << 30, None]
+    # adapter gradients: A, B, r, s, X, ldx, dY, lddy, d_out, d_in, d_seq, dA, dB, ws, ws_bytes, stream
+    g = [FAKE, FAKE, 8, 2.0, FAKE, 64, FAKE, 64, 64, 64, 16, FAKE, FAKE, FAKE, 1 << 30, None]
     g[0] = None
     assert lib.qlora_lora_grads(*g) == -1                      # null pointer
     g[0] = FAKE
-    g[7] = 96
+    g[9], g[5] = 96, 96
     assert lib.qlora_lora_grads(*g) == -2                      # d_in % 64 != 0
-    g[7] = 64
+    g[9], g[5] = 64, 64
     g[2] = 0
     assert lib.qlora_lora_grads(*g) == -1                      # r < 1
     g[2] = 8
-    g[9] = FAKE + 8
+    g[11] = FAKE + 8
     assert lib.qlora_lora_grads(*g) == -1                      # misaligned dA
-    g[9] = FAKE
-    g[12] = 16
+    g[11] = FAKE
+    g[5] = 32
+    assert lib.qlora_lora_grads(*g) == -1                      # ldx < d_in
+    g[5] = 64
+    g[7] = 68
+    assert lib.qlora_lora_grads(*g) == -1                      # lddy not a multiple of 8
+    g[7] = 64
+    g[14] = 16
     assert lib.qlora_lora_grads(*g) == -3                      # workspace too small
     assert lib.qlora_lora_grads_workspace_bytes(64, 64, 16, 0) == 0
     assert lib.qlora_lora_grads_workspace_bytes(4096, 4096, 4096, 16) >= 2 * 2 * 4096 * 64
@@ -119,10 +148,10 @@ def test_second_level_formats_sizes_and_validation():
     # unknown format -> -1 on every entry point
     assert lib.nf4_quantize_ex(FAKE, 4, 64, 7, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == -1
     assert lib.nf4_double_dequant_ex(FAKE, FAKE, FAKE, FAKE, 4, 64, -1, FAKE, None) == -1
-    assert lib.qlora_linear_fwd_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
-                                   1 << 30, None) == -1
-    assert lib.qlora_linear_bwd_x_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
-                                     1 << 30, None) == -1
+    assert lib.qlora_linear_fwd_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 64, 4, FAKE, 64,
+                                   FAKE, 1 << 30, None) == -1
+    assert lib.qlora_linear_bwd_x_ex(FAKE, FAKE, FAKE, FAKE, 64, 64, 3, FAKE, FAKE, 8, 1.0, FAKE, 64, 4, FAKE, 64,
+                                     FAKE, 1 << 30, None) == -1
     # the 8-bit formats need qconst and qmean; "none" does not (a too-small workspace
     # is the first thing it reports)
     for dq in (0, 1):
@@ -130,10 +159,10 @@ def test_second_level_formats_sizes_and_validation():
         assert lib.nf4_quantize_ex(FAKE, 4, 64, dq, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == -1
     assert lib.nf4_quantize_ex(FAKE, 4, 64, 2, FAKE, None, FAKE, None, FAKE, 1, None) == -3
     assert lib.nf4_quantize_ex(FAKE, 4, 64, 2, FAKE, None, None, None, FAKE, 1 << 20, None) == -1   # qscale needed
-    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, None, 64, 64, 2, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
-                                   1, None) == -3
-    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, FAKE, 64, 64, 1, FAKE, FAKE, 8, 1.0, FAKE, 4, FAKE, FAKE,
-                                   1 << 30, None) == -1
+    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, None, 64, 64, 2, FAKE, FAKE, 8, 1.0, FAKE, 64, 4, FAKE, 64,
+                                   FAKE, 1, None) == -3
+    assert lib.qlora_linear_fwd_ex(FAKE, None, FAKE, FAKE, 64, 64, 1, FAKE, FAKE, 8, 1.0, FAKE, 64, 4, FAKE, 64,
+                                   FAKE, 1 << 30, None) == -1
 
 
 def test_factor_entry_points_validation():
@@ -142,18 +171,21 @@ def test_factor_entry_points_validation():
     assert lib.int8_quantize(FAKE, 0, 64, FAKE, FAKE, None) == -1
     assert lib.int8_quantize(FAKE + 4, 4, 64, FAKE, FAKE, None) == -1          # misaligned W
     assert lib.int8_dequant(FAKE, None, 4, 64, FAKE, None) == -1
-    assert lib.qlr_linear_workspace_bytes(64, 64, 4, 8) >= lib.qlora_linear_workspace_bytes(64, 64, 4, 8) + \
+    assert lib.qlr_linear_workspace_bytes(64, 64, 4, 8) >= lib.qlora_linear_fwd_workspace_bytes(64, 64, 4, 8) + \
         2 * 8 * 64 * 2
     assert lib.qlr_linear_workspace_bytes(64, 64, 4, 0) == 0
     args = [FAKE, FAKE, FAKE, FAKE, 64, 64, 0]
-    tail = [8, 1.0, FAKE, 4, FAKE, FAKE, 1 << 30, None]
+    tail = [8, 1.0, FAKE, 64, 4, FAKE, 64, FAKE, 1 << 30, None]
     assert lib.qlr_linear_fwd(*args, 3, FAKE, FAKE, 4, FAKE, FAKE, *tail) == -1       # bits
     assert lib.qlr_linear_fwd(*args, 4, FAKE, FAKE, 16, FAKE, FAKE, *tail) == -1      # bits
     assert lib.qlr_linear_fwd(*args, 4, None, FAKE, 8, FAKE, FAKE, *tail) == -1       # null factor
-    small = [8, 1.0, FAKE, 4, FAKE, FAKE, 1024, None]
+    small = [8, 1.0, FAKE, 64, 4, FAKE, 64, FAKE, 1024, None]
     assert lib.qlr_linear_fwd(*args, 4, FAKE, FAKE, 8, FAKE, FAKE, *small) == -3      # workspace
-    bad_shape = [FAKE, FAKE, FAKE, FAKE, 64, 100, 0]
-    assert lib.qlr_linear_fwd(*bad_shape, 8, FAKE, FAKE, 8, FAKE, FAKE, *tail) == -2
+    bad_shape = [FAKE, FAKE, FAKE, FAKE, 64, 96, 0]
+    tail96 = [8, 1.0, FAKE, 96, 4, FAKE, 64, FAKE, 1 << 30, None]
+    assert lib.qlr_linear_fwd(*bad_shape, 8, FAKE, FAKE, 8, FAKE, FAKE, *tail96) == -2
+    assert lib.qlr_linear_fwd(*args, 8, FAKE, FAKE, 8, FAKE, FAKE, 8, 1.0, FAKE, 64, 4, FAKE, 32, FAKE, 1 << 30,
+                              None) == -1                                          # ldy < d_out
 
 
 def test_codebook_null_pointer():
