@@ -46,6 +46,8 @@ SIGNATURES = {
     "nf4_double_dequant_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
     "qlora_linear_fwd_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
                                      _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
+    "qlora_linear_fwd_noalloc": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
+                                          _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_bwd_x_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
                                        _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "int8_quantize": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
@@ -254,6 +256,27 @@ def linear_fwd(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torc
     row views of wider arrays (unit column stride)."""
     return _linear("qlora_linear_fwd_ex", q, A, B, s, X, q.d_in, q.d_out, out, workspace,
                    linear_fwd_workspace_bytes)
+
+
+def linear_fwd_noalloc(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """qlora_linear_fwd_noalloc: the forward for 1..64 tokens with no workspace (the library's
+    static per-device scratch instead). Calls that overlap on one device race."""
+    dev = q.device
+    r = A.shape[0]
+    _need(A, torch.bfloat16, (r, q.d_in), "A", dev)
+    _need(B, torch.bfloat16, (q.d_out, r), "B", dev)
+    if X.dim() != 2 or X.shape[1] != q.d_in:
+        raise ValueError(f"input must be [d_seq, {q.d_in}]")
+    d_seq = X.shape[0]
+    ldx = _rows(X, torch.bfloat16, (d_seq, q.d_in), "input", dev)
+    o = out if out is not None else torch.empty(d_seq, q.d_out, dtype=torch.bfloat16, device=dev)
+    ldy = _rows(o, torch.bfloat16, (d_seq, q.d_out), "out", dev)
+    rc = lib().qlora_linear_fwd_noalloc(_ptr(q.codes), _ptr(q.qconst), _ptr(q.qscale), _ptr(q.qmean), q.d_out,
+                                        q.d_in, _dq_code(q.dq), _ptr(A), _ptr(B), r, float(s), _ptr(X), ldx, d_seq,
+                                        _ptr(o), ldy, _stream(dev))
+    _check(rc, "qlora_linear_fwd_noalloc")
+    return o
 
 
 def linear_bwd_x(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, dY: torch.Tensor,

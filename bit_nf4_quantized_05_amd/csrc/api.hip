@@ -263,6 +263,47 @@ GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
 }
 }  // namespace
 
+// ---- scratch of the allocation-free forward ---------------------------------
+// One static device array (each device holds its own copy, from module load until the
+// process ends). Host code never uses the array's name as an address: the address of
+// each device's copy is taken once with hipGetSymbolAddress, with that device current,
+// and kept per device.
+namespace {
+constexpr int64_t kNoAllocScratchBytes = QN_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes % 256 == 0, "scratch size");
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (nullptr and the error text set on failure).
+char* scratch_of_current_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        hip_fail(e, "hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        fail(-4, "device index out of range");
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
 extern "C" {
 
 int qn_profile_enable(int on) {
@@ -411,6 +452,25 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
                      int64_t workspace_bytes, void* stream) {
     return qlora_linear_fwd_ex(codes, qconst, qscale, qmean, d_out, d_in, QN_DQ_INT8, A, B, r, s, X, ldx, d_seq, Y,
                                ldy, workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_fwd_noalloc(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,
+                             int64_t d_out, int64_t d_in, int dq, const uint16_t* A, const uint16_t* B, int r,
+                             float s, const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy,
+                             void* stream) {
+    if (d_seq < 1) return fail(-1, "sizes must be >= 1");
+    if (d_seq > qn::kSkinnyMaxTokens)
+        return fail(-2, "qlora_linear_fwd_noalloc takes at most 64 tokens (more would dequantise W into scratch)");
+    char* ws = scratch_of_current_device();
+    if (ws == nullptr) return -4;
+    LinWs lw;
+    qn::BlockConsts bc;
+    int rc = check_linear(codes, qconst, qscale, qmean, dq, d_out, d_in, A, B, r, X, ldx, d_seq, Y, ldy, false, ws,
+                          kNoAllocScratchBytes, &lw, &bc);
+    if (rc == -3) return fail(-2, "qlora_linear_fwd_noalloc: these sizes need more than the static scratch holds");
+    if (rc) return rc;
+    return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy, ws, lw,
+                          static_cast<hipStream_t>(stream));
 }
 
 int qlora_linear_bwd_x_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,

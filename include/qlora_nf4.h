@@ -194,6 +194,28 @@ int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float*
                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * qlora_linear_fwd_noalloc - qlora_linear_fwd_ex for 1 <= d_seq <= 64 tokens that allocates
+ * nothing and takes no workspace, for callers that cannot allocate device memory or pass
+ * a workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, results (bit for bit) and kernels as qlora_linear_fwd_ex;
+ * the partial sums those kernels keep go to a static device array of
+ * QN_NOALLOC_SCRATCH_BYTES bytes that each device holds from the library's load until
+ * the process ends. Every call on one device uses that device's array: calls that
+ * overlap on one device (other streams, other threads) race and must not be made.
+ * Nothing in the array needs to start at any value: a call writes all of it that it
+ * reads. Returns -2 when d_seq > 64 (the GEMM path would need W dequantised into
+ * scratch, 2 bytes per weight) or when the sizes need more scratch than the array
+ * holds (e.g. 64 tokens of a 28672-row layer); -4 if the array's address cannot be
+ * obtained. Otherwise as qlora_linear_fwd_ex.
+ */
+#define QN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+int qlora_linear_fwd_noalloc(const uint8_t* codes, const int8_t* qconst, const float* qscale,
+                             const float* qmean, int64_t d_out, int64_t d_in, int dq,
+                             const uint16_t* A, const uint16_t* B, int r, float s,
+                             const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy,
+                             void* stream);
+
+/*
  * qlora_linear_bwd_x - input gradient dX = dequant(W)^T dY + s A^T (B^T dY).
  *   [P2 card 1: gradients flow through the dequantised weights, only A and B
  *    are trained; the formula is the adjoint of the forward above]
