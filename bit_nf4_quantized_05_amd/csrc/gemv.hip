@@ -83,14 +83,16 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
 // halves by a cross-lane read. Each code byte (two weights) is looked up as a pair
 // of bf16 code values and dotted with the bf16 x pair (v_dot2_f32_bf16); a_hat
 // multiplies each half-block partial once (the constant factors out of the sum
-// over its block). The lookup table is replicated kLutCopies times with copy c in
-// bank c, so a half-wave never collides, and the x chunks are XOR-swizzled so the
-// 16-byte reads of 16 lanes hit 16 distinct bank groups. s (A x) is formed before
+// over its block). The pair table holds one copy per lane (64 KB), so a wave's
+// lookups never share a bank, and the LDS address of a lookup, byte << 8 | lane << 2,
+// is one v_perm_b32 of the code word and the lane offset (two ALU operations per byte
+// before: extract, then shift and merge; 6.3 -> 6.0 us per 4096 x 4096 call). The x
+// chunks are XOR-swizzled so the 16-byte reads of 16 lanes hit 16 distinct bank groups. s (A x) is formed before
 // the weight loop, so each wave finishes on its own (formed after it, the A loads
 // would have longer to land, but the call measured 7.6 against 6.9 us).
 constexpr int kGvWaves = 16;
 constexpr int kGvSeg = 4096;
-constexpr int kLutCopies = 32;
+constexpr int kLutCopies = 64;
 
 struct GvRowSeg {
     uint4 cw[2];            // code words of the two chunks
@@ -98,19 +100,27 @@ struct GvRowSeg {
     float sv;               // its group scale (a_j without a second level)
 };
 
-__device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv, const uint32_t* lut,
-                                                 uint32_t lane_off) {
+// LDS byte address (within the table) of the bf16 pair of byte i of code word w for
+// the lane whose byte offset is lane4 = 4 lane: [0, 0, byte, lane4] by one v_perm_b32
+// (selector bytes 0..3 pick bytes of w, 4 picks lane4's low byte, 12 gives zero).
+__device__ __forceinline__ uint32_t lut_addr(uint32_t w, uint32_t lane4, uint32_t i) {
+    return __builtin_amdgcn_perm(lane4, w, 0x0C0C0004u | (i << 8));
+}
+
+__device__ __forceinline__ uint32_t lut_pair(const char* lut, uint32_t w, uint32_t lane4, uint32_t i) {
+    return *reinterpret_cast<const uint32_t*>(lut + lut_addr(w, lane4, i));
+}
+
+__device__ __forceinline__ float gemv_half_block(const uint4 c, const uint4* xv, const char* lut, uint32_t lane4) {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
     float part = 0.0f;
 #pragma unroll
     for (int w4 = 0; w4 < 4; ++w4) {
         const uint32_t xw[4] = {xv[w4].x, xv[w4].y, xv[w4].z, xv[w4].w};
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lut[byte * kLutCopies + lane_off]),
+        for (int b = 0; b < 4; ++b)
+            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, lut_pair(lut, cw[w4], lane4, b)),
                                                    __builtin_bit_cast(bf16x2, xw[b]), part, false);
-        }
     }
     return part;
 }
@@ -199,36 +209,39 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     }
     const int nbv = 2 * r;                        // 16-byte pieces of the 16 rows of B
     const uint4* b4 = reinterpret_cast<const uint4*>(B + static_cast<int64_t>(row0) * r);
-    uint4 bst[8];
+    constexpr int kBst = kAx ? 1 : 8;             // r <= 16 in the one-launch form: one piece per lane
+    uint4 bst[kBst];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) bst[i] = uint4{0, 0, 0, 0};
+    for (int i = 0; i < kBst; ++i) bst[i] = uint4{0, 0, 0, 0};
     if (wave == 14) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kBst; ++i)
             if (64 * i < nbv) bst[i] = b4[min(lane + 64 * i, nbv - 1)];
     }
     GvRowSeg g0, g1;
 
     // ---- tables and staged data to LDS; the barriers wait for LDS writes only
-    if (tid < 256) {
-        // code-book values picked from the (scalar) kernel arguments by selects: an
-        // indexed read would be a memory load
+    {
+        // code-book pairs picked from the (scalar) kernel arguments by selects (an
+        // indexed read would be a memory load); thread t fills pair t / 4, copies
+        // 16 (t % 4) .. + 15
+        const int pr = tid >> 2;
         float lo = tab.code[0], hi = tab.code[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) {
-            lo = (tid & 15) == i ? tab.code[i] : lo;
-            hi = (tid >> 4) == i ? tab.code[i] : hi;
+            lo = (pr & 15) == i ? tab.code[i] : lo;
+            hi = (pr >> 4) == i ? tab.code[i] : hi;
         }
         const uint32_t v = pack_bf16x2(lo, hi);
 #pragma unroll
-        for (int c = 0; c < kLutCopies / 4; ++c) lut4[tid * (kLutCopies / 4) + c] = uint4{v, v, v, v};
-        qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));      // T[q] at q + 128
+        for (int c = 0; c < 4; ++c) lut4[pr * (kLutCopies / 4) + (tid & 3) * 4 + c] = uint4{v, v, v, v};
+        if (tid < 256) qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));      // T[q] at q + 128
     }
     stage_store(st, 0);
     if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
     if (wave == 14) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kBst; ++i)
             if (lane + 64 * i < nbv) bs[lane + 64 * i] = bst[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -270,8 +283,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    const uint32_t* lut = reinterpret_cast<const uint32_t*>(lut4);
-    const uint32_t lane_off = static_cast<uint32_t>(lane & (kLutCopies - 1));
+    const char* lut = reinterpret_cast<const char*>(lut4);
+    const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
     const float mu = bc.mean[0];
     float acc[T];
 #pragma unroll
@@ -287,7 +300,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                 uint4 xv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) xv[e] = xs[kb][0][h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
-                acc[0] += a * gemv_half_block(g.cw[h], xv, lut, lane_off);
+                acc[0] += a * gemv_half_block(g.cw[h], xv, lut, lane4);
             } else {
                 // one code-pair lookup per byte for all tokens; per token the same dot
                 // order as the single-token form
@@ -302,8 +315,7 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
                     for (int k = 0; k < T; ++k) xv[k] = xs[kb][k][h * 256 + 4 * lane + (w4 ^ ((lane >> 2) & 3))];
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
-                        const uint32_t byte = (cw[w4] >> (8 * b)) & 0xFFu;
-                        const bf16x2 lv = __builtin_bit_cast(bf16x2, lut[byte * kLutCopies + lane_off]);
+                        const bf16x2 lv = __builtin_bit_cast(bf16x2, lut_pair(lut, cw[w4], lane4, b));
 #pragma unroll
                         for (int k = 0; k < T; ++k) {
                             const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};

@@ -284,3 +284,54 @@ def test_decode_gemv_full_size():
     cfg = WL.CONFIGS["decode"]
     _say("[gemv] decode 4096x4096 d_seq=1 r=16")
     _fwd_bwd_full_check(cfg, check_bwd=True)
+
+
+def test_decode_result_does_not_depend_on_workspace_contents():
+    """The decode GEMV keeps nothing from call to call in its workspace: whatever the
+    workspace held before (zeros, all ones, random bytes, the previous call's partials),
+    the result is the same bits."""
+    cfg = WL.CONFIGS["decode"]
+    w, a, b = _layer(cfg)
+    q = _gpu_quantize(w)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    X = to_gpu_bf16(WL.make_x(cfg))
+    need = qn.linear_fwd_workspace_bytes(cfg.d_out, cfg.d_in, 1, cfg.r)
+    want = qn.linear_fwd(q, A, B, cfg.s, X)
+    torch.cuda.synchronize()
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    fills = [lambda t: t.zero_(), lambda t: t.fill_(0xFF),
+             lambda t: t.copy_(torch.randint(0, 256, (need,), generator=gen, dtype=torch.uint8))]
+    for fill in fills:
+        fill(ws)
+        for _ in range(3):
+            got = qn.linear_fwd(q, A, B, cfg.s, X, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+def test_decode_under_graph_replay_with_new_inputs():
+    """Replays of a captured decode call with new x and new A in place must each equal
+    the eager call on the same inputs."""
+    cfg = WL.CONFIGS["decode"]
+    w, a, b = _layer(cfg)
+    q = _gpu_quantize(w)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    X = torch.empty(1, cfg.d_in, dtype=torch.bfloat16, device=dev())
+    Y = torch.empty(1, cfg.d_out, dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(qn.linear_fwd_workspace_bytes(cfg.d_out, cfg.d_in, 1, cfg.r), dtype=torch.uint8, device=dev())
+    X.copy_(torch.randn(1, cfg.d_in, device=dev()).to(torch.bfloat16))
+    qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws)
+    for i in range(4):
+        X.copy_(torch.randn(1, cfg.d_in, device=dev()).to(torch.bfloat16))
+        A.copy_((torch.randn(cfg.r, cfg.d_in, device=dev()) * 0.01).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = Y.clone()
+        ref = qn.linear_fwd(q, A, B, cfg.s, X)                    # eager, its own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
