@@ -27,6 +27,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -58,25 +59,34 @@ def parse():
 
 
 _ROOT = os.path.dirname(os.path.abspath(__file__))
-# counter summaries under profiles/ and the kernel source each was measured with
-GEMM_TRAFFIC = ("gemm_nt_kernel_4096x4096x4160_traffic.md", "gemm_nt.hip")
-DECODE_TRAFFIC = ("gemv_nf4_kernel_4096x4096_decode_traffic.md", "gemv.hip")
+# counter summaries under profiles/ and the source files (csrc/) of the kernel each was
+# measured with: the kernel's translation unit and every header it includes
+_HEADERS = ("internal.h", "mfma_device.h", "nf4_device.h")
+GEMM_TRAFFIC = ("gemm_nt_kernel_4096x4096x4160_traffic.md", ("gemm_nt.hip",) + _HEADERS)
+DECODE_TRAFFIC = ("gemv_nf4_kernel_4096x4096_decode_traffic.md", ("gemv.hip",) + _HEADERS)
+
+
+def sources_sha256(files) -> str:
+    """SHA-256 over the listed csrc/ files, concatenated in the listed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(_ROOT, "bit_nf4_quantized_05_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(which):
-    """HBM bytes per launch (per call for the decode pair) from a committed counter
-    summary, or None when the kernel source has changed since the counters were taken
-    (the summary records the SHA-256 of the source file it was measured with)."""
-    import hashlib
+    """HBM bytes per launch (per call for the decode kernel) from a committed counter
+    summary, or None when any source the kernel is compiled from has changed since the
+    counters were taken (the summary records the SHA-256 of those files)."""
     import re
-    profile, source = which
+    profile, files = which
     try:
         text = open(os.path.join(_ROOT, "profiles", profile)).read()
-        src = os.path.join(_ROOT, "bit_nf4_quantized_05_amd", "csrc", source)
-        src_hash = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        src_hash = sources_sha256(files)
     except OSError:
         return None
-    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    h = re.search(r"sources_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
     if not h or not t or h.group(1) != src_hash:
         return None
@@ -187,18 +197,24 @@ def rotated_copies(qn, q, n: int, dev) -> list:
     return out
 
 
+def _cpu_threads():
+    """(cores the process may run on, BLAS threads numpy uses)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    return cores, blas
+
+
 def cpu_baseline(cfg, dcfg, tokens: int) -> dict:
     """The oracle, as it stands, on the step's workload (or a token sample of it):
     full quantise + dequantise of W, forward and input gradient for `tokens`
     tokens, and the d_seq = 1 forward, in float64 with numpy."""
-    import numpy as np
     import workloads as WL
     from oracle import nf4_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores, blas = _cpu_threads()
     w = WL.make_weight(cfg)
     a, b = WL.make_lora(cfg)
     x = WL.make_x(cfg)[:tokens]
@@ -212,11 +228,96 @@ def cpu_baseline(cfg, dcfg, tokens: int) -> dict:
     O.linear_fwd(wh, a, b, dcfg.s, x1)
     dt = time.perf_counter() - t0
     flops = 2 * (2 * cfg.d_out * cfg.d_in * tokens + 2 * cfg.r * tokens * (cfg.d_in + cfg.d_out)) + dcfg.fwd_flops()
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": round(dt, 3),
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas), "affinity_cores": int(cores),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "blas_env": {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")},
             "sample": (f"{cfg.d_out}x{cfg.d_in} layer: full NF4+DQ quantise and bf16 dequantise, fwd + dX for "
-                       f"{tokens} of the {cfg.d_seq} tokens and the d_seq=1 forward, float64 numpy "
-                       f"(BLAS threads = cores)")}
+                       f"{tokens} of the {cfg.d_seq} tokens and the d_seq=1 forward; float64 numpy, the "
+                       f"elementwise steps on one thread, the products on {blas} BLAS threads")}
+
+
+def cpu_per_workload(rows_cap: int = 1024, tokens_cap: int = 256) -> dict:
+    """The oracle on each of the five workloads, on a bounded sample where the layer is
+    large: quantise + dequantise of the first min(d_out, rows_cap) rows (whole blocks,
+    the second level over the sample's own groups), then forward and input gradient of
+    those rows on the first min(d_seq, tokens_cap) tokens (the input gradient is the
+    sample rows' share of dX). Rates per the algorithmic units of each stage."""
+    import workloads as WL
+    from oracle import nf4_oracle as O
+    out = {}
+    for name in ("tiny", "decode", "prefill", "mlp_up", "mlp_down", "large"):
+        cfg = WL.CONFIGS[name]
+        rows, toks = min(cfg.d_out, rows_cap), min(cfg.d_seq, tokens_cap)
+        w = WL.make_weight(cfg)[:rows]
+        a, b = WL.make_lora(cfg)
+        b = b[:rows]
+        x = WL.make_x(cfg)[:toks]
+        dy = WL.make_dy(cfg)[:toks, :rows]
+        n = rows * cfg.d_in
+        t0 = time.perf_counter()
+        q = O.quantize(w)
+        t1 = time.perf_counter()
+        wh = O.double_dequant(q["codes"], q["qconst"], q["qscale"], q["qmean"], rows, cfg.d_in)
+        t2 = time.perf_counter()
+        O.linear_fwd(wh, a, b, cfg.s, x)
+        O.linear_bwd_x(wh, a, b, cfg.s, dy)
+        t3 = time.perf_counter()
+        flops = 2 * (2 * rows * cfg.d_in * toks + 2 * cfg.r * toks * (cfg.d_in + rows))
+        out[name] = {"sample": f"{rows} of {cfg.d_out} rows x {cfg.d_in}, {toks} of {cfg.d_seq} tokens",
+                     "quantize_GBps": round(4.516 * n / (t1 - t0) / 1e9, 4),
+                     "dequant_GBps": round(2.516 * n / (t2 - t1) / 1e9, 4),
+                     "fwd_dX_TFLOPs": round(flops / (t3 - t2) / 1e12, 4),
+                     "seconds": round(t3 - t0, 3)}
+    return out
+
+
+def stream_floor(torch, copies, reps: int) -> dict:
+    """Graph-replayed microseconds per call of the calibration kernels
+    (include/qn_calibrate.h) over the rotated weight copies: the decode GEMV's own loads
+    alone, and a plain streaming read of each copy's packed codes."""
+    import ctypes
+    path = os.path.join(_ROOT, "bit_nf4_quantized_05_amd", "libqn_calibrate.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_nf4_quantized_05_amd.build`")
+    cal = ctypes.CDLL(path)
+    cal.qn_calibrate_code_stream.restype = ctypes.c_int
+    cal.qn_calibrate_code_stream.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 2
+    cal.qn_calibrate_read.restype = ctypes.c_int
+    cal.qn_calibrate_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    d_out, d_in = copies[0].d_out, copies[0].d_in
+    sink = torch.empty(max(d_out, 4096), dtype=torch.int32, device=copies[0].device)
+    grid = 2048
+
+    def code_stream(st):
+        for c in copies:
+            rc = cal.qn_calibrate_code_stream(c.codes.data_ptr(), c.qconst.data_ptr(), c.qscale.data_ptr(),
+                                              d_out, d_in, sink.data_ptr(), st)
+            assert rc == 0, rc
+
+    def plain_read(st):
+        for c in copies:
+            rc = cal.qn_calibrate_read(c.codes.data_ptr(), c.codes.numel(), grid, sink.data_ptr(), st)
+            assert rc == 0, rc
+
+    out = {}
+    for name, fn in (("code_stream_us", code_stream), ("plain_read_us", plain_read)):
+        fn(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(torch.cuda.current_stream().cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(1e3 * e0.elapsed_time(e1) / (reps * len(copies)), 3)
+        del g
+    out["plain_read_GBps"] = round(copies[0].codes.numel() / (out["plain_read_us"] * 1e-6) / 1e9, 1)
+    return out
 
 
 def main():
@@ -248,6 +349,9 @@ def main():
 
     log("[bench] generating inputs")
     W = torch.from_numpy(WL.make_weight(cfg)).to(dev)
+    # the quantise leg reads one of 5 copies of W per step (320 MB, more than the 256 MB
+    # Infinity Cache), so its rate is an HBM rate
+    Ws = [W] + [W.clone() for _ in range(4)]
     a_bits, b_bits = WL.make_lora(cfg)
     A, B = bf16(a_bits), bf16(b_bits)
     X = bf16(WL.make_x(cfg))
@@ -266,7 +370,7 @@ def main():
     torch.cuda.synchronize()
 
     def step(i):
-        qn.quantize(W, out=q, workspace=qws)
+        qn.quantize(Ws[i % len(Ws)], out=q, workspace=qws)
         qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=lws)
         qn.linear_bwd_x(q, A, B, cfg.s, dY, out=dX, workspace=lws)
         qn.linear_fwd(copies[i % len(copies)], A, B, dcfg.s, x1, out=y1, workspace=dws)
@@ -288,26 +392,39 @@ def main():
     step_flops = 2 * cfg.fwd_flops() + dcfg.fwd_flops()
     value = step_flops / (elapsed / args.steps) / 1e12
 
-    # ---- the same K steps again with the library's per-kernel HIP events on
+    # ---- the same K steps again with the library's per-kernel HIP events on, read back
+    # after each step (per-step averages of each kernel, whose median is reported beside
+    # the mean over all steps)
     log(f"[bench] profiled pass of {args.steps} steps")
-    qn.profile_enable(True)
+    per_step = {}
+    totals = {}
     t0 = time.perf_counter()
     for i in range(args.steps):
+        qn.profile_enable(True)
         step(i)
+        for k, (n, ms) in qn.profile_read().items():
+            per_step.setdefault(k, []).append(1e3 * ms / n)
+            tn, tms = totals.get(k, (0, 0.0))
+            totals[k] = (tn + n, tms + ms)
     torch.cuda.synchronize()
     prof_elapsed = time.perf_counter() - t0
-    prof = qn.profile_read()
     qn.profile_enable(False)
-    kernels = {k: {"launches": n, "avg_us": round(1e3 * ms / n, 3)} for k, (n, ms) in sorted(prof.items())}
+    prof = totals
+    kernels = {k: {"launches": n, "avg_us": round(1e3 * ms / n, 3),
+                   "median_us": round(statistics.median(per_step[k]), 3)} for k, (n, ms) in sorted(prof.items())}
     log("[bench] kernels:", json.dumps(kernels))
 
     # dominant kernel: the fused GEMM (fwd and dX launches have equal algorithmic flops)
     g_n, g_ms = prof["gemm_nt_kernel"]
     gemm_flops = 2 * cfg.d_seq * cfg.d_out * cfg.d_in + 2 * cfg.d_seq * cfg.d_out * cfg.r
     achieved = gemm_flops / (g_ms / g_n * 1e-3) / 1e12
+    achieved_med = gemm_flops / (kernels["gemm_nt_kernel"]["median_us"] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": "gemm_nt_kernel", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(GEMM_TRAFFIC)}
+                "traffic": measured_traffic(GEMM_TRAFFIC),
+                "flops_per_launch": gemm_flops, "avg_us": kernels["gemm_nt_kernel"]["avg_us"],
+                "median_us": kernels["gemm_nt_kernel"]["median_us"],
+                "frac_median": round(achieved_med / PEAK_BF16_TFLOPS, 4)}
 
     # ---- decode (d_seq = 1) over rotated layer copies
     log(f"[bench] decode: {args.decode_iters} calls over {len(copies)} copies")
@@ -353,6 +470,12 @@ def main():
     graph_call_us = 1e3 * e0.elapsed_time(e1) / (g_reps * len(copies))
     del graph
 
+    # the floor of this access pattern on this machine: the decode kernel's own loads
+    # (codes and block constants, one row per wave) without its arithmetic, x or LoRA
+    # term, and a plain read of each copy's 8 MiB of codes, both over the same copies
+    # captured in a HIP graph as above
+    floor = stream_floor(torch, copies, g_reps)
+
     # one launch when A fits one segment (this layer); else the A x slice kernel runs first
     dk = {k: 1e3 * ms / n for k, (n, ms) in dprof.items() if k in ("gemv_nf4_kernel", "lora_ax_partial_kernel")}
     gv_n, gv_ms = dprof["gemv_nf4_kernel"]
@@ -369,7 +492,10 @@ def main():
               "roofline": {"bound": "hbm", "kernel": " + ".join(sorted(dk)),
                            "achieved": round(d_gbps, 1), "peak": PEAK_HBM_GBPS,
                            "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
-                           "traffic": measured_traffic(DECODE_TRAFFIC)}}
+                           "traffic": measured_traffic(DECODE_TRAFFIC),
+                           "floor_call_us": floor["code_stream_us"],
+                           "frac_of_floor": round(floor["code_stream_us"] / graph_call_us, 4)},
+              "floor": floor}
 
     # ---- adapter gradients (dA, dB) of the same layer, outside the timed step
     log(f"[bench] adapter gradients: {args.steps} calls")
@@ -467,6 +593,8 @@ def main():
     if args.cpu_tokens > 0:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, dcfg, args.cpu_tokens)
+        log("[bench] cpu baseline: oracle on each workload (bounded samples)")
+        out["cpu_baseline"]["per_workload"] = cpu_per_workload()
     print(json.dumps(out), flush=True)
 
 

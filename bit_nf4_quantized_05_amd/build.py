@@ -1,4 +1,6 @@
-"""Builds libqlora_nf4.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libqlora_nf4.so (HIP, gfx950) in-tree with hipcc, and beside it
+libqn_calibrate.so, the benchmark's streaming-read calibration kernels
+(include/qn_calibrate.h), which are not part of the layer.
 
     python -m bit_nf4_quantized_05_amd.build
 """
@@ -13,6 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libqlora_nf4.so")
+CALIB_OUT = os.path.join(PKG, "libqn_calibrate.so")
+CALIB_SOURCES = ["calibrate.hip"]
 BUILD = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "prologue.hip", "gemv.hip", "skinny.hip", "lora_grads.hip", "factors.hip",
@@ -39,18 +43,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(CALIB_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + CALIB_SOURCES))
+    _link(objs[:len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], CALIB_OUT)
     if verbose:
-        print("built", OUT)
+        print("built", OUT, "and", CALIB_OUT)
     return OUT
 
 

@@ -199,3 +199,27 @@ def test_missing_library_is_an_error(monkeypatch, tmp_path):
         _lib.lib()
     monkeypatch.undo()
     assert isinstance(_lib.lib(), ctypes.CDLL)
+
+
+def test_calibration_library_exports_and_validation():
+    """libqn_calibrate.so (the benchmark's streaming-read floor, include/qn_calibrate.h)
+    exports what its header declares and rejects bad arguments before any device work."""
+    path = os.path.join(ROOT, "bit_nf4_quantized_05_amd", "libqn_calibrate.so")
+    cal = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qn_calibrate.h")).read(), flags=re.S)
+    names = set(re.findall(r"^\s*int\s+([a-z][a-z0-9_]*)\s*\(", text, flags=re.M))
+    assert names == {"qn_calibrate_code_stream", "qn_calibrate_read"}
+    for n in names:
+        assert hasattr(cal, n)
+    f = cal.qn_calibrate_code_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 2
+    assert f(None, FAKE, FAKE, 64, 64, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, 64, 96, FAKE, None) == -1          # d_in % 64 != 0
+    assert f(FAKE + 8, FAKE, FAKE, 64, 64, FAKE, None) == -1      # misaligned codes
+    g = cal.qn_calibrate_read
+    g.restype = ctypes.c_int
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(FAKE, 24, 1, FAKE, None) == -1                       # not a multiple of 16
+    assert g(FAKE, 4096, 0, FAKE, None) == -1                     # no workgroups
+    assert g(None, 4096, 4, FAKE, None) == -1
