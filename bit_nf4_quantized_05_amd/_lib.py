@@ -44,6 +44,7 @@ SIGNATURES = {
     "qn_nf4_sizes_ex": (_c_int, [_c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp]),
     "nf4_quantize_ex": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "nf4_double_dequant_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "qlora_set_fwd_gemm": (_c_int, [_c_int]),
     "qlora_linear_fwd_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
                                      _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_fwd_noalloc": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
@@ -256,6 +257,19 @@ def linear_fwd(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torc
     row views of wider arrays (unit column stride)."""
     return _linear("qlora_linear_fwd_ex", q, A, B, s, X, q.d_in, q.d_out, out, workspace,
                    linear_fwd_workspace_bytes)
+
+
+# forms of the forward product for more than 64 tokens (qlora_set_fwd_gemm)
+FWD_GEMM_AUTO, FWD_GEMM_STAGED, FWD_GEMM_FUSED = 0, 1, 2
+
+
+def set_fwd_gemm(form: int) -> int:
+    """qlora_set_fwd_gemm: process-wide choice of how the forward GEMM meets W_hat (staged in
+    the workspace or formed inside the GEMM); returns the previous choice."""
+    rc = lib().qlora_set_fwd_gemm(int(form))
+    if rc < 0:
+        raise ValueError(f"unknown forward GEMM form {form}")
+    return rc
 
 
 def linear_fwd_noalloc(q: NF4Weight, A: torch.Tensor, B: torch.Tensor, s: float, X: torch.Tensor,

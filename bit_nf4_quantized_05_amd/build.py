@@ -19,7 +19,7 @@ CALIB_OUT = os.path.join(PKG, "libqn_calibrate.so")
 CALIB_SOURCES = ["calibrate.hip"]
 BUILD = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "prologue.hip", "gemv.hip", "skinny.hip", "lora_grads.hip", "factors.hip",
+SOURCES = ["api.hip", "quantize.hip", "gemm_nt.hip", "gemm_nf4.hip", "prologue.hip", "gemv.hip", "skinny.hip", "lora_grads.hip", "factors.hip",
            "tables.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

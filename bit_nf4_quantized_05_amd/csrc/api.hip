@@ -205,6 +205,14 @@ namespace {
 // The forward once the arguments are checked: d_seq == 1 (and up to 3 tokens when r <= 16
 // and d_in <= 4096) streams the codes (GEMV), d_seq <= 64 runs the small-batch kernel,
 // otherwise dequantise + pre-pass + GEMM.
+// forward GEMM form for d_seq > 64 (qlora_set_fwd_gemm)
+std::atomic<int> g_fwd_gemm{QN_FWD_GEMM_AUTO};
+
+// AUTO: W_hat staged in the workspace, then the GEMM
+bool fwd_gemm_fused(int64_t /*d_seq*/, int64_t /*d_out*/, int64_t /*d_in*/) {
+    return g_fwd_gemm.load(std::memory_order_relaxed) == QN_FWD_GEMM_FUSED;
+}
+
 int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_out, int64_t d_in,
                    const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t ldx,
                    int64_t d_seq, uint16_t* Y, int64_t ldy, char* ws, const LinWs& lw, hipStream_t st) {
@@ -224,17 +232,20 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
             return hip_fail(e, "qlora_linear_fwd (small batch)");
         return 0;
     }
-    uint16_t* what = reinterpret_cast<uint16_t*>(ws + lw.what);
+    const bool fused = fwd_gemm_fused(d_seq, d_out, d_in);
+    uint16_t* what = fused ? nullptr : reinterpret_cast<uint16_t*>(ws + lw.what);
     uint16_t* t = reinterpret_cast<uint16_t*>(ws + lw.lora);
     uint16_t* bpad = reinterpret_cast<uint16_t*>(ws + lw.adapt);
     const bool pad = r != lw.r_pad;
-    // dequant W_hat + T = s (X A^T) + B padded to r_pad columns, in one launch
+    // T = s (X A^T) + B padded to r_pad columns (+ the dequantised W_hat when staged), in
+    // one launch
     if ((e = qn::launch_prologue(codes, bc, d_out, d_in, false, what, X, ldx, d_seq, d_in,
                                  A, d_in, false, r, s, t, lw.r_pad, pad ? 1 : 0, B, bpad, d_out, r,
                                  reinterpret_cast<float*>(ws + lw.ppart), st)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (prologue)");
     if ((e = qn::launch_gemm_nt(X, ldx, what, d_in, d_in, t, lw.r_pad, pad ? bpad : B, lw.r_pad, lw.r_pad, Y,
-                                ldy, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st)) != hipSuccess)
+                                ldy, d_seq, d_out, reinterpret_cast<float*>(ws + lw.gpart), st,
+                                fused ? codes : nullptr, &bc)) != hipSuccess)
         return hip_fail(e, "qlora_linear_fwd (gemm)");
     return 0;
 }
@@ -444,6 +455,11 @@ int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float*
     if (rc) return rc;
     return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy, static_cast<char*>(workspace),
                           lw, static_cast<hipStream_t>(stream));
+}
+
+int qlora_set_fwd_gemm(int form) {
+    if (form != QN_FWD_GEMM_AUTO && form != QN_FWD_GEMM_STAGED && form != QN_FWD_GEMM_FUSED) return -1;
+    return g_fwd_gemm.exchange(form);
 }
 
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale, const float* qmean,

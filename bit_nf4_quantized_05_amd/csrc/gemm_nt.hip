@@ -29,6 +29,7 @@
 // tile; gemm_split_reduce adds a tile's S partials in split order and rounds to bf16.
 #include <hip/hip_runtime.h>
 
+#include "gemm_common.h"
 #include "internal.h"
 #include "mfma_device.h"
 #include "nf4_device.h"
@@ -41,56 +42,11 @@ namespace {
 // ---------------------------------------------------------------------------
 // Main NT GEMM
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kChunks = BM * BK / 8;           // 16-byte chunks per operand tile (2048)
-constexpr int kGroupM = 4;                     // tile rows per raster group
-
 // Two LDS stages as distinct objects, so the compiler can tell that reads of one
 // stage do not depend on in-flight direct-to-LDS loads into the other. Each holds
 // [P tile | Q tile] = 2 x 2048 chunks = 64 KB.
 __shared__ uint4 g_st0[2 * kChunks];
 __shared__ uint4 g_st1[2 * kChunks];
-
-// Scheduling hints: interleave `n` groups of (1 LDS read, 2 MFMA).
-#define QN_INTERLEAVE_DS_MFMA(n)                                  \
-    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {          \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);        \
-    }
-
-struct GemmArgs {
-    const uint16_t* P; int64_t ldp;
-    const uint16_t* Q; int64_t ldq; int kt1;
-    const uint16_t* P2; int64_t ldp2;
-    const uint16_t* Q2; int64_t ldq2; int kt2;
-    uint16_t* C; int64_t ldc; int M, N, tiles_m, tiles_n;
-    uint32_t bytesP, bytesQ, bytesP2, bytesQ2;   // buffer extents for the load descriptors
-    float* part; int splits, kper;               // split path: partials [splits][rem][256 x 256], K-steps per split
-    int full, rem;                               // split path: whole tiles, then rem split tiles
-};
-
-// logical tile index -> (tile row, tile column): grouped raster of kGroupM tile rows
-__device__ __forceinline__ void tile_coords(const GemmArgs& g, int logical, int& tm, int& tn) {
-    const int gsize = kGroupM * g.tiles_n;
-    const int grp = logical / gsize;
-    const int first_m = grp * kGroupM;
-    const int gm = min(g.tiles_m - first_m, kGroupM);
-    tm = first_m + (logical % gsize) % gm;
-    tn = (logical % gsize) / gm;
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
-                                             static_cast<int>(bytes), 0x00020000);
-}
-
-// Workgroup barrier without the memory fence __syncthreads() adds (which would wait
-// for every in-flight load, including the stages fetched ahead). The loads a barrier
-// certifies are waited for explicitly with QN_WAIT_VM before it; LDS has no cache.
-// The "memory" clobber keeps the compiler from moving memory accesses across it.
-#define QN_BARRIER() asm volatile("s_barrier" ::: "memory")
 
 // WM x WN waves; each wave owns a (256/WM) x (256/WN) sub-tile of 32x32 MFMA tiles.
 template <int WM, int WN, bool kSplit>
@@ -363,8 +319,20 @@ int64_t gemm_split_part_floats(int64_t M, int64_t N, int64_t K1) {
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
                           int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N, float* part,
-                          hipStream_t st) {
+                          hipStream_t st, const uint8_t* codes, const BlockConsts* bc) {
     GemmArgs g;
+    const bool deq = codes != nullptr;              // Q = W_hat formed from the codes in the kernel
+    g.codes = codes;
+    g.bc = deq ? *bc : BlockConsts{nullptr, nullptr, nullptr, 0, 0};
+    {
+        const NF4Tables& tab = tables();
+        for (int i = 0; i < 16; ++i) g.code[i] = tab.code[i];
+    }
+    const int64_t nblk = deq ? N * (K1 / BK) : 0;   // NF4 blocks of the weight (K1 % 64 == 0)
+    g.bytesC = static_cast<uint32_t>(nblk * 32);
+    g.bytesBq = static_cast<uint32_t>(nblk);
+    g.bytesBs = static_cast<uint32_t>(deq ? 4 * (((nblk - 1) >> g.bc.gshift) + 1) : 0);
+    if (deq) { Q = P; ldq = ldp; }                  // no bf16 weight operand
     g.tiles_m = static_cast<int>((M + BM - 1) / BM);
     g.tiles_n = static_cast<int>((N + BN - 1) / BN);
     if (P2 == nullptr) { P2 = P; Q2 = Q; ldp2 = ldp; ldq2 = ldq; K2 = 0; }
@@ -384,12 +352,18 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
     g.part = part;
     if (g.splits <= 1 || part == nullptr) {
         g.splits = 1;
+        if (deq) return launch_gemm_nf4_body(g, false, st);
         QN_LAUNCH("gemm_nt_kernel", st, gemm_nt_kernel, dim3(g.tiles_m * g.tiles_n), dim3(64 * kGemmWM * kGemmWN), 0,
                   st, g);
         return hipGetLastError();
     }
-    QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.full + g.rem * g.splits), dim3(64 * kGemmWM * kGemmWN), 0,
-              st, g);
+    if (deq) {
+        const hipError_t e = launch_gemm_nf4_body(g, true, st);
+        if (e != hipSuccess) return e;
+    } else {
+        QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.full + g.rem * g.splits), dim3(64 * kGemmWM * kGemmWN),
+                  0, st, g);
+    }
     QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce, dim3(static_cast<unsigned>(g.rem * 64)), dim3(256), 0, st, g);
     return hipGetLastError();
 }

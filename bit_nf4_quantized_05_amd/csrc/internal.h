@@ -70,10 +70,12 @@ hipError_t launch_dequant_rows(const uint8_t* codes, const BlockConsts& bc, int6
 struct GemmSplit { int splits, full, rem; };
 GemmSplit gemm_split(int64_t M, int64_t N, int64_t K1);
 int64_t gemm_split_part_floats(int64_t M, int64_t N, int64_t K1);
+// With codes (and bc) given, Q is instead the weight dequantised inside the GEMM from its
+// packed NF4 codes ([N, K1] row-major, K1 % 64 == 0; Q and ldq are not used).
 hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, int64_t K1,
                           const uint16_t* P2, int64_t ldp2, const uint16_t* Q2, int64_t ldq2,
                           int64_t K2, uint16_t* C, int64_t ldc, int64_t M, int64_t N, float* part,
-                          hipStream_t st);
+                          hipStream_t st, const uint8_t* codes = nullptr, const BlockConsts* bc = nullptr);
 
 // ---- prologue.hip ----
 // One launch before the GEMM of a linear call: LoRA pre-pass

@@ -45,6 +45,20 @@ __device__ __forceinline__ float block_constant(int fmt, int8_t q, float b, floa
     return mu + prod;
 }
 
+// block_constant with selects in place of branches (the same float32 operations and
+// the same result), for loops where a branch would split the instruction schedule
+__device__ __forceinline__ float block_constant_nb(int fmt, int8_t q, float b, float mu) {
+    const uint32_t u = static_cast<uint8_t>(q);
+    const uint32_t e = (u >> 3) & 0xFu, m = u & 0x7u;
+    const float mag = e == 0 ? static_cast<float>(m) * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    const float f8 = (u & 0x80u) ? -mag : mag;
+    const bool fp8 = fmt == kDqFp8;
+    const float num = fp8 ? f8 : static_cast<float>(q);
+    const float den = fp8 ? static_cast<float>(kE4m3Max) : static_cast<float>(kInt8Step);
+    const float prod = b * (num / den);
+    return fmt == kDqNone ? b : mu + prod;
+}
+
 // Ordered sums over K-split partials: v = p[0] + p[stride] + ... + p[(n-1) stride], float32
 // adds from +0.0 in that order. The loads are issued B at a time (slices past n re-read
 // the last one and are masked to +0.0, which leaves a sum that started at +0.0

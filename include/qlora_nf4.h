@@ -177,14 +177,34 @@ int64_t qlora_linear_bwd_x_workspace_bytes(int64_t d_out, int64_t d_in, int64_t 
  * d_seq >= 1, ldx >= d_in and ldy >= d_out, both multiples of 8 (-1 otherwise).
  * d_seq == 1 (and d_seq = 2, 3 when r <= 16 and d_in <= 4096) runs a
  * streaming GEMV over the packed codes; other d_seq <= 64 stream the codes once into
- * small MFMA tiles; larger d_seq dequantises W to bf16 in the workspace and runs the
- * MFMA GEMM with the LoRA branch as extra K-steps.
+ * small MFMA tiles; larger d_seq runs the MFMA GEMM with the LoRA branch as extra
+ * K-steps, on W_hat either dequantised to bf16 in the workspace first or formed tile by
+ * tile inside the GEMM (qlora_set_fwd_gemm; the results are the same bits either way).
  */
 int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qscale,
                      const float* qmean, int64_t d_out, int64_t d_in,
                      const uint16_t* A, const uint16_t* B, int r, float s,
                      const uint16_t* X, int64_t ldx, int64_t d_seq, uint16_t* Y, int64_t ldy,
                      void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * qlora_set_fwd_gemm - choose how the forward product for d_seq > 64 tokens meets W_hat
+ *   [P2 card 1: the 4-bit weights are dequantised to BF16 whenever a weight is used in a
+ *    matrix product]
+ *   QN_FWD_GEMM_AUTO    the library's choice for the shape (the default)
+ *   QN_FWD_GEMM_STAGED  the dequantiser writes W_hat [d_out, d_in] bf16 to the workspace
+ *                       and the GEMM reads it back
+ *   QN_FWD_GEMM_FUSED   the GEMM forms each K-step's 256 x 64 tile of W_hat in LDS from the
+ *                       codes and block constants; W_hat never reaches memory
+ * Both forms compute the same bf16 weights and run the same MFMA sequence, so Y is the
+ * same bits. The choice is process-wide and applies to calls made after it returns;
+ * workspace sizes do not depend on it. Returns the previous choice, or -1 (nothing
+ * changed) for an unknown value.
+ */
+#define QN_FWD_GEMM_AUTO 0
+#define QN_FWD_GEMM_STAGED 1
+#define QN_FWD_GEMM_FUSED 2
+int qlora_set_fwd_gemm(int form);
 
 /* qlora_linear_fwd for a weight quantised in format dq. */
 int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,
