@@ -52,6 +52,10 @@ def parse():
                          "and 28672x8192)")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="tokens of the prefill workload the CPU oracle runs (0 = skip the CPU baseline)")
+    ap.add_argument("--no-fwd-forms", action="store_true",
+                    help="skip the comparison of the two forward GEMM forms (W_hat staged / formed in the GEMM)")
+    ap.add_argument("--fwd-forms-only", action="store_true",
+                    help="only run the comparison of the two forward GEMM forms, print it as JSON and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 512 MiB device copies (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -182,6 +186,51 @@ def layer_leg(qn, torch, WL, name: str, dev) -> dict:
            "bwd_x_gemm_frac_of_peak": round(gemm_flops / (gb * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del W, X, dY, Y, dX, lws, qws, q
     torch.cuda.empty_cache()
+    return out
+
+
+def fwd_forms_leg(qn, torch, WL, dev, reps: int = 3) -> dict:
+    """Forward call with W_hat staged in the workspace and with it formed inside the GEMM
+    (qlora_set_fwd_gemm), on the prefill, MLP and large layers at their token counts and
+    on the large layer at 512 tokens: call time, per-kernel times, TFLOP/s of the call, and
+    which form the library's default (AUTO) takes there."""
+    import numpy as np
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    out = {}
+    for name, tokens in (("prefill", None), ("mlp_up", None), ("mlp_down", None), ("large", None), ("large", 512)):
+        base = WL.CONFIGS[name]
+        cfg = base if tokens is None else WL.custom(f"{name}_{tokens}", base.d_out, base.d_in, tokens, base.r,
+                                                     s=base.s, w_sigma=base.w_sigma)
+        log(f"[bench] forward forms {cfg.name} {cfg.d_out}x{cfg.d_in} d_seq={cfg.d_seq}")
+        W = torch.from_numpy(WL.make_weight(cfg)).to(dev)
+        q = qn.quantize(W)
+        del W
+        a, b = WL.make_lora(cfg)
+        A, B, X = bf16(a), bf16(b), bf16(WL.make_x(cfg))
+        Y = torch.empty(cfg.d_seq, cfg.d_out, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(qn.linear_fwd_workspace_bytes(cfg.d_out, cfg.d_in, cfg.d_seq, cfg.r), dtype=torch.uint8,
+                         device=dev)
+        res = {"d_out": cfg.d_out, "d_in": cfg.d_in, "d_seq": cfg.d_seq, "r": cfg.r}
+        prev = qn.set_fwd_gemm(qn.FWD_GEMM_AUTO)
+        try:
+            for form, fname in ((qn.FWD_GEMM_AUTO, "auto"), (qn.FWD_GEMM_STAGED, "staged"),
+                                (qn.FWD_GEMM_FUSED, "fused")):
+                qn.set_fwd_gemm(form)
+                us, k = timed_calls(qn, torch, lambda i: qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws), reps)
+                if fname == "auto":
+                    res["auto_takes"] = "fused" if any(n.startswith("gemm_nf4") for n in k) else "staged"
+                    continue
+                res[fname] = {"call_us": round(us, 2), "kernel_us": k,
+                              "TFLOPs": round(cfg.fwd_flops() / (us * 1e-6) / 1e12, 1)}
+        finally:
+            qn.set_fwd_gemm(prev)
+        res["fused_over_staged"] = round(res["fused"]["call_us"] / res["staged"]["call_us"], 3)
+        out[cfg.name] = res
+        del q, A, B, X, Y, ws
+        torch.cuda.empty_cache()
     return out
 
 
@@ -339,6 +388,9 @@ def main():
         print("bench.py needs an MI355X GPU", flush=True)
         sys.exit(1)
     dev = torch.device("cuda", 0)
+    if args.fwd_forms_only:
+        print(json.dumps({"fwd_forms": fwd_forms_leg(qn, torch, WL, dev)}), flush=True)
+        return
     cfg = WL.CONFIGS["prefill"]
     dcfg = WL.CONFIGS["decode"]
     assert (cfg.d_out, cfg.d_in, cfg.r, cfg.s) == (dcfg.d_out, dcfg.d_in, dcfg.r, dcfg.s)
@@ -564,6 +616,10 @@ def main():
             log(f"[bench] layer {name}")
             layers[name] = layer_leg(qn, torch, WL, name, dev)
 
+    fwd_forms = {}
+    if not args.no_fwd_forms:
+        fwd_forms = fwd_forms_leg(qn, torch, WL, dev)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -587,6 +643,7 @@ def main():
         "small_batch": small_batch,
         "dq_formats": dq_formats,
         "layers": layers,
+        "fwd_forms": fwd_forms,
         "kernels": kernels,
         "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
     }

@@ -208,9 +208,16 @@ namespace {
 // forward GEMM form for d_seq > 64 (qlora_set_fwd_gemm)
 std::atomic<int> g_fwd_gemm{QN_FWD_GEMM_AUTO};
 
-// AUTO: W_hat staged in the workspace, then the GEMM
-bool fwd_gemm_fused(int64_t /*d_seq*/, int64_t /*d_out*/, int64_t /*d_in*/) {
-    return g_fwd_gemm.load(std::memory_order_relaxed) == QN_FWD_GEMM_FUSED;
+// AUTO picks the in-GEMM dequantisation for a weight whose bf16 copy would not fit the
+// 256 MB Infinity Cache (d_out d_in >= 2^27) at up to 1024 tokens (at most 4 tile rows of
+// 256 tokens, each of which dequantises every weight again); otherwise W_hat is staged.
+// Measured at 65..2048 tokens: fused / staged call time 0.55..0.95 for 28672 x 8192 up
+// to 1024 tokens and 1.10 at 2048; 0.98..1.37 for the 11008 x 4096 and 4096 x 11008 MLP
+// layers and 1.00..1.23 for 4096 x 4096, whose staged W_hat stays in the cache.
+bool fwd_gemm_fused(int64_t d_seq, int64_t d_out, int64_t d_in) {
+    const int form = g_fwd_gemm.load(std::memory_order_relaxed);
+    if (form != QN_FWD_GEMM_AUTO) return form == QN_FWD_GEMM_FUSED;
+    return d_out * d_in >= (int64_t{1} << 27) && d_seq <= 1024;
 }
 
 int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_out, int64_t d_in,

@@ -191,7 +191,8 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
  * qlora_set_fwd_gemm - choose how the forward product for d_seq > 64 tokens meets W_hat
  *   [P2 card 1: the 4-bit weights are dequantised to BF16 whenever a weight is used in a
  *    matrix product]
- *   QN_FWD_GEMM_AUTO    the library's choice for the shape (the default)
+ *   QN_FWD_GEMM_AUTO    the library's choice for the shape (the default): fused for a
+ *                       weight of 2^27 or more elements at up to 1024 tokens, else staged
  *   QN_FWD_GEMM_STAGED  the dequantiser writes W_hat [d_out, d_in] bf16 to the workspace
  *                       and the GEMM reads it back
  *   QN_FWD_GEMM_FUSED   the GEMM forms each K-step's 256 x 64 tile of W_hat in LDS from the

@@ -122,9 +122,12 @@ def test_fused_result_is_independent_of_a_previous_call():
         _assert_same_bits(u, v, c.name)
 
 
-@pytest.mark.parametrize("cfg_name", ["prefill", "mlp_up", "mlp_down", "large"])
-def test_fused_equals_staged_full_size(cfg_name):
+@pytest.mark.parametrize("cfg_name,d_seq", [("prefill", None), ("mlp_up", None), ("mlp_down", None), ("large", None),
+                                            ("large", 512), ("large", 1000)])
+def test_fused_equals_staged_full_size(cfg_name, d_seq):
     cfg = WL.CONFIGS[cfg_name]
+    if d_seq is not None:
+        cfg = WL.custom(f"{cfg.name}_{d_seq}tok", cfg.d_out, cfg.d_in, d_seq, cfg.r, s=cfg.s, w_sigma=cfg.w_sigma)
     _say(f"[fused fwd] full size {cfg.name} {cfg.d_out}x{cfg.d_in} d_seq={cfg.d_seq} r={cfg.r}")
     q = qn.quantize(to_gpu_f32(WL.make_weight(cfg)))
     a, b = WL.make_lora(cfg)
@@ -133,3 +136,22 @@ def test_fused_equals_staged_full_size(cfg_name):
                     ).to(torch.bfloat16)
     y_staged, y_fused = _both_forms(q, A, B, cfg.s, X)
     _assert_same_bits(y_fused, y_staged, cfg.name)
+
+
+def test_auto_form_follows_the_shape_rule():
+    """AUTO takes the fused form for a weight of 2^27 or more elements at up to 1024 tokens
+    and stages W_hat otherwise; either way the result is the same bits as staged."""
+    cfg = WL.custom("auto_large", 16384, 8192, 300, 16, s=1.0)
+    q = qn.quantize(to_gpu_f32(WL.make_weight(cfg)))
+    a, b = WL.make_lora(cfg)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    X = to_gpu_bf16(WL.make_x(cfg))
+    qn.set_fwd_gemm(qn.FWD_GEMM_AUTO)
+    qn.profile_enable(True)
+    y_auto = qn.linear_fwd(q, A, B, cfg.s, X).clone()
+    torch.cuda.synchronize()
+    kernels = qn.profile_read()
+    qn.profile_enable(False)
+    assert any(k.startswith("gemm_nf4") for k in kernels), f"AUTO did not take the fused form: {sorted(kernels)}"
+    y_staged, _ = _both_forms(q, A, B, cfg.s, X)
+    _assert_same_bits(y_auto, y_staged, cfg.name)
