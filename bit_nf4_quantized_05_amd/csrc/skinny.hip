@@ -87,6 +87,8 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
     const uint4* codes4 = reinterpret_cast<const uint4*>(a.codes);
     const uint4* x4 = reinterpret_cast<const uint4*>(a.X);
     const float mu = a.bc.mean[0];
+    const char* code_lds = reinterpret_cast<const char*>(s_code);
+    const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
     {
         // code book from the (scalar) kernel arguments by selects
         for (int e = tid; e < 16 * 64; e += 256) {
@@ -177,9 +179,16 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
                 const uint32_t words[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
+                    // weight 2b + h of the word is nibble h of byte b: the lane's copy of code
+                    // value c sits at byte offset c << 8 | lane << 2, one v_perm_b32 of the byte
+                    // of low (high) nibbles and the lane offset
+                    const uint32_t nib[2] = {words[st] & 0x0F0F0F0Fu, (words[st] >> 4) & 0x0F0F0F0Fu};
                     float w[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) w[e] = s_code[((words[st] >> (4 * e)) & 0xFu) * 64 + lane] * ah;
+                    for (int e = 0; e < 8; ++e)
+                        w[e] = *reinterpret_cast<const float*>(
+                                   code_lds + __builtin_amdgcn_perm(lane4, nib[e & 1], 0x0C0C0004u | ((e >> 1) << 8))) *
+                               ah;
                     mma<TT>(acc, xs,
                             uint4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
                                   pack_bf16x2(w[6], w[7])},
