@@ -66,7 +66,7 @@ _ROOT = os.path.dirname(os.path.abspath(__file__))
 # counter summaries under profiles/ and the source files (csrc/) of the kernel each was
 # measured with: the kernel's translation unit and every header it includes
 _HEADERS = ("internal.h", "mfma_device.h", "nf4_device.h")
-GEMM_TRAFFIC = ("gemm_nt_kernel_4096x4096x4160_traffic.md", ("gemm_nt.hip",) + _HEADERS)
+GEMM_TRAFFIC = ("gemm_nt_kernel_4096x4096x4160_traffic.md", ("gemm_nt.hip", "gemm_common.h") + _HEADERS)
 DECODE_TRAFFIC = ("gemv_nf4_kernel_4096x4096_decode_traffic.md", ("gemv.hip",) + _HEADERS)
 
 
