@@ -51,6 +51,7 @@ CASES = [
     ("decode_two_launch", WL.custom("g2", 512, 4160, 1, 24), 1),   # A x slice kernel + GEMV
     ("gemv_three_tokens", WL.custom("g3", 1024, 4096, 3, 16), 3),  # the GEMV on 3 tokens
     ("small_batch", WL.custom("gs", 1024, 2048, 16, 16), 16),      # small-batch kernel + reduce
+    ("small_batch_40", WL.custom("gs2", 1024, 2048, 40, 16), 40),  # the same on three token tiles
     ("gemm_path", WL.custom("gg", 1024, 1536, 300, 16), 300),      # prologue (+ reduce) + GEMM, dX with B itself
     ("gemm_split_r40", WL.custom("gk", 512, 4096, 200, 40), 200),  # split GEMM; dX through a transpose of B
 ]

@@ -203,8 +203,16 @@ def test_linear_fwd_bwd_small(cfg):
 # 2 <= d_seq <= 64 runs the small-batch kernel (codes streamed once, dequantised in
 # registers into 16x16x32 MFMAs): 1..4 token tiles, ragged token counts, K-slices
 # that end inside a block pair (d_in 4160: 65 blocks), several K-splits per
-# workgroup (d_in 11008: 22 slices over 8 splits), r up to 256.
+# workgroup (d_in 11008: 22 slices over 8 splits), r up to 256; also a single block per
+# row (d_in 64), block counts below one slice, ranks 1, 3, 7 and 17 (ragged rank tiles)
+# and outlier weights at 16 tokens or fewer.
 SMALL_BATCH = [
+    WL.custom("sb_4_r1_k64", 64, 64, 4, 1, s=2.0),
+    WL.custom("sb_9_r7_k192", 320, 192, 9, 7, s=0.5),
+    WL.custom("sb_13_r3_k1280", 128, 1280, 13, 3, s=1.0),
+    WL.custom("sb_16_r16_k4096", 1024, 4096, 16, 16, s=1.5),
+    WL.custom("sb_5_r16_outliers", 448, 1024, 5, 16, s=2.0, outlier_frac=0.01),
+    WL.custom("sb_16_r17", 256, 1024, 16, 17, s=1.0),
     WL.custom("sb_2", 128, 256, 2, 8, s=2.0),
     WL.custom("sb_15", 192, 4160, 15, 3, s=1.0),
     WL.custom("sb_16", 256, 1024, 16, 16, s=2.0),
