@@ -56,6 +56,9 @@ def parse():
                     help="skip the comparison of the two forward GEMM forms (W_hat staged / formed in the GEMM)")
     ap.add_argument("--fwd-forms-only", action="store_true",
                     help="only run the comparison of the two forward GEMM forms, print it as JSON and exit")
+    ap.add_argument("--tile-rounds-only", action="store_true",
+                    help="only time the forward GEMM at 2048 tokens over output widths that fill 1/2 to 2 rounds "
+                         "of 256x256 tiles on the 256 CUs (what bounds the MLP-pair GEMMs), print it as JSON and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run three plain 512 MiB device copies (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -234,6 +237,64 @@ def fwd_forms_leg(qn, torch, WL, dev, reps: int = 3) -> dict:
     return out
 
 
+def gemm_plan(M: int, N: int, K1: int, K2: int) -> dict:
+    """The GEMM launch the library makes for C[M, N] with K1 main and K2 LoRA columns:
+    256x256 tiles, one workgroup per CU (160 KB of LDS); when the last round holds at
+    most 128 tiles, their main K-steps are split S = min(4, 256 // R, K1 / 512) ways.
+    critical_steps = K-steps (of 64) of the busiest CU."""
+    T = -(-M // 256) * -(-N // 256)
+    kt1, kt2 = K1 // 64, K2 // 64
+    R = T % 256
+    S = min(4, 256 // R, kt1 // 8) if 0 < R <= 128 else 1
+    if S < 2:
+        return {"tiles": T, "splits": 1, "workgroups": T, "rounds": round(T / 256, 3),
+                "critical_steps": -(-T // 256) * (kt1 + kt2)}
+    kper = -(-kt1 // S)
+    return {"tiles": T, "splits": S, "workgroups": T - R + R * S, "rounds": round(T / 256, 3),
+            "critical_steps": (T // 256) * (kt1 + kt2) + kper + kt2}
+
+
+def tile_rounds_leg(qn, torch, WL, dev, reps: int = 5) -> dict:
+    """Forward GEMM (W_hat staged) at 2048 tokens, r = 64, over output widths whose
+    256x256 tiles fill from half a round to two rounds of the 256 CUs, and the MLP pair's
+    4096x11008 layer: kernel times, the K-steps on the busiest CU, and microseconds per
+    such step. A constant time per step says the GEMM is bound by the per-CU K-step rate
+    times the busiest CU's steps (round quantisation), plus the split reduction."""
+    import numpy as np
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    out = {}
+    prev = qn.set_fwd_gemm(qn.FWD_GEMM_STAGED)
+    try:
+        for d_out, d_in in ((4096, 4096), (8192, 4096), (10240, 4096), (11008, 4096), (12288, 4096),
+                            (16384, 4096), (4096, 11008)):
+            cfg = WL.custom(f"rounds_{d_out}x{d_in}", d_out, d_in, 2048, 64, s=2.0)
+            log(f"[bench] tile rounds {d_out}x{d_in} d_seq=2048")
+            W = torch.from_numpy(WL.make_weight(cfg)).to(dev)
+            q = qn.quantize(W)
+            del W
+            a, b = WL.make_lora(cfg)
+            A, B, X = bf16(a), bf16(b), bf16(WL.make_x(cfg))
+            Y = torch.empty(cfg.d_seq, d_out, dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(qn.linear_fwd_workspace_bytes(d_out, d_in, cfg.d_seq, cfg.r), dtype=torch.uint8,
+                             device=dev)
+            us, k = timed_calls(qn, torch, lambda i: qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws), reps)
+            plan = gemm_plan(cfg.d_seq, d_out, d_in, 64)
+            main = sum(v for n, v in k.items() if n in ("gemm_nt_kernel", "gemm_nt_split"))
+            red = k.get("gemm_split_reduce", 0.0)
+            out[f"{d_out}x{d_in}"] = dict(plan, gemm_us=round(main, 2), reduce_us=round(red, 2),
+                                         us_per_critical_step=round(main / plan["critical_steps"], 3),
+                                         gemm_TFLOPs=round(cfg.fwd_flops() / ((main + red) * 1e-6) / 1e12, 1),
+                                         call_us=round(us, 2))
+            del q, A, B, X, Y, ws
+            torch.cuda.empty_cache()
+    finally:
+        qn.set_fwd_gemm(prev)
+    return out
+
+
 def rotated_copies(qn, q, n: int, dev) -> list:
     """n device copies of the quantised weight q (rotating through them keeps each
     call's weight out of the 256 MB Infinity Cache)."""
@@ -396,6 +457,9 @@ def main():
     dev = torch.device("cuda", 0)
     if args.fwd_forms_only:
         print(json.dumps({"fwd_forms": fwd_forms_leg(qn, torch, WL, dev)}), flush=True)
+        return
+    if args.tile_rounds_only:
+        print(json.dumps({"tile_rounds": tile_rounds_leg(qn, torch, WL, dev)}), flush=True)
         return
     cfg = WL.CONFIGS["prefill"]
     dcfg = WL.CONFIGS["decode"]

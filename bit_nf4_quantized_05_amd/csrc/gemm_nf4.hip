@@ -220,11 +220,13 @@ __device__ __forceinline__ void gemm_nf4_body(const GemmArgs& g) {
         NF_ISSUE_MAIN(k_ + 1, 1 - (S))                                                            \
         NF_DQ_LOADS(kshift + min(k_ + 2, kmain - 1), FC(S), dq_q, dq_s)                           \
         __builtin_amdgcn_sched_barrier(0);                                                        \
+        __builtin_amdgcn_s_setprio(1);                                                            \
         NF_SUB_DQ(S, 1, fb, fa, 0)                                                                \
         NF_SUB_DQ(S, 2, fa, fb, 1)                                                                \
         NF_SUB_DQ(S, 3, fb, fa, 2)                                                                \
         NF_DQ_LOOKUP()                                                                            \
         NF_DQ_STORE(1 - (S), 3)                                                                   \
+        __builtin_amdgcn_s_setprio(0);                                                            \
         __builtin_amdgcn_s_waitcnt(0);                                                            \
         QN_BARRIER();                                                                             \
         NF_FRAGS(1 - (S), 0, fa)                                                                  \
@@ -236,12 +238,14 @@ __device__ __forceinline__ void gemm_nf4_body(const GemmArgs& g) {
         }                                                                                         \
         QN_INTERLEAVE_DS_MFMA((TM + TN));                                                         \
     }
-    // Step k (the last main step, or a LoRA step) on stage S, as in gemm_nt.
+    // Step k (the last main step, or a LoRA step) on stage S, as in gemm_nt. Both kinds of
+    // step raise the wave's issue priority for their pre-barrier sub-steps, as gemm_nt does.
 #define NF_STEP(KTV, S)                                                                           \
     {                                                                                             \
         const int k_ = (KTV);                                                                     \
         if (k_ + 1 < KT) NF_ISSUE_LORA(k_ + 1, 1 - (S))                                           \
         NF_FRAGS(S, 1, fb)                                                                        \
+        __builtin_amdgcn_s_setprio(1);                                                            \
         NF_MFMAS(fa)                                                                              \
         QN_INTERLEAVE_DS_MFMA((TM + TN));                                                         \
         NF_FRAGS(S, 2, fa)                                                                        \
@@ -250,6 +254,7 @@ __device__ __forceinline__ void gemm_nf4_body(const GemmArgs& g) {
         NF_FRAGS(S, 3, fb)                                                                        \
         NF_MFMAS(fa)                                                                              \
         QN_INTERLEAVE_DS_MFMA((TM + TN));                                                         \
+        __builtin_amdgcn_s_setprio(0);                                                            \
         __builtin_amdgcn_s_waitcnt(0);                                                            \
         QN_BARRIER();                                                                             \
         if (k_ + 1 < KT) NF_FRAGS(1 - (S), 0, fa)                                                 \
