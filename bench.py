@@ -10,9 +10,10 @@ DQ groups of 256, LoRA r = 16, s = 2), inputs already resident in HBM:
 `value` = algorithmic flops of the step (both GEMMs with their LoRA terms and the
 GEMV; quantisation counts 0 flops) / step time, in TFLOP/s.
 
-Also reported: per-kernel average durations (HIP events recorded by the library
-on each kernel's own stream, in a second pass of the same K steps right after the
-timed one, so the event records do not perturb `value`), the MFMA roofline fraction of
+Also reported: per-kernel average and per-launch median durations (HIP events recorded
+inline by the library on each kernel's own stream, in a second back-to-back pass of the
+same K steps read after it; the events add about 10 us after each kernel, so `value`
+comes from the first pass, which records nothing), the MFMA roofline fraction of
 the dominant kernel (the GEMM), the decode path's effective GB/s over 32 layer
 copies (> 256 MB, beyond the Infinity Cache), the small-batch forward (2, 16 and 64
 tokens) over the same rotated copies, quantise and decode with the FP8 and no-DQ
@@ -502,7 +503,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps
+    # ---- timed region: K steps back to back, nothing else recorded
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -514,26 +515,23 @@ def main():
     step_flops = 2 * cfg.fwd_flops() + dcfg.fwd_flops()
     value = step_flops / (elapsed / args.steps) / 1e12
 
-    # ---- the same K steps again with the library's per-kernel HIP events on, read back
-    # after each step (per-step averages of each kernel, whose median is reported beside
-    # the mean over all steps)
-    log(f"[bench] profiled pass of {args.steps} steps")
-    per_step = {}
-    totals = {}
+    # ---- the same K steps again, back to back, with every kernel the library launches
+    # bracketed by a pair of HIP events on its own stream (recorded inline, read after the
+    # pass): per-kernel average and per-launch median. The event records leave a gap of
+    # about 10 us after each kernel, so this pass is not the one `value` is taken from.
+    log(f"[bench] instrumented pass of {args.steps} steps")
+    qn.profile_enable(True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        qn.profile_enable(True)
         step(i)
-        for k, (n, ms) in qn.profile_read().items():
-            per_step.setdefault(k, []).append(1e3 * ms / n)
-            tn, tms = totals.get(k, (0, 0.0))
-            totals[k] = (tn + n, tms + ms)
     torch.cuda.synchronize()
-    prof_elapsed = time.perf_counter() - t0
+    inst_elapsed = time.perf_counter() - t0
+    prof = qn.profile_read()
+    per_launch = {k: qn.profile_durations(k) for k in prof}
     qn.profile_enable(False)
-    prof = totals
     kernels = {k: {"launches": n, "avg_us": round(1e3 * ms / n, 3),
-                   "median_us": round(statistics.median(per_step[k]), 3)} for k, (n, ms) in sorted(prof.items())}
+                   "median_us": round(1e3 * statistics.median(per_launch[k]), 3)} for k, (n, ms) in sorted(prof.items())}
     log("[bench] kernels:", json.dumps(kernels))
 
     # dominant kernel: the fused GEMM (fwd and dX launches have equal algorithmic flops)
@@ -715,7 +713,7 @@ def main():
         "layers": layers,
         "fwd_forms": fwd_forms,
         "kernels": kernels,
-        "ms_per_step_profiled": round(prof_elapsed * 1e3 / args.steps, 4),
+        "ms_per_step_instrumented": round(inst_elapsed * 1e3 / args.steps, 4),
     }
     if args.cpu_tokens > 0:
         log(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens")

@@ -59,6 +59,7 @@ SIGNATURES = {
                                 _c_vp]),
     "qn_profile_enable": (_c_int, [_c_int]),
     "qn_profile_read": (_c_int, [_c_vp, _c_int, _c_vp, _c_vp, _c_int]),
+    "qn_profile_durations": (_c_int, [ctypes.c_char_p, _c_vp, _c_int]),
 }
 
 # second-level formats: the QN_DQ_* codes of the header
@@ -351,6 +352,15 @@ def profile_read(cap: int = 64) -> dict:
         nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
         out[nm] = (int(launches[i]), float(total[i]))
     return out
+
+
+def profile_durations(name: str, cap: int = 4096) -> list:
+    """Milliseconds of each launch of kernel `name` timed since profile_enable, in order."""
+    buf = (ctypes.c_float * cap)()
+    n = lib().qn_profile_durations(name.encode(), ctypes.addressof(buf), cap)
+    if n < 0:
+        _check(n, "qn_profile_durations")
+    return [float(buf[i]) for i in range(min(n, cap))]
 
 
 # ---- quantised low-rank factors (W ~ Q + L R with L, R at 4 or 8 bits) ----------

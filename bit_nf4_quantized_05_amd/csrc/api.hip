@@ -357,6 +357,23 @@ int qn_profile_read(char* names, int name_len, int64_t* launches, double* total_
     return static_cast<int>(agg.size());
 }
 
+int qn_profile_durations(const char* name, float* ms, int cap) {
+    if (!name || (!ms && cap > 0) || cap < 0) return fail(-1, "bad argument");
+    std::lock_guard<std::mutex> lk(qn::g_prof_mu);
+    int n = 0;
+    for (auto& r : qn::g_prof) {
+        if (std::strcmp(r.name, name) != 0) continue;
+        hipError_t e = hipEventSynchronize(r.stop);
+        if (e != hipSuccess) return hip_fail(e, "qn_profile_durations");
+        float t = 0.0f;
+        e = hipEventElapsedTime(&t, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "qn_profile_durations");
+        if (n < cap) ms[n] = t;
+        ++n;
+    }
+    return n;
+}
+
 int qn_version(void) { return 100; }
 
 const char* qn_last_error(void) { return g_err.c_str(); }

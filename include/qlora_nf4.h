@@ -339,6 +339,13 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s,
  */
 int qn_profile_enable(int on);
 int qn_profile_read(char* names, int name_len, int64_t* launches, double* total_ms, int cap);
+/*
+ * The duration of each recorded launch of the kernel called `name` (as qn_profile_read
+ * names it), in launch order: waits for those launches' events and writes the first
+ * min(count, cap) milliseconds to ms (host pointer). Returns the number of such launches
+ * (0 for a name never launched), or -1 on a bad argument, -4 on a HIP error.
+ */
+int qn_profile_durations(const char* name, float* ms, int cap);
 
 #ifdef __cplusplus
 }

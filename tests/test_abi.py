@@ -192,6 +192,36 @@ def test_codebook_null_pointer():
     assert _lib.lib().qn_codebook(None) == -1
 
 
+def test_profile_durations_validation():
+    """Per-launch kernel timing: bad arguments are rejected and a kernel that was never
+    recorded has no launches (no device work)."""
+    lib = _lib.lib()
+    assert lib.qn_profile_enable(1) == 0
+    try:
+        assert lib.qn_profile_durations(None, None, 0) == -1
+        assert lib.qn_profile_durations(b"gemm_nt_kernel", None, 4) == -1
+        assert lib.qn_profile_durations(b"gemm_nt_kernel", None, -1) == -1
+        buf = (ctypes.c_float * 4)()
+        assert lib.qn_profile_durations(b"gemm_nt_kernel", ctypes.addressof(buf), 4) == 0
+        assert qn.profile_durations("never_launched") == []
+    finally:
+        assert lib.qn_profile_enable(0) == 0
+
+
+def test_forward_form_switch():
+    """qlora_set_fwd_gemm returns the previous form and rejects unknown values."""
+    prev = qn.set_fwd_gemm(qn.FWD_GEMM_STAGED)
+    try:
+        assert prev in (qn.FWD_GEMM_AUTO, qn.FWD_GEMM_STAGED, qn.FWD_GEMM_FUSED)
+        assert qn.set_fwd_gemm(qn.FWD_GEMM_FUSED) == qn.FWD_GEMM_STAGED
+        assert qn.set_fwd_gemm(qn.FWD_GEMM_AUTO) == qn.FWD_GEMM_FUSED
+        assert _lib.lib().qlora_set_fwd_gemm(3) == -1
+        assert _lib.lib().qlora_set_fwd_gemm(-1) == -1
+        assert qn.set_fwd_gemm(qn.FWD_GEMM_AUTO) == qn.FWD_GEMM_AUTO
+    finally:
+        qn.set_fwd_gemm(prev)
+
+
 def test_missing_library_is_an_error(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "nope.so"))
