@@ -166,11 +166,25 @@ struct ProfRec {
 std::mutex g_prof_mu;
 std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_prof;
+// Events are created once and reused: creating one per launch costs the host more than
+// a short kernel runs, which left the device idle between launches while timing was on.
+std::vector<hipEvent_t> g_pool;
+constexpr size_t kPoolPrefill = 1024;
+
+hipEvent_t take_event_locked() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
+}
 
 void prof_clear_locked() {
     for (auto& r : g_prof) {
-        (void)hipEventDestroy(r.start);
-        (void)hipEventDestroy(r.stop);
+        g_pool.push_back(r.start);
+        g_pool.push_back(r.stop);
     }
     g_prof.clear();
 }
@@ -178,10 +192,11 @@ void prof_clear_locked() {
 
 void* prof_begin(hipStream_t st) {
     if (!g_prof_on.load(std::memory_order_relaxed)) return nullptr;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t e = take_event_locked();
+    if (!e) return nullptr;
     if (hipEventRecord(e, st) != hipSuccess) {
-        (void)hipEventDestroy(e);
+        g_pool.push_back(e);
         return nullptr;
     }
     return e;
@@ -189,13 +204,13 @@ void* prof_begin(hipStream_t st) {
 
 void prof_end(void* token, const char* name, hipStream_t st) {
     if (!token) return;
-    hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) {
-        (void)hipEventDestroy(static_cast<hipEvent_t>(token));
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEvent_t e = take_event_locked();
+    if (!e || hipEventRecord(e, st) != hipSuccess) {
+        g_pool.push_back(static_cast<hipEvent_t>(token));
+        if (e) g_pool.push_back(e);
         return;
     }
-    (void)hipEventRecord(e, st);
-    std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof.push_back({name, static_cast<hipEvent_t>(token), e});
 }
 }  // namespace qn
@@ -327,6 +342,12 @@ extern "C" {
 int qn_profile_enable(int on) {
     std::lock_guard<std::mutex> lk(qn::g_prof_mu);
     qn::prof_clear_locked();
+    while (on && qn::g_pool.size() < qn::kPoolPrefill) {
+        hipEvent_t e = nullptr;
+        const hipError_t err = hipEventCreate(&e);
+        if (err != hipSuccess) return hip_fail(err, "qn_profile_enable");
+        qn::g_pool.push_back(e);
+    }
     qn::g_prof_on.store(on != 0);
     return 0;
 }

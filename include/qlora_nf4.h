@@ -331,6 +331,9 @@ int qlora_lora_grads(const uint16_t* A, const uint16_t* B, int r, float s,
  * it launches with a pair of HIP events recorded on that kernel's stream, so the
  * elapsed time of each kernel is measured on the stream it runs on.
  *   qn_profile_enable(1) clears old records and starts recording; (0) stops and clears.
+ *   The events are created once (1024 of them when recording first starts, more as
+ *   needed) and reused, so recording adds no event creation to a launch. Returns 0, or
+ *   -4 on a HIP error (creating events needs a device).
  *   qn_profile_read waits for the recorded events and fills, per distinct kernel
  *   (up to `cap` of them), its name (NUL-terminated, truncated to name_len bytes,
  *   row i at names + i*name_len), launch count and total milliseconds. Host

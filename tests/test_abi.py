@@ -196,7 +196,8 @@ def test_profile_durations_validation():
     """Per-launch kernel timing: bad arguments are rejected and a kernel that was never
     recorded has no launches (no device work)."""
     lib = _lib.lib()
-    assert lib.qn_profile_enable(1) == 0
+    # enabling creates the reusable events, which needs a device: 0 with one, -4 without
+    assert lib.qn_profile_enable(1) in (0, -4)
     try:
         assert lib.qn_profile_durations(None, None, 0) == -1
         assert lib.qn_profile_durations(b"gemm_nt_kernel", None, 4) == -1
