@@ -343,3 +343,31 @@ def test_decode_under_graph_replay_with_new_inputs():
         ref = qn.linear_fwd(q, A, B, cfg.s, X)                    # eager, its own workspace
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+
+
+def test_kernel_timing_records_each_launch_and_changes_no_result():
+    """qn_profile_enable / qn_profile_read / qn_profile_durations: one duration per launch,
+    in launch order, summing to the aggregate; outputs are the same bits with timing on."""
+    cfg = WL.custom("timed", 512, 768, 300, 16, s=2.0)
+    q = qn.quantize(to_gpu_f32(WL.make_weight(cfg)))
+    a, b = WL.make_lora(cfg)
+    A, B, X = to_gpu_bf16(a), to_gpu_bf16(b), to_gpu_bf16(WL.make_x(cfg))
+    y_plain = qn.linear_fwd(q, A, B, cfg.s, X).clone()
+    qn.profile_enable(True)
+    try:
+        ys = [qn.linear_fwd(q, A, B, cfg.s, X).clone() for _ in range(3)]
+        torch.cuda.synchronize()
+        agg = qn.profile_read()
+        gemm = [k for k in agg if k.startswith("gemm_")]
+        assert gemm, f"no GEMM launch recorded: {sorted(agg)}"
+        for k, (n, total_ms) in agg.items():
+            each = qn.profile_durations(k)
+            assert len(each) == n, k
+            assert all(t > 0.0 for t in each), k
+            assert abs(sum(each) - total_ms) <= 1e-6 * n + 1e-6 * total_ms, k
+        assert agg[gemm[0]][0] % 3 == 0
+    finally:
+        qn.profile_enable(False)
+    assert qn.profile_durations(gemm[0]) == []
+    for y in ys:
+        assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
