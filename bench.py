@@ -188,9 +188,57 @@ def layer_leg(qn, torch, WL, name: str, dev) -> dict:
            "fwd_gemm_TFLOPs": tf(gf), "fwd_gemm_frac_of_peak": round(gemm_flops / (gf * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
            "bwd_x_gemm_TFLOPs": tf(gb),
            "bwd_x_gemm_frac_of_peak": round(gemm_flops / (gb * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del W, X, dY, Y, dX, lws, qws, q
+    del X, dY, Y, dX, lws, qws
+    torch.cuda.empty_cache()
+
+    # decode (d_seq = 1) on this layer: rotated copies of the weight (together > 256 MB,
+    # so each call's weight comes from HBM), the calls over all copies captured once in a
+    # HIP graph and replayed; GPU time per call with the gaps between launches
+    ncopy = max(2, -(-300_000_000 // weight_bytes(cfg)))
+    copies = rotated_copies(qn, q, ncopy, dev)
+    del W, q
+    x1 = bf16(WL.make_x(cfg)[:1])
+    y1 = torch.empty(1, cfg.d_out, dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(max(1, qn.linear_fwd_workspace_bytes(cfg.d_out, cfg.d_in, 1, cfg.r)), dtype=torch.uint8,
+                      device=dev)
+    call_us, dk = timed_calls(qn, torch, lambda i: qn.linear_fwd(copies[i % ncopy], A, B, cfg.s, x1, out=y1,
+                                                                  workspace=dws), 2 * ncopy)
+    g_us = graph_call_us(torch, lambda: [qn.linear_fwd(c, A, B, cfg.s, x1, out=y1, workspace=dws) for c in copies],
+                         ncopy, max(1, 128 // ncopy))
+    nbytes = decode_bytes(cfg)
+    out["decode"] = {"copies": ncopy, "bytes_per_call": nbytes, "call_us_graph_replay": round(g_us, 3),
+                     "GBps": round(nbytes / (g_us * 1e-6) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "call_us_back_to_back": round(call_us, 2), "kernel_us": dk}
+    del copies, x1, y1, dws
     torch.cuda.empty_cache()
     return out
+
+
+def graph_call_us(torch, fn, calls: int, reps: int) -> float:
+    """GPU microseconds per call of fn() (which makes `calls` calls), captured once in a
+    HIP graph (after a warm-up on a side stream) and replayed reps times between events."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / (reps * calls)
+    del graph
+    return us
 
 
 def fwd_forms_leg(qn, torch, WL, dev, reps: int = 3) -> dict:

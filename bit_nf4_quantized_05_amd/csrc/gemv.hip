@@ -363,6 +363,181 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
     }
 }
 
+// ---------------------------------------------------------------------------
+// gemv_nf4_persist (d_seq = 1, layers of more than 4096 rows): the same per-row work
+// as gemv_nf4_kernel<1, kAx>, but one workgroup per CU walks many rows. Wave w of
+// workgroup b takes rows g * 16 + w for the row groups g = b, b + grid, ...; a row is
+// one unit per 4096-weight segment, and the loads of a wave's next unit (its code
+// words, block constants, and on a row's last segment its row of B) go out before the
+// current unit is computed, so a wave keeps two units in flight without any barrier.
+// x (d_in <= kGvXMax) is staged in LDS whole, once, with the tables and s (A x), which
+// the one-launch form (r <= 16, d_in <= 4096) forms once per workgroup. Each row's
+// sums run in the order of gemv_nf4_kernel, so the outputs are the same bits. With one
+// workgroup of 16 rows per CU and round, the kernel above waits out a full load
+// latency per round (28672 x 8192: 7 rounds, 54 us for 126 MB).
+// ---------------------------------------------------------------------------
+constexpr int kGvXMax = 16384;            // x held whole in LDS (32 KB)
+constexpr int kGvPersistWgs = 256;        // one workgroup per CU
+
+struct GvUnit {
+    uint4 cw[2];            // code words of the two chunks
+    int8_t qv;              // second-level code of block l
+    float sv;               // its group scale (a_j without a second level)
+    uint16_t bw[4];         // B[row, lane + 64 i] on a row's last segment (clamped, masked at use)
+};
+
+template <bool kAx>
+__global__ __launch_bounds__(1024)
+void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out, int d_in,
+                      const uint16_t* __restrict__ x, const uint16_t* __restrict__ B, int r, float s,
+                      const float* __restrict__ part, int nparts, const uint16_t* __restrict__ A,
+                      uint16_t* __restrict__ y, NF4Tables tab) {
+    __shared__ uint4 lut4[256 * kLutCopies / 4];
+    __shared__ uint4 xs[kGvXMax / 8];
+    __shared__ float tvs[1024];
+    __shared__ float qlut[256];
+    __shared__ float s_t[256];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nbpr = d_in / 64;
+    const int upr = d_in / 32;
+    const int nseg = (d_in + kGvSeg - 1) / kGvSeg;
+    const int nch = d_in / 8;
+    const int ngroups = (d_out + kGvWaves - 1) / kGvWaves;
+    const int grid = static_cast<int>(gridDim.x);
+    const int my_groups = (ngroups - static_cast<int>(blockIdx.x) + grid - 1) / grid;
+    const int nunits = my_groups * nseg;
+    const uint4* x4 = reinterpret_cast<const uint4*>(x);
+
+    // ---- x whole (chunk c of segment c / 512 at its swizzled place; zero past d_in),
+    // A rows or the A x slice partials, tables
+    uint4 xr[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xr[i] = x4[min(tid + 1024 * i, nch - 1)];
+    uint4 av[8];
+    uint4 tst = uint4{0, 0, 0, 0};
+    if constexpr (kAx) {
+        const uint4* ar = reinterpret_cast<const uint4*>(A) + static_cast<int64_t>(min(wave, r - 1)) * nch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = ar[min(lane + 64 * e, nch - 1)];
+    } else {
+        if (wave >= 10 && wave < 14)
+            tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nparts * r + 3) / 4 - 1)];
+    }
+    {
+        const int pr = tid >> 2;
+        float lo = tab.code[0], hi = tab.code[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            lo = (pr & 15) == i ? tab.code[i] : lo;
+            hi = (pr >> 4) == i ? tab.code[i] : hi;
+        }
+        const uint32_t v = pack_bf16x2(lo, hi);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lut4[pr * (kLutCopies / 4) + (tid & 3) * 4 + c] = uint4{v, v, v, v};
+        if (tid < 256) qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 1024 * i;
+        if (c < nseg * (kGvSeg / 8)) xs[(c & ~511) + gv_xpos(c & 511)] = c < nch ? xr[i] : uint4{0, 0, 0, 0};
+    }
+    if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    auto unit_issue = [&](GvUnit& k, int u) {
+        const int gi = u / nseg;
+        const int S = u - gi * nseg;
+        const int row = min((static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave, d_out - 1);
+        {
+            const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
+            k.qv = bc.q[b];
+            k.sv = bc.scale[b >> bc.gshift];
+        }
+        const int64_t row_u = static_cast<int64_t>(row) * upr;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = S * kGvSeg + h * 2048 + lane * 32;
+            k.cw[h] = codes[row_u + (col < d_in ? col / 32 : 0)];
+        }
+        if (S == nseg - 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) k.bw[i] = B[static_cast<int64_t>(row) * r + min(lane + 64 * i, r - 1)];
+        }
+    };
+    GvUnit g0, g1;
+    unit_issue(g0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kAx) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = lane + 64 * e;
+            if (c < nch) {
+                const uint4 xv = xs[gv_xpos(c)];
+                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                        __builtin_bit_cast(bf16x2, xw[q]), t, false);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+        if (lane == 0 && wave < r) s_t[wave] = s * t;
+    } else {
+        if (tid < r) {
+            float t = 0.0f;
+            for (int p = 0; p < nparts; ++p) t += tvs[p * r + tid];
+            s_t[tid] = s * t;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const char* lut = reinterpret_cast<const char*>(lut4);
+    const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+    const float mu = bc.mean[0];
+    float acc = 0.0f;
+    auto unit = [&](const GvUnit& cur, GvUnit& nxt, int u) {
+        if (u + 1 < nunits) {
+            unit_issue(nxt, u + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int gi = u / nseg;
+        const int S = u - gi * nseg;
+        const bool bok = S * 64 + lane < nbpr;
+        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? cur.sv : mu + cur.sv * qlut[cur.qv + 128];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a = __shfl(ah, h * 32 + (lane >> 1));
+            uint4 xv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[e] = xs[S * 512 + h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
+            acc += a * gemv_half_block(cur.cw[h], xv, lut, lane4);
+        }
+        if (S == nseg - 1) {
+            // rank-r term of the row, row sum, store (the order of gemv_nf4_kernel)
+            const int row = (static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave;
+            float v = acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = lane + 64 * i;
+                if (j < r) v += bf16_to_f32(cur.bw[i]) * s_t[j];
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+            if (lane == 0 && row < d_out) y[row] = bf16_bits(v);
+            acc = 0.0f;
+        }
+    };
+    for (int u = 0; u < nunits; u += 2) {
+        unit(g0, g1, u);
+        if (u + 1 < nunits) unit(g1, g0, u + 1);
+    }
+}
+
 }  // namespace
 
 bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r) {
@@ -374,8 +549,18 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
                            const uint16_t* x, int64_t ldx, int64_t d_seq, uint16_t* y, int64_t ldy, float* ws_part,
                            hipStream_t st) {
     if (!gemv_takes_tokens(d_seq, d_in, r)) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>((d_out + kGvWaves - 1) / kGvWaves));
+    const int64_t ngroups = (d_out + kGvWaves - 1) / kGvWaves;
+    const dim3 grid(static_cast<unsigned>(ngroups));
     const int nt = static_cast<int>(d_seq);
+    // more row groups than CUs, one token, x small enough to keep whole: the persistent form
+    const bool persist = nt == 1 && ngroups > kGvPersistWgs && d_in <= kGvXMax;
+    const dim3 pgrid(static_cast<unsigned>(std::min<int64_t>(ngroups, kGvPersistWgs)));
+    if (persist && r <= kGvWaves && d_in <= kGvSeg) {
+        QN_LAUNCH("gemv_nf4_persist", st, gemv_nf4_persist<true>, pgrid, dim3(64 * kGvWaves), 0, st,
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B, r,
+                  s, ws_part, 0, A, y, tables());
+        return hipGetLastError();
+    }
     if (r <= kGvWaves && d_in <= kGvSeg) {
         // one launch: every workgroup forms s A x from A (r x d_in <= 16 x 4096 bf16)
 #define QN_GV_LAUNCH(TT) \
@@ -395,6 +580,12 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     const int nparts = (nb64 + per - 1) / per;   // <= want
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
               static_cast<int>(d_in), x, r, per, ws_part);
+    if (persist) {
+        QN_LAUNCH("gemv_nf4_persist", st, gemv_nf4_persist<false>, pgrid, dim3(64 * kGvWaves), 0, st,
+                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B, r,
+                  s, ws_part, nparts, A, y, tables());
+        return hipGetLastError();
+    }
     QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<1, false>), grid, dim3(64 * kGvWaves), 0, st,
               reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x,
               static_cast<int>(ldx), 1, B, r, s, ws_part, nparts, A, y, static_cast<int>(ldy), tables());

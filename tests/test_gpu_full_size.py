@@ -142,3 +142,18 @@ def test_linear_large_layer_whole_token_rows():
                                      rng.choice(np.arange(256, cfg.d_seq - 256), 64, replace=False)]))
     assert toks.size == 576
     _products(cfg, toks)
+
+
+@pytest.mark.parametrize("cfg_name", ["mlp_up", "mlp_down", "large"])
+def test_decode_full_size_every_output(cfg_name):
+    """d_seq = 1 on the full-size layers in the launch configuration the bench uses (more
+    than 4096 rows: one workgroup per CU walking many rows), every output against float64."""
+    cfg = WL.CONFIGS[cfg_name]
+    _say(f"[full decode] {cfg_name} d_out={cfg.d_out} d_in={cfg.d_in} r={cfg.r}")
+    a, b = WL.make_lora(cfg)
+    q = _quantize(cfg)
+    ref = _oracle_for(cfg)
+    x1 = WL.make_x(cfg)[:1]
+    y = qn.linear_fwd(q, to_gpu_bf16(a), to_gpu_bf16(b), cfg.s, to_gpu_bf16(x1))
+    torch.cuda.synchronize()
+    check_close(bf16_f64(y), O.linear_fwd(ref["what"], a, b, cfg.s, x1), f"decode {cfg.name}")

@@ -294,6 +294,47 @@ def test_decode_gemv_full_size():
     _fwd_bwd_full_check(cfg, check_bwd=True)
 
 
+# layers of more than 4096 rows take the persistent decode kernel (one workgroup per CU
+# walking many 16-row groups); the first 4096 rows of such a layer, quantised as part of
+# it, form a layer of exactly 256 groups, which takes the one-group-per-workgroup kernel.
+# Both must give the same bits on those rows. Shapes: the one-launch A x form (r <= 16,
+# d_in <= 4096), the two-launch form with 1, 2 (the second 64 wide) and 3 segments per
+# row, d_in = 64; 260 row groups (4 workgroups take two, the rest one), 272 (16 take two)
+# and 516 (4 take three, the rest two).
+PERSIST = [
+    (4160, 4096, 16, "int8"),
+    (4160, 64, 1, "int8"),
+    (4352, 4160, 3, "fp8"),
+    (4160, 11008, 64, "int8"),
+    (8256, 8192, 64, "none"),
+]
+
+
+@pytest.mark.parametrize("shape", PERSIST, ids=[f"{s[0]}x{s[1]}_r{s[2]}_{s[3]}" for s in PERSIST])
+def test_persistent_decode_equals_per_group_kernel(shape):
+    d_out, d_in, r, dq = shape
+    _say(f"[gemv persist] {d_out}x{d_in} r={r} dq={dq}")
+    cfg = WL.custom("persist", d_out, d_in, 1, r, s=1.5)
+    w = WL.make_weight(cfg)
+    a, b = WL.make_lora(cfg)
+    q = qn.quantize(to_gpu_f32(w), dq=dq)
+    A, B, X = to_gpu_bf16(a), to_gpu_bf16(b), to_gpu_bf16(WL.make_x(cfg))
+    y = qn.linear_fwd(q, A, B, cfg.s, X)
+    rows = 4096
+    nb = rows * d_in // 64
+    assert nb % 256 == 0
+    sub = qn.NF4Weight(codes=q.codes[:nb * 32], qconst=q.qconst[:nb] if dq != "none" else q.qconst,
+                       qscale=q.qscale[:nb // 256] if dq != "none" else q.qscale[:nb], qmean=q.qmean,
+                       d_out=rows, d_in=d_in, dq=dq)
+    y_sub = qn.linear_fwd(sub, A, B[:rows].contiguous(), cfg.s, X)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :rows].contiguous().view(torch.int16), y_sub.view(torch.int16))
+    if d_in <= 4160:
+        ref = O.quantize(w, dq=dq)
+        wh = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], d_out, d_in, dq=dq)
+        check_close(bf16_f64(y), O.linear_fwd(wh, a, b, cfg.s, WL.make_x(cfg)), f"decode {d_out}x{d_in}")
+
+
 def test_decode_result_does_not_depend_on_workspace_contents():
     """The decode GEMV keeps nothing from call to call in its workspace: whatever the
     workspace held before (zeros, all ones, random bytes, the previous call's partials),
