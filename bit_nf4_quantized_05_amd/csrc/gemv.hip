@@ -74,11 +74,12 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
 // loads by one wave each and passed through LDS: the x segment (waves 0..7), the
 // A x slice partials (waves 10..13) and the 16 rows of B (wave 14). The block
 // constants are per row: lane l loads block l's 8-bit code (or a_j) and scale with
-// its code words. The first segment's code loads go out only after the first
-// barrier (x, B and the tables in LDS): issued at once with x they filled the
-// memory queues ahead of it and every wave started later (one-launch decode on a
-// 4096 x 4096 layer: 7.3 -> 6.7 us median). The next segment's loads go out before
-// the current one is computed.
+// its code words. In the one-launch form the first segment's code loads go out only
+// after the first barrier (x, B and the tables in LDS): issued at once with x they
+// filled the memory queues ahead of it and every wave started later (one-launch decode
+// on a 4096 x 4096 layer: 7.3 -> 6.7 us median); the two-launch form, which fetches no
+// A rows, issues them right behind x. The next segment's loads go out before the
+// current one is computed.
 // A lane forms a_hat of block l and hands it to the two lanes owning the block's
 // halves by a cross-lane read. Each code byte (two weights) is looked up as a pair
 // of bf16 code values and dotted with the bf16 x pair (v_dot2_f32_bf16); a_hat
@@ -219,6 +220,14 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
             if (64 * i < nbv) bst[i] = b4[min(lane + 64 * i, nbv - 1)];
     }
     GvRowSeg g0, g1;
+    // without A rows to fetch, the first segment's code loads go out right behind x (the
+    // two-launch form: 4096 x 11008 16.5 -> 15.5 us per call); with them they wait for
+    // the first barrier (issued behind the 128 KB of A they made the 4096 x 4096 call
+    // 6.35 -> 6.94 us)
+    if constexpr (!kAx) {
+        seg_issue(g0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 
     // ---- tables and staged data to LDS; the barriers wait for LDS writes only
     {
@@ -245,8 +254,10 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
             if (lane + 64 * i < nbv) bs[lane + 64 * i] = bst[i];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    seg_issue(g0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kAx) {
+        seg_issue(g0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (kAx) {
         // s (A x) of rank row `wave` for each token: 8 chunk dot products per lane, then
         // a fixed xor tree; token k's entries at s_t[16 k + rank]
@@ -425,6 +436,33 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         if (wave >= 10 && wave < 14)
             tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nparts * r + 3) / 4 - 1)];
     }
+    auto unit_issue = [&](GvUnit& k, int u) {
+        const int gi = u / nseg;
+        const int S = u - gi * nseg;
+        const int row = min((static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave, d_out - 1);
+        {
+            const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
+            k.qv = bc.q[b];
+            k.sv = bc.scale[b >> bc.gshift];
+        }
+        const int64_t row_u = static_cast<int64_t>(row) * upr;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int col = S * kGvSeg + h * 2048 + lane * 32;
+            k.cw[h] = codes[row_u + (col < d_in ? col / 32 : 0)];
+        }
+        if (S == nseg - 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) k.bw[i] = B[static_cast<int64_t>(row) * r + min(lane + 64 * i, r - 1)];
+        }
+    };
+    // the first unit's loads: right behind x in the two-launch form, after the first
+    // barrier when the workgroup also fetches the rows of A (as in gemv_nf4_kernel)
+    GvUnit g0, g1;
+    if constexpr (!kAx) {
+        unit_issue(g0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     {
         const int pr = tid >> 2;
         float lo = tab.code[0], hi = tab.code[0];
@@ -446,29 +484,10 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
     if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    auto unit_issue = [&](GvUnit& k, int u) {
-        const int gi = u / nseg;
-        const int S = u - gi * nseg;
-        const int row = min((static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave, d_out - 1);
-        {
-            const int64_t b = static_cast<int64_t>(row) * nbpr + min(S * 64 + lane, nbpr - 1);
-            k.qv = bc.q[b];
-            k.sv = bc.scale[b >> bc.gshift];
-        }
-        const int64_t row_u = static_cast<int64_t>(row) * upr;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = S * kGvSeg + h * 2048 + lane * 32;
-            k.cw[h] = codes[row_u + (col < d_in ? col / 32 : 0)];
-        }
-        if (S == nseg - 1) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) k.bw[i] = B[static_cast<int64_t>(row) * r + min(lane + 64 * i, r - 1)];
-        }
-    };
-    GvUnit g0, g1;
-    unit_issue(g0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kAx) {
+        unit_issue(g0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if constexpr (kAx) {
         float t = 0.0f;
 #pragma unroll
