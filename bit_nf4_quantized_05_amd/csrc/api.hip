@@ -107,9 +107,9 @@ LinWs linear_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r, bool bwd) {
     w.adapt2 = off;                                                                          // B^T (unless the pre-pass reads B)
     if (bwd && !qn::prepass_takes_kmajor(r)) off += align_up(2 * static_cast<int64_t>(r) * d_out, 256);
     w.t = off;                                                                               // GEMV: partial A x
-    if (streams && qn::gemv_takes_tokens(d_seq, d_in, r)) off += align_up(4 * ((d_in + 63) / 64) * static_cast<int64_t>(r), 256);
+    if (streams && qn::gemv_takes_tokens(d_seq, d_out, d_in, r)) off += align_up(4 * qn::gemv_part_floats(d_seq, d_in, r), 256);
     w.part = off;                                                                            // small batch: K-split partials
-    if (streams && !qn::gemv_takes_tokens(d_seq, d_in, r))
+    if (streams && !qn::gemv_takes_tokens(d_seq, d_out, d_in, r))
         off += align_up(4 * static_cast<int64_t>(qn::skinny_splits(d_in, d_seq)) * d_seq * (d_out + w.r_pad), 256);
     w.gpart = off;                                                                           // GEMM K-split partials (few tiles)
     if (gemm) off += align_up(4 * (bwd ? qn::gemm_split_part_floats(d_seq, d_in, d_out)
@@ -239,7 +239,7 @@ int linear_fwd_run(const uint8_t* codes, const qn::BlockConsts& bc, int64_t d_ou
                    const uint16_t* A, const uint16_t* B, int r, float s, const uint16_t* X, int64_t ldx,
                    int64_t d_seq, uint16_t* Y, int64_t ldy, char* ws, const LinWs& lw, hipStream_t st) {
     hipError_t e;
-    if (qn::gemv_takes_tokens(d_seq, d_in, r)) {
+    if (qn::gemv_takes_tokens(d_seq, d_out, d_in, r)) {
         e = qn::launch_gemv_nf4(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy,
                                 reinterpret_cast<float*>(ws + lw.t), st);
         if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd (gemv)");

@@ -26,41 +26,55 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kAxMaxParts = 16;
 
+// T tokens (rows of x at stride ldx): part[(w T + t) r + j] (the one-token layout for T = 1)
+template <int T>
 __global__ __launch_bounds__(256)
 void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint16_t* __restrict__ x,
-                            int r, int blocks_per_part, float* __restrict__ part) {
-    __shared__ float red[256];
+                            int64_t ldx, int r, int blocks_per_part, float* __restrict__ part) {
+    __shared__ float red[T][256];
     const int tid = threadIdx.x;
     const int groups = 256 / r;                   // threads per rank row
     const int nb64 = d_in / 64;
     const int b_lo = blockIdx.x * blocks_per_part;
     const int b_hi = min(b_lo + blocks_per_part, nb64);
-    float acc = 0.0f;
+    float acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
     if (tid < groups * r) {
         const int j = tid % r;
         for (int b = b_lo + tid / r; b < b_hi; b += groups) {
             const uint4* ar = reinterpret_cast<const uint4*>(A + static_cast<int64_t>(j) * d_in + b * 64);
-            const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * 64);
-            uint4 av[8], xv[8];
+            uint4 av[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { av[e] = ar[e]; xv[e] = xr[e]; }
+            for (int e = 0; e < 8; ++e) av[e] = ar[e];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
-                const uint32_t xw[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
+            for (int t = 0; t < T; ++t) {
+                const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx + static_cast<int64_t>(b) * 64);
+                uint4 xv[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
-                                                          __builtin_bit_cast(bf16x2, xw[q]), acc, false);
+                for (int e = 0; e < 8; ++e) xv[e] = xr[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                    const uint32_t xw[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                                 __builtin_bit_cast(bf16x2, xw[q]), acc[t], false);
+                }
             }
         }
     }
-    red[tid] = acc;
+#pragma unroll
+    for (int t = 0; t < T; ++t) red[t][tid] = acc[t];
     __syncthreads();
     if (tid < r) {
-        float t = 0.0f;
-        for (int g = 0; g < groups; ++g) t += red[g * r + tid];
-        part[static_cast<int64_t>(blockIdx.x) * r + tid] = t;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float v = 0.0f;
+            for (int g = 0; g < groups; ++g) v += red[t][g * r + tid];
+            part[(static_cast<int64_t>(blockIdx.x) * T + t) * r + tid] = v;
+        }
     }
 }
 
@@ -387,7 +401,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 // workgroup of 16 rows per CU and round, the kernel above waits out a full load
 // latency per round (28672 x 8192: 7 rounds, 54 us for 126 MB).
 // ---------------------------------------------------------------------------
-constexpr int kGvXMax = 16384;            // x held whole in LDS (32 KB)
+constexpr int kGvXMax = 16384;            // x held whole in LDS (32 KB), one token
+constexpr int kGvXMaxT = 8192;            // the same with 2 or 3 tokens (16 KB each)
 constexpr int kGvPersistWgs = 256;        // one workgroup per CU
 
 struct GvUnit {
@@ -397,17 +412,22 @@ struct GvUnit {
     uint16_t bw[4];         // B[row, lane + 64 i] on a row's last segment (clamped, masked at use)
 };
 
-template <bool kAx>
+// T = 1, 2 or 3 tokens (x and y rows at strides ldx, ldy): each code-pair lookup serves
+// every token, with per token the dot order of the one-token form; s (A x) per token
+// at s_t[16 t + j] (one-launch form) or s_t[t r + j] (from the T-token slice partials).
+template <int T, bool kAx>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out, int d_in,
-                      const uint16_t* __restrict__ x, const uint16_t* __restrict__ B, int r, float s,
+                      const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ B, int r, float s,
                       const float* __restrict__ part, int nparts, const uint16_t* __restrict__ A,
-                      uint16_t* __restrict__ y, NF4Tables tab) {
+                      uint16_t* __restrict__ y, int64_t ldy, NF4Tables tab) {
+    constexpr int kX = T == 1 ? kGvXMax : kGvXMaxT;
+    constexpr int kXPer = kX / 8 / 1024;          // 16-byte x chunks per thread and token
     __shared__ uint4 lut4[256 * kLutCopies / 4];
-    __shared__ uint4 xs[kGvXMax / 8];
+    __shared__ uint4 xs[T][kX / 8];
     __shared__ float tvs[1024];
     __shared__ float qlut[256];
-    __shared__ float s_t[256];
+    __shared__ float s_t[T * 256];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -423,9 +443,11 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
 
     // ---- x whole (chunk c of segment c / 512 at its swizzled place; zero past d_in),
     // A rows or the A x slice partials, tables
-    uint4 xr[2];
+    uint4 xr[T][kXPer];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xr[i] = x4[min(tid + 1024 * i, nch - 1)];
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i) xr[t][i] = x4[t * (ldx / 8) + min(tid + 1024 * i, nch - 1)];
     uint4 av[8];
     uint4 tst = uint4{0, 0, 0, 0};
     if constexpr (kAx) {
@@ -434,7 +456,7 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         for (int e = 0; e < 8; ++e) av[e] = ar[min(lane + 64 * e, nch - 1)];
     } else {
         if (wave >= 10 && wave < 14)
-            tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nparts * r + 3) / 4 - 1)];
+            tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nparts * T * r + 3) / 4 - 1)];
     }
     auto unit_issue = [&](GvUnit& k, int u) {
         const int gi = u / nseg;
@@ -477,10 +499,12 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         if (tid < 256) qlut[tid] = dq_step(bc.fmt, static_cast<int8_t>(tid - 128));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + 1024 * i;
-        if (c < nseg * (kGvSeg / 8)) xs[(c & ~511) + gv_xpos(c & 511)] = c < nch ? xr[i] : uint4{0, 0, 0, 0};
-    }
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < kXPer; ++i) {
+            const int c = tid + 1024 * i;
+            if (c < nseg * (kGvSeg / 8)) xs[t][(c & ~511) + gv_xpos(c & 511)] = c < nch ? xr[t][i] : uint4{0, 0, 0, 0};
+        }
     if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
@@ -489,28 +513,37 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (kAx) {
-        float t = 0.0f;
+        // one token at a time (the scheduling barrier keeps the next token's x reads from
+        // being hoisted)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = lane + 64 * e;
-            if (c < nch) {
-                const uint4 xv = xs[gv_xpos(c)];
-                const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
-                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+        for (int k = 0; k < T; ++k) {
+            float t = 0.0f;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
-                                                        __builtin_bit_cast(bf16x2, xw[q]), t, false);
+            for (int e = 0; e < 8; ++e) {
+                const int c = lane + 64 * e;
+                if (c < nch) {
+                    const uint4 xv = xs[k][gv_xpos(c)];
+                    const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
+                    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
+                                                            __builtin_bit_cast(bf16x2, xw[q]), t, false);
+                }
             }
-        }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
-        if (lane == 0 && wave < r) s_t[wave] = s * t;
+            for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+            if (lane == 0 && wave < r) s_t[16 * k + wave] = s * t;
+            if constexpr (T > 1) __builtin_amdgcn_sched_barrier(0);
+        }
     } else {
         if (tid < r) {
-            float t = 0.0f;
-            for (int p = 0; p < nparts; ++p) t += tvs[p * r + tid];
-            s_t[tid] = s * t;
+#pragma unroll
+            for (int k = 0; k < T; ++k) {
+                float t = 0.0f;
+                for (int p = 0; p < nparts; ++p) t += tvs[(p * T + k) * r + tid];
+                s_t[k * r + tid] = s * t;
+            }
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -518,7 +551,9 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
     const char* lut = reinterpret_cast<const char*>(lut4);
     const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
     const float mu = bc.mean[0];
-    float acc = 0.0f;
+    float acc[T];
+#pragma unroll
+    for (int k = 0; k < T; ++k) acc[k] = 0.0f;
     auto unit = [&](const GvUnit& cur, GvUnit& nxt, int u) {
         if (u + 1 < nunits) {
             unit_issue(nxt, u + 1);
@@ -531,24 +566,52 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const float a = __shfl(ah, h * 32 + (lane >> 1));
-            uint4 xv[4];
+            if constexpr (T == 1) {
+                uint4 xv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) xv[e] = xs[S * 512 + h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
-            acc += a * gemv_half_block(cur.cw[h], xv, lut, lane4);
+                for (int e = 0; e < 4; ++e) xv[e] = xs[0][S * 512 + h * 256 + 4 * lane + (e ^ ((lane >> 2) & 3))];
+                acc[0] += a * gemv_half_block(cur.cw[h], xv, lut, lane4);
+            } else {
+                const uint32_t cw[4] = {cur.cw[h].x, cur.cw[h].y, cur.cw[h].z, cur.cw[h].w};
+                float pt[T];
+#pragma unroll
+                for (int k = 0; k < T; ++k) pt[k] = 0.0f;
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    uint4 xv[T];
+#pragma unroll
+                    for (int k = 0; k < T; ++k) xv[k] = xs[k][S * 512 + h * 256 + 4 * lane + (w4 ^ ((lane >> 2) & 3))];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const bf16x2 lv = __builtin_bit_cast(bf16x2, lut_pair(lut, cw[w4], lane4, b));
+#pragma unroll
+                        for (int k = 0; k < T; ++k) {
+                            const uint32_t xw[4] = {xv[k].x, xv[k].y, xv[k].z, xv[k].w};
+                            pt[k] = __builtin_amdgcn_fdot2_f32_bf16(lv, __builtin_bit_cast(bf16x2, xw[b]), pt[k], false);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int k = 0; k < T; ++k) acc[k] += a * pt[k];
+            }
         }
         if (S == nseg - 1) {
             // rank-r term of the row, row sum, store (the order of gemv_nf4_kernel)
             const int row = (static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave;
-            float v = acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int j = lane + 64 * i;
-                if (j < r) v += bf16_to_f32(cur.bw[i]) * s_t[j];
+            for (int k = 0; k < T; ++k) {
+                float v = acc[k];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = lane + 64 * i;
+                    if (j < r) v += bf16_to_f32(cur.bw[i]) * s_t[(kAx ? 16 : r) * k + j];
+                }
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+                if (lane == 0 && row < d_out) y[k * ldy + row] = bf16_bits(v);
+                acc[k] = 0.0f;
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-            if (lane == 0 && row < d_out) y[row] = bf16_bits(v);
-            acc = 0.0f;
         }
     };
     for (int u = 0; u < nunits; u += 2) {
@@ -559,55 +622,77 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
 
 }  // namespace
 
-bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r) {
-    return d_seq == 1 || (d_seq <= kGemvMaxTokens && r <= kGvWaves && d_in <= kGvSeg);
+bool gemv_takes_tokens(int64_t d_seq, int64_t d_out, int64_t d_in, int r) {
+    if (d_seq == 1) return true;
+    if (d_seq > kGemvMaxTokens) return false;
+    if (r <= kGvWaves && d_in <= kGvSeg) return true;              // one launch, s A x per workgroup
+    // persistent, after the A x slice kernel: 2 tokens (28672 x 8192, r = 64: 45.6 us per
+    // call against 61 us in the small-batch kernels; 11008 x 4096: 17.2 against 19.4); a
+    // third token costs more than it saves there (21.7 against 19.4 us on 11008 x 4096)
+    return d_seq == 2 && (d_out + kGvWaves - 1) / kGvWaves > kGvPersistWgs && d_in <= kGvXMaxT;
+}
+
+int64_t gemv_part_floats(int64_t d_seq, int64_t d_in, int r) {
+    return std::min<int64_t>(1024, std::max<int64_t>(1, d_in / 64) * r * d_seq);
 }
 
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, int64_t ldx, int64_t d_seq, uint16_t* y, int64_t ldy, float* ws_part,
                            hipStream_t st) {
-    if (!gemv_takes_tokens(d_seq, d_in, r)) return hipErrorInvalidValue;
+    if (!gemv_takes_tokens(d_seq, d_out, d_in, r)) return hipErrorInvalidValue;
     const int64_t ngroups = (d_out + kGvWaves - 1) / kGvWaves;
     const dim3 grid(static_cast<unsigned>(ngroups));
     const int nt = static_cast<int>(d_seq);
-    // more row groups than CUs, one token, x small enough to keep whole: the persistent form
-    const bool persist = nt == 1 && ngroups > kGvPersistWgs && d_in <= kGvXMax;
+    // more row groups than CUs and x small enough to keep whole: the persistent form
+    const bool persist = ngroups > kGvPersistWgs && d_in <= (nt == 1 ? kGvXMax : kGvXMaxT);
     const dim3 pgrid(static_cast<unsigned>(std::min<int64_t>(ngroups, kGvPersistWgs)));
-    if (persist && r <= kGvWaves && d_in <= kGvSeg) {
-        QN_LAUNCH("gemv_nf4_persist", st, gemv_nf4_persist<true>, pgrid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B, r,
-                  s, ws_part, 0, A, y, tables());
+    const bool one_launch = r <= kGvWaves && d_in <= kGvSeg;
+    const uint4* c4 = reinterpret_cast<const uint4*>(codes);
+    const int dout = static_cast<int>(d_out), din = static_cast<int>(d_in);
+#define QN_GVP_LAUNCH(TT, AX, NP) \
+    QN_LAUNCH("gemv_nf4_persist", st, (gemv_nf4_persist<TT, AX>), pgrid, dim3(64 * kGvWaves), 0, st, c4, bc, dout, \
+              din, x, ldx, B, r, s, ws_part, NP, A, y, ldy, tables())
+    if (persist && one_launch) {
+        if (nt == 1) QN_GVP_LAUNCH(1, true, 0);
+        else if (nt == 2) QN_GVP_LAUNCH(2, true, 0);
+        else QN_GVP_LAUNCH(3, true, 0);
         return hipGetLastError();
     }
-    if (r <= kGvWaves && d_in <= kGvSeg) {
+    if (one_launch) {
         // one launch: every workgroup forms s A x from A (r x d_in <= 16 x 4096 bf16)
 #define QN_GV_LAUNCH(TT) \
         QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<TT, true>), grid, dim3(64 * kGvWaves), 0, st, \
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, \
-                  static_cast<int>(ldx), nt, B, r, s, ws_part, 0, A, y, static_cast<int>(ldy), tables())
+                  c4, bc, dout, din, x, static_cast<int>(ldx), nt, B, r, s, ws_part, 0, A, y, static_cast<int>(ldy), \
+                  tables())
         if (nt == 1) QN_GV_LAUNCH(1);
         else if (nt == 2) QN_GV_LAUNCH(2);
         else QN_GV_LAUNCH(3);
 #undef QN_GV_LAUNCH
         return hipGetLastError();
     }
-    // slices of A x: at most 16, and nparts * r <= 1024 partials in all
+    // slices of A x: at most 16, and nparts * d_seq * r <= 1024 partials in all
+    // (gemv_part_floats); two tokens only in the persistent form
     const int nb64 = static_cast<int>(d_in / 64);
-    const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / r}));
+    const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / (r * nt)}));
     const int per = (nb64 + want - 1) / want;
     const int nparts = (nb64 + per - 1) / per;   // <= want
-    QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel, dim3(nparts), dim3(256), 0, st, A,
-              static_cast<int>(d_in), x, r, per, ws_part);
+#define QN_AX_LAUNCH(TT) \
+    QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel<TT>, dim3(nparts), dim3(256), 0, st, A, din, x, \
+              ldx, r, per, ws_part)
+    if (nt > 2) return hipErrorInvalidValue;
+    if (nt == 1) QN_AX_LAUNCH(1);
+    else QN_AX_LAUNCH(2);
+#undef QN_AX_LAUNCH
     if (persist) {
-        QN_LAUNCH("gemv_nf4_persist", st, gemv_nf4_persist<false>, pgrid, dim3(64 * kGvWaves), 0, st,
-                  reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x, B, r,
-                  s, ws_part, nparts, A, y, tables());
+        if (nt == 1) QN_GVP_LAUNCH(1, false, nparts);
+        else QN_GVP_LAUNCH(2, false, nparts);
         return hipGetLastError();
     }
-    QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<1, false>), grid, dim3(64 * kGvWaves), 0, st,
-              reinterpret_cast<const uint4*>(codes), bc, static_cast<int>(d_out), static_cast<int>(d_in), x,
-              static_cast<int>(ldx), 1, B, r, s, ws_part, nparts, A, y, static_cast<int>(ldy), tables());
+#undef QN_GVP_LAUNCH
+    if (nt != 1) return hipErrorInvalidValue;
+    QN_LAUNCH("gemv_nf4_kernel", st, (gemv_nf4_kernel<1, false>), grid, dim3(64 * kGvWaves), 0, st, c4, bc, dout, din,
+              x, static_cast<int>(ldx), 1, B, r, s, ws_part, nparts, A, y, static_cast<int>(ldy), tables());
     return hipGetLastError();
 }
 

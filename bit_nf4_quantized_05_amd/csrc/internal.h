@@ -118,11 +118,12 @@ hipError_t launch_transpose_pad(const uint16_t* src, int64_t rows, int64_t cols,
 // ---- gemv.hip ----
 // y[t, o] = sum_i w_hat[o,i] x[t, i] + s * sum_k B[o,k] (A x_t)[k], streaming the packed
 // codes, for d_seq = 1, or for 2 <= d_seq <= kGemvMaxTokens tokens when r <= 16 and
-// d_in <= 4096 (gemv_takes_tokens); x rows at stride ldx, y rows at stride ldy (elements,
-// multiples of 8); ws_part holds at most d_in/64 x r floats of partial A x sums (d_seq = 1
-// only).
+// d_in <= 4096, or for 2 tokens when d_out > 4096 and d_in <= 8192 (gemv_takes_tokens); x rows at stride
+// ldx, y rows at stride ldy (elements, multiples of 8); ws_part holds gemv_part_floats
+// floats of partial A x sums (two-launch forms).
 constexpr int kGemvMaxTokens = 3;
-bool gemv_takes_tokens(int64_t d_seq, int64_t d_in, int r);
+bool gemv_takes_tokens(int64_t d_seq, int64_t d_out, int64_t d_in, int r);
+int64_t gemv_part_floats(int64_t d_seq, int64_t d_in, int r);
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
                            const uint16_t* A, const uint16_t* B, int r, float s,
                            const uint16_t* x, int64_t ldx, int64_t d_seq, uint16_t* y, int64_t ldy, float* ws_part,

@@ -335,6 +335,57 @@ def test_persistent_decode_equals_per_group_kernel(shape):
         check_close(bf16_f64(y), O.linear_fwd(wh, a, b, cfg.s, WL.make_x(cfg)), f"decode {d_out}x{d_in}")
 
 
+# Few tokens on layers of more than 4096 rows take the persistent GEMV too: 2 or 3 with the
+# rows of A in the same launch (r <= 16, d_in <= 4096; the first 4096 rows must equal the
+# 256-group kernel's bits), 2 after the two-token A x slice kernel (r > 16 or d_in > 4096,
+# d_in <= 8192). Every output is also checked against float64, one case on row windows of
+# wider X and Y buffers.
+PERSIST_TOKENS = [
+    (4160, 4096, 16, 2, "int8"),
+    (4160, 64, 1, 3, "int8"),
+    (4160, 8192, 64, 2, "int8"),
+    (4352, 4160, 3, 2, "fp8"),
+    (4352, 1024, 33, 2, "none"),
+]
+
+
+@pytest.mark.parametrize("shape", PERSIST_TOKENS,
+                         ids=[f"{s[0]}x{s[1]}_r{s[2]}_t{s[3]}_{s[4]}" for s in PERSIST_TOKENS])
+def test_persistent_gemv_few_tokens(shape):
+    d_out, d_in, r, t, dq = shape
+    _say(f"[gemv persist tokens] {d_out}x{d_in} r={r} tokens={t} dq={dq}")
+    cfg = WL.custom("persist_t", d_out, d_in, t, r, s=0.75)
+    w = WL.make_weight(cfg)
+    a, b = WL.make_lora(cfg)
+    q = qn.quantize(to_gpu_f32(w), dq=dq)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    x = WL.make_x(cfg)
+    if d_in == 1024:
+        xw = torch.zeros(t, d_in + 64, dtype=torch.bfloat16, device=dev())
+        xw[:, 32:32 + d_in] = to_gpu_bf16(x)
+        X = xw[:, 32:32 + d_in]
+        yw = torch.full((t, d_out + 128), 3.0, dtype=torch.bfloat16, device=dev())
+        qn.linear_fwd(q, A, B, cfg.s, X, out=yw[:, 64:64 + d_out])
+        torch.cuda.synchronize()
+        assert bool((yw[:, :64] == 3.0).all()) and bool((yw[:, 64 + d_out:] == 3.0).all()), "wrote outside Y"
+        y = yw[:, 64:64 + d_out].contiguous()
+    else:
+        X = to_gpu_bf16(x)
+        y = qn.linear_fwd(q, A, B, cfg.s, X)
+    if r <= 16 and d_in <= 4096:
+        rows = 4096
+        nb = rows * d_in // 64
+        sub = qn.NF4Weight(codes=q.codes[:nb * 32], qconst=q.qconst[:nb], qscale=q.qscale[:nb // 256],
+                           qmean=q.qmean, d_out=rows, d_in=d_in, dq=dq)
+        y_sub = qn.linear_fwd(sub, A, B[:rows].contiguous(), cfg.s, X.contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(y[:, :rows].contiguous().view(torch.int16), y_sub.view(torch.int16))
+    torch.cuda.synchronize()
+    ref = O.quantize(w, dq=dq)
+    wh = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], d_out, d_in, dq=dq)
+    check_close(bf16_f64(y), O.linear_fwd(wh, a, b, cfg.s, x), f"gemv {t} tokens {d_out}x{d_in}")
+
+
 def test_decode_result_does_not_depend_on_workspace_contents():
     """The decode GEMV keeps nothing from call to call in its workspace: whatever the
     workspace held before (zeros, all ones, random bytes, the previous call's partials),

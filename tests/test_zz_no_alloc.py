@@ -17,9 +17,11 @@ pytestmark = pytest.mark.gpu
 
 # (first call, second smaller call): GEMV one-launch, GEMV two-launch (A x partials in
 # scratch), 2-3 token GEMV, small batch with K-split partials in scratch, and the
-# persistent GEMV of layers with more than 4096 rows (two-launch, then one-launch)
+# persistent GEMV of layers with more than 4096 rows (two-launch, then one-launch; at 1
+# token, and at 2 tokens then 3)
 PAIRS = [
     (WL.custom("k", 8192, 8192, 1, 64), WL.custom("l", 4160, 4096, 1, 16, seed=1)),
+    (WL.custom("m", 8192, 8192, 2, 64), WL.custom("n", 4160, 4096, 3, 16, seed=1)),
     (WL.custom("a", 4096, 4096, 1, 16), WL.custom("b", 1024, 512, 1, 8, seed=1)),
     (WL.custom("c", 2048, 8192, 1, 64), WL.custom("d", 512, 1024, 1, 24, seed=1)),
     (WL.custom("e", 4096, 4096, 64, 16), WL.custom("f", 1024, 2048, 16, 8, seed=1)),
