@@ -158,7 +158,7 @@ int nf4_double_dequant_ex(const uint8_t* codes, const int8_t* qconst, const floa
 
 /* Workspace bytes of qlora_linear_fwd(_ex) and of qlora_linear_bwd_x(_ex) for the given
  * sizes (0 on bad sizes). The forward with d_seq <= 64 streams the packed codes and needs
- * only partial sums (16 KB at d_seq = 1 with r = 16); every other call dequantises W
+ * only partial sums (at most 4 KB at d_seq = 1); every other call dequantises W
  * into the workspace (2 bytes per weight). qlora_linear_workspace_bytes is the larger
  * of the two, enough for either call. */
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
