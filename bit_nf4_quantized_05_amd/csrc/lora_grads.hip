@@ -196,20 +196,45 @@ void lora_grad_mfma(GradArgs g) {
     }
 }
 
+// dB: one output per thread, dB[n, j] at idx = n r + j, its slice partials idx + s d_out r.
+// dA [r, d_in] (n fastest) from partials [S][d_in][r] (j fastest): workgroup b - nbB sums
+// the contiguous partials of 32 columns n (32 r floats per slice, read in order), keeps
+// them in LDS (row pitch r + 1) and writes 32 contiguous columns of each of the r rows
+// of dA. Each output is the same ordered sum over the slices either way.
+constexpr int kRdCols = 32;
+
+// the ordered slice sum with as many loads in flight as there are slices (up to 16): the
+// loads past the last slice would re-read it for nothing
+__device__ __forceinline__ float slice_sum(const float* p, int64_t stride, int n) {
+    if (n <= 4) return ordered_sum<4>(p, stride, n);
+    if (n <= 8) return ordered_sum<8>(p, stride, n);
+    return ordered_sum<16>(p, stride, n);
+}
+
 __global__ __launch_bounds__(256)
 void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __restrict__ partA, int SA,
-                      int64_t d_out, int64_t d_in, int r, float* __restrict__ dA, float* __restrict__ dB) {
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int64_t nB = d_out * r;
-    if (idx < nB) {                                   // dB[n, j], n = idx / r
-        dB[idx] = ordered_sum<16>(partB + idx, nB, SB);
+                      int64_t d_out, int64_t d_in, int r, int nbB, float* __restrict__ dA, float* __restrict__ dB) {
+    extern __shared__ float tile[];                    // kRdCols x (r + 1)
+    const int tid = threadIdx.x;
+    if (static_cast<int>(blockIdx.x) < nbB) {
+        const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + tid;
+        const int64_t nB = d_out * r;
+        if (idx < nB) dB[idx] = slice_sum(partB + idx, nB, SB);
         return;
     }
-    const int64_t k = idx - nB;                       // dA[j, n], n fastest
-    if (k >= d_in * r) return;
-    const int64_t j = k / d_in, n = k % d_in;
+    const int64_t n0 = static_cast<int64_t>(static_cast<int>(blockIdx.x) - nbB) * kRdCols;
+    const int ncol = static_cast<int>(min<int64_t>(kRdCols, d_in - n0));
     const int64_t nA = d_in * r;
-    dA[k] = ordered_sum<16>(partA + n * r + j, nA, SA);
+    const int cnt = ncol * r;
+    for (int e = tid; e < cnt; e += 256) {
+        const int nn = e / r, j = e - nn * r;
+        tile[nn * (r + 1) + j] = slice_sum(partA + n0 * r + e, nA, SA);
+    }
+    __syncthreads();
+    for (int e = tid; e < r * kRdCols; e += 256) {
+        const int j = e / kRdCols, nn = e % kRdCols;
+        if (nn < ncol) dA[static_cast<int64_t>(j) * d_in + n0 + nn] = tile[nn * (r + 1) + j];
+    }
 }
 
 // token slices (multiples of kGK) for N columns: about kGSlices workgroups in all
@@ -255,9 +280,11 @@ hipError_t launch_lora_grads(const uint16_t* X, int64_t ldx, const uint16_t* dY,
     } else {
         QN_LAUNCH("lora_grad_mfma", st, lora_grad_mfma<2>, grid, dim3(256), 0, st, g);
     }
-    const int64_t total = (d_out + d_in) * r;
-    QN_LAUNCH("lora_grad_reduce", st, lora_grad_reduce, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0,
-              st, jB.part, jB.S, jA.part, jA.S, d_out, d_in, r, dA, dB);
+    const int nbB = static_cast<int>((d_out * r + 255) / 256);
+    const int nbA = static_cast<int>((d_in + kRdCols - 1) / kRdCols);
+    QN_LAUNCH("lora_grad_reduce", st, lora_grad_reduce, dim3(static_cast<unsigned>(nbB + nbA)), dim3(256),
+              static_cast<unsigned>(4 * kRdCols * (r + 1)), st, jB.part, jB.S, jA.part, jA.S, d_out, d_in, r, nbB,
+              dA, dB);
     return hipGetLastError();
 }
 
