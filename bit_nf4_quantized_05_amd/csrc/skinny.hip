@@ -224,6 +224,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 // the last split and are masked out), so a chunk costs one memory round trip.
 constexpr int kRdRows = 16;
 
+template <int SPL>   // SPL >= splits loads per output issued at once (clamped)
 __global__ __launch_bounds__(256)
 void skinny_reduce(const float* __restrict__ part, const float* __restrict__ part_a, int splits, float s,
                    int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y,
@@ -236,13 +237,13 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
     const int tid = threadIdx.x;
     const int o0 = static_cast<int>(blockIdx.x) * kRdRows;
     const int npairs = d_seq * kRdRows;
-    float pv[kPairs][kSkSplits];
+    float pv[kPairs][SPL];
 #pragma unroll
     for (int q = 0; q < kPairs; ++q) {
         const int e = min(tid + 256 * q, npairs - 1);
         const int64_t idx = static_cast<int64_t>(e / kRdRows) * d_out + o0 + e % kRdRows;
 #pragma unroll
-        for (int sp = 0; sp < kSkSplits; ++sp)
+        for (int sp = 0; sp < SPL; ++sp)
             pv[q][sp] = part[static_cast<int64_t>(min(sp, splits - 1)) * d_seq * d_out + idx];
     }
     float acc[kPairs];
@@ -263,14 +264,14 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
         for (int e0 = 0; e0 < nt; e0 += 256) {
             const int e = min(e0 + tid, nt - 1);
             const int t = e / nj, j = e % nj;
-            float av[kSkSplits];
+            float av[SPL];
 #pragma unroll
-            for (int sp = 0; sp < kSkSplits; ++sp)
+            for (int sp = 0; sp < SPL; ++sp)
                 av[sp] = part_a[(static_cast<int64_t>(min(sp, splits - 1)) * d_seq + t) * r_pad + j0 + j];
             if (e0 + tid < nt) {
                 float v = 0.0f;
 #pragma unroll
-                for (int sp = 0; sp < kSkSplits; ++sp) v += sp < splits ? av[sp] : 0.0f;
+                for (int sp = 0; sp < SPL; ++sp) v += sp < splits ? av[sp] : 0.0f;
                 s_t[t * kP + j] = __uint_as_float(static_cast<uint32_t>(bf16_bits(s * v)) << 16);
             }
         }
@@ -283,7 +284,7 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
 #pragma unroll
             for (int q = 0; q < kPairs; ++q) {
 #pragma unroll
-                for (int sp = 0; sp < kSkSplits; ++sp) acc[q] += sp < splits ? pv[q][sp] : 0.0f;
+                for (int sp = 0; sp < SPL; ++sp) acc[q] += sp < splits ? pv[q][sp] : 0.0f;
             }
         }
         __syncthreads();
@@ -335,8 +336,15 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
         case 4: QN_LAUNCH("skinny_nf4", st, skinny_nf4<4>, grid, dim3(256), 0, st, a, tab); break;
         default: return hipErrorInvalidValue;
     }
-    QN_LAUNCH("skinny_reduce", st, skinny_reduce, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256), 0, st,
-              part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y, ldy);
+    // as many partial loads per output as there are splits (4 or 8), not 8 at clamped addresses
+    if (a.splits <= 4) {
+        QN_LAUNCH("skinny_reduce", st, skinny_reduce<4>, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256), 0,
+                  st, part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y, ldy);
+    } else {
+        QN_LAUNCH("skinny_reduce", st, skinny_reduce<kSkSplits>, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256),
+                  0, st, part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y,
+                  ldy);
+    }
     return hipGetLastError();
 }
 
