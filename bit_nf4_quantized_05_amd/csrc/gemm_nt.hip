@@ -279,7 +279,9 @@ void gemm_nt_split(GemmArgs g) {
 }
 
 // Split tiles: C[m, n..n+3] = bf16(sum of the tile's partials in split order), 4 outputs
-// per thread; 64 workgroups per tile (4 rows each).
+// per thread; 64 workgroups per tile (4 rows each). SP = the split count (2..4): that
+// many partial loads per thread.
+template <int SP>
 __global__ __launch_bounds__(256)
 void gemm_split_reduce(GemmArgs g) {
     const int j = static_cast<int>(blockIdx.x) / 64;                  // split tile
@@ -291,13 +293,12 @@ void gemm_split_reduce(GemmArgs g) {
     if (m >= g.M || n >= g.N) return;
     const float* p = g.part + static_cast<int64_t>(j) * (BM * BN) + ml * BN + nl;
     const int64_t stride = static_cast<int64_t>(g.rem) * (BM * BN);
-    float4 v[4];
+    float4 v[SP];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) v[s] = *reinterpret_cast<const float4*>(p + min(s, g.splits - 1) * stride);
+    for (int s = 0; s < SP; ++s) v[s] = *reinterpret_cast<const float4*>(p + s * stride);
     float4 t = v[0];
 #pragma unroll
-    for (int s = 1; s < 4; ++s)
-        if (s < g.splits) { t.x += v[s].x; t.y += v[s].y; t.z += v[s].z; t.w += v[s].w; }
+    for (int s = 1; s < SP; ++s) { t.x += v[s].x; t.y += v[s].y; t.z += v[s].z; t.w += v[s].w; }
     *reinterpret_cast<uint2*>(g.C + static_cast<int64_t>(m) * g.ldc + n) =
         uint2{pack_bf16x2(t.x, t.y), pack_bf16x2(t.z, t.w)};
 }
@@ -370,7 +371,10 @@ hipError_t launch_gemm_nt(const uint16_t* P, int64_t ldp, const uint16_t* Q, int
         QN_LAUNCH("gemm_nt_split", st, gemm_nt_split, dim3(g.full + g.rem * g.splits), dim3(64 * kGemmWM * kGemmWN),
                   0, st, g);
     }
-    QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce, dim3(static_cast<unsigned>(g.rem * 64)), dim3(256), 0, st, g);
+    const dim3 rgrid(static_cast<unsigned>(g.rem * 64));
+    if (g.splits == 2) QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce<2>, rgrid, dim3(256), 0, st, g);
+    else if (g.splits == 3) QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce<3>, rgrid, dim3(256), 0, st, g);
+    else QN_LAUNCH("gemm_split_reduce", st, gemm_split_reduce<4>, rgrid, dim3(256), 0, st, g);
     return hipGetLastError();
 }
 
