@@ -15,13 +15,14 @@ namespace {
 // d_seq = 1 (decode), and 2 or 3 tokens. When all of A fits one 4096-column segment
 // with r <= 16 (A <= 128 KB, read from L2 by every workgroup), one launch: each
 // gemv_nf4 workgroup forms s A x itself, wave j the dot product of row j of A with the
-// x segment (of each token) it has staged in LDS anyway. Otherwise (one token only)
-// two launches:
+// x segment (of each token) it has staged in LDS anyway. Otherwise (one token, or two
+// on layers of more than 4096 rows) two launches:
 //   lora_ax_partial: the 64-column blocks of x are split into nparts contiguous
-//     slices (nparts * r <= 1024); workgroup w writes, for every rank row j, the dot
-//     product of A[j] and x over slice w to part[w][j] (fixed summation order).
-//   gemv_nf4: streams the packed codes once and adds B (s A x), summing the slice
-//     partials in a fixed order: y = W_hat x + B (s A x).
+//     slices (nparts * tokens * r <= 1024); workgroup w writes, for every token t and
+//     rank row j, the dot product of A[j] and x_t over slice w to part[w][t][j] (fixed
+//     summation order).
+//   gemv_nf4 / gemv_nf4_persist: streams the packed codes once and adds B (s A x),
+//     summing the slice partials in a fixed order: y = W_hat x + B (s A x).
 // Both are deterministic, and every workgroup forms the same s A x bits.
 // ---------------------------------------------------------------------------
 constexpr int kAxMaxParts = 16;
