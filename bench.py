@@ -210,7 +210,17 @@ def layer_leg(qn, torch, WL, name: str, dev) -> dict:
                      "GBps": round(nbytes / (g_us * 1e-6) / 1e9, 1),
                      "frac_of_hbm_peak": round(nbytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                      "call_us_back_to_back": round(call_us, 2), "kernel_us": dk}
-    del copies, x1, y1, dws
+    # the same with 2 tokens (the persistent GEMV on these layers)
+    x2 = bf16(WL.make_x(cfg)[:2])
+    y2 = torch.empty(2, cfg.d_out, dtype=torch.bfloat16, device=dev)
+    dws2 = torch.empty(max(1, qn.linear_fwd_workspace_bytes(cfg.d_out, cfg.d_in, 2, cfg.r)), dtype=torch.uint8,
+                       device=dev)
+    g2 = graph_call_us(torch, lambda: [qn.linear_fwd(c, A, B, cfg.s, x2, out=y2, workspace=dws2) for c in copies],
+                       ncopy, max(1, 128 // ncopy))
+    nb2 = decode_bytes(cfg, d_seq=2)
+    out["decode"]["two_tokens"] = {"call_us_graph_replay": round(g2, 3), "bytes_per_call": nb2,
+                                   "GBps": round(nb2 / (g2 * 1e-6) / 1e9, 1)}
+    del copies, x1, y1, dws, x2, y2, dws2
     torch.cuda.empty_cache()
     return out
 
