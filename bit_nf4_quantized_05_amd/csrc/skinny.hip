@@ -5,17 +5,21 @@
 // (0.516 B per weight) dominates, so the packed codes are read once and dequantised
 // in registers straight into MFMA operands; nothing is written back but Y.
 //
-// skinny_nf4: a workgroup takes 64 rows of W (16 per wave) and K-slices of 8 blocks
-// (512 weights) s = split, split + splits, ...; the splits are summed by the second
-// kernel. ceil(r / 64) more row blocks take the rows of A instead (bf16, loaded as
-// they are), so the same launch also forms the K-split partials of A x. Per slice, the x slice of every token (zero past d_seq) is staged in LDS
-// with its 16-byte chunks XOR-swizzled by the token index, and a_hat of the 64 rows
-// x 8 blocks is formed once into LDS. Per 128-weight pair of blocks, lane l of a wave
-// (row i = l % 16, k-group g = l / 16) loads 16 code bytes = weights [128 p + 32 g,
-// +32) of its row (one 16-byte load; the k order inside the pair is permuted, and the
-// x fragments follow the same permutation), forms bf16(c[code] * a_hat) exactly as the
-// dequantiser does, and feeds v_mfma_f32_16x16x32_bf16 with one 16-token tile of x as
-// the other operand (up to 4 tiles).
+// skinny_nf4: a workgroup takes 64 rows of W and K-slices of 8 blocks (512 weights)
+// s = split, split + splits, ...; the splits are summed by the second kernel.
+// ceil(r / 64) more row blocks take the rows of A instead (bf16, loaded as they are),
+// so the same launch also forms the K-split partials of A x. The 64 rows are 4 groups
+// of 16, each taken by two waves: of a slice's four 128-weight block pairs, wave kq of
+// the group takes pairs kq and kq + 2 (two waves per SIMD where one workgroup fills a
+// CU); at the end the second wave's accumulators are added to the first's through LDS.
+// Per slice, the x slice of every token (zero past d_seq) is staged in LDS with its
+// 16-byte chunks XOR-swizzled by the token index, and a_hat of the 64 rows x 8 blocks
+// is formed once into LDS. Per block pair p, lane l of a wave (row i = l % 16, k-group
+// g = l / 16) loads 16 code bytes = weights [128 p + 32 g, +32) of its row (one 16-byte
+// load; the k order inside the pair is permuted, and the x fragments follow the same
+// permutation), forms bf16(c[code] * a_hat) exactly as the dequantiser does, and feeds
+// v_mfma_f32_16x16x32_bf16 with one 16-token tile of x as the other operand (up to 4
+// tiles).
 // skinny_reduce: per 16 rows, adds the split partials in order; forms T' = bf16(s A x)
 // from the A x partials (in split order, as the large-batch pre-pass rounds it) and
 // adds the rank-r term T' B^T (both staged in LDS); rounds to bf16.
@@ -32,7 +36,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSkRows = 64;         // rows of W per workgroup (16 per wave)
+constexpr int kSkRows = 64;         // rows of W per workgroup (4 groups of 16)
+constexpr int kSkKq = 2;            // waves per 16-row group (they split each slice's block pairs)
+constexpr int kSkThreads = 64 * 4 * kSkKq;
 constexpr int kSkBlk = 8;           // 64-weight blocks per K-slice
 constexpr int kSkTok = 64;          // tokens at most
 constexpr int kSkSplits = 8;        // K-split partials at most
@@ -62,25 +68,31 @@ __device__ __forceinline__ void mma(f32x4 (&acc)[TT], const uint4* xs, const uin
 }
 
 template <int TT>   // 16-token tiles
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(kSkThreads)
 void skinny_nf4(SkArgs a, NF4Tables tab) {
+    constexpr int KQ = kSkKq;
+    constexpr int NW = 4 * KQ;                     // waves
+    constexpr int NT = 64 * NW;                    // threads
+    constexpr int PP = kSkBlk / 2 / KQ;            // block pairs per wave and slice
     __shared__ uint4 xs[TT * 16 * kSkBlk * 8];     // [token][64 chunks of 8 weights], swizzled
     __shared__ float s_code[16 * 64];              // code book, copy per lane (conflict-free lookups)
     __shared__ float s_ahat[kSkRows * kSkBlk];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave & 3;                       // 16-row group
+    const int kq = wave >> 2;                      // block pairs kq, kq + KQ, ... of each slice
     const int row_blocks = a.d_out / kSkRows;
     const int all_blocks = row_blocks + (a.r + kSkRows - 1) / kSkRows;
     const int rb = static_cast<int>(blockIdx.x) % all_blocks;
     const int sp = static_cast<int>(blockIdx.x) / all_blocks;
     const bool lora = rb >= row_blocks;            // workgroup-uniform: rows of A
-    const int ra = (rb - row_blocks) * kSkRows + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * 16 + (threadIdx.x & 15);
+    const int ra = (rb - row_blocks) * kSkRows + rg * 16 + (threadIdx.x & 15);
     const int nb = a.d_in / 64;
     const int nslices = (nb + kSkBlk - 1) / kSkBlk;
-    const int i = lane & 15;                       // row within the wave / token within a tile
+    const int i = lane & 15;                       // row within the group / token within a tile
     const int g = lane >> 4;                       // k-group
-    const int o = lora ? 0 : rb * kSkRows + wave * 16 + i;
+    const int o = lora ? 0 : rb * kSkRows + rg * 16 + i;
     const int64_t row_u = static_cast<int64_t>(o) * (a.d_in / 32);   // 16-byte code words per row
     const uint4* arow = reinterpret_cast<const uint4*>(a.A + static_cast<int64_t>(lora ? min(ra, a.r - 1) : 0) * a.d_in);
     const bool aok = lora && ra < a.r;
@@ -91,7 +103,7 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
     const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
     {
         // code book from the (scalar) kernel arguments by selects
-        for (int e = tid; e < 16 * 64; e += 256) {
+        for (int e = tid; e < 16 * 64; e += NT) {
             const int c = e >> 6;
             float v = tab.code[0];
 #pragma unroll
@@ -108,12 +120,12 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
     // row of 1 KB per wave instruction, lane l writing slot l = chunk l ^ (token % 16).
     // The addresses are clamped into X: a token past d_seq only feeds an output column
     // that is never stored, a chunk past the row meets zero weights.
-    constexpr int kXRows = TT * 16 / 4;            // token rows per wave
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int kXRows = TT * 16 / NW;           // token rows per wave
+    static_assert(kXRows * NW == TT * 16, "token rows split evenly over the waves");
     auto stage_x = [&](int b0, int nbk) {
 #pragma unroll
         for (int j = 0; j < kXRows; ++j) {
-            const int tok = wv + 4 * j;
+            const int tok = wave + NW * j;
             const int c = min(lane ^ (tok & 15), nbk * 8 - 1);
             load_lds16(x4 + (static_cast<int64_t>(min(tok, a.d_seq - 1)) * a.ldx + b0 * 64) / 8 + c, xs + tok * 64);
         }
@@ -126,22 +138,24 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             const int nbk = min(kSkBlk, nb - b0);
             __syncthreads();                         // the previous slice's readers are done
             stage_x(b0, nbk);
-            uint4 aw[kSkBlk / 2][4];
+            uint4 aw[PP][4];
 #pragma unroll
-            for (int p = 0; p < kSkBlk / 2; ++p) {
+            for (int pp = 0; pp < PP; ++pp) {
+                const int p = kq + KQ * pp;
                 const int bl = 2 * p + (g >> 1);
                 const int64_t e0 = static_cast<int64_t>(b0 + min(bl, nbk - 1)) * 64 + 32 * (g & 1);   // clamped
 #pragma unroll
-                for (int st = 0; st < 4; ++st) aw[p][st] = arow[e0 / 8 + st];
+                for (int st = 0; st < 4; ++st) aw[pp][st] = arow[e0 / 8 + st];
             }
-            QN_WAIT_VM(kSkBlk * 2);                  // this wave's x rows have landed (A words may be in flight)
+            QN_WAIT_VM(PP * 4);                      // this wave's x rows have landed (A words may be in flight)
             __syncthreads();
 #pragma unroll
-            for (int p = 0; p < kSkBlk / 2; ++p) {
+            for (int pp = 0; pp < PP; ++pp) {
+                const int p = kq + KQ * pp;
                 if (2 * p >= nbk) break;
                 const bool ok = aok && 2 * p + (g >> 1) < nbk;
 #pragma unroll
-                for (int st = 0; st < 4; ++st) mma<TT>(acc, xs, ok ? aw[p][st] : uint4{0, 0, 0, 0}, 16 * p + 4 * g + st, i);
+                for (int st = 0; st < 4; ++st) mma<TT>(acc, xs, ok ? aw[pp][st] : uint4{0, 0, 0, 0}, 16 * p + 4 * g + st, i);
             }
         }
     } else {
@@ -151,32 +165,36 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             // x rows and block constants first, then this wave's code words
             __syncthreads();                         // the previous slice's readers are done
             stage_x(b0, nbk);
-            int8_t qv[2];
-            float sv[2];
+            constexpr int kCq = (kSkRows * kSkBlk + NT - 1) / NT;
+            int8_t qv[kCq];
+            float sv[kCq];
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int e = tid + 256 * q;        // (row e / 8, block e % 8) of the workgroup's rows
+            for (int q = 0; q < kCq; ++q) {
+                const int e = min(tid + NT * q, kSkRows * kSkBlk - 1);   // (row e / 8, block e % 8) of the rows
                 const int64_t blk = static_cast<int64_t>(rb * kSkRows + (e >> 3)) * nb + b0 + min(e & 7, nbk - 1);
                 qv[q] = a.bc.q[blk];
                 sv[q] = a.bc.scale[blk >> a.bc.gshift];
             }
-            uint4 cw[kSkBlk / 2];
+            uint4 cw[PP];
 #pragma unroll
-            for (int p = 0; p < kSkBlk / 2; ++p) {
-                const int bl = 2 * p + (g >> 1);     // block of this lane's 32 weights
+            for (int pp = 0; pp < PP; ++pp) {
+                const int p = kq + KQ * pp;
+                const int bl = 2 * p + (g >> 1);
                 const int word = (b0 + min(bl, nbk - 1)) * 2 + (g & 1);   // clamped into the row
-                cw[p] = codes4[row_u + word];
+                cw[pp] = codes4[row_u + word];
             }
-            QN_WAIT_VM(kSkBlk / 2);                  // x rows and block constants in (code words may not be)
+            QN_WAIT_VM(PP);                          // x rows and block constants in (code words may not be)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) s_ahat[tid + 256 * q] = block_constant(a.bc.fmt, qv[q], sv[q], mu);
+            for (int q = 0; q < kCq; ++q)
+                if (tid + NT * q < kSkRows * kSkBlk) s_ahat[tid + NT * q] = block_constant(a.bc.fmt, qv[q], sv[q], mu);
             __syncthreads();
 #pragma unroll
-            for (int p = 0; p < kSkBlk / 2; ++p) {
+            for (int pp = 0; pp < PP; ++pp) {
+                const int p = kq + KQ * pp;
                 const int bl = 2 * p + (g >> 1);
                 if (2 * p >= nbk) break;              // uniform: no block of this pair exists
-                const float ah = bl < nbk ? s_ahat[(wave * 16 + i) * kSkBlk + bl] : 0.0f;
-                const uint32_t words[4] = {cw[p].x, cw[p].y, cw[p].z, cw[p].w};
+                const float ah = bl < nbk ? s_ahat[(rg * 16 + i) * kSkBlk + bl] : 0.0f;
+                const uint32_t words[4] = {cw[pp].x, cw[pp].y, cw[pp].z, cw[pp].w};
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
                     // weight 2b + h of the word is nibble h of byte b: the lane's copy of code
@@ -197,6 +215,26 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
             }
         }
     }
+    {
+        // the KQ waves of a row group add their accumulators in kq order through LDS
+        // (the x buffer, free once every wave is past its last MFMA)
+        static_assert((KQ - 1) * 4 * TT * 64 <= TT * 16 * kSkBlk * 8, "reduction fits the x buffer");
+        f32x4* red = reinterpret_cast<f32x4*>(xs);
+        __syncthreads();
+        if (kq > 0) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) red[(((kq - 1) * 4 + rg) * TT + t) * 64 + lane] = acc[t];
+        }
+        __syncthreads();
+        if (kq > 0) return;
+#pragma unroll
+        for (int q = 1; q < KQ; ++q)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const f32x4 v = red[(((q - 1) * 4 + rg) * TT + t) * 64 + lane];
+                acc[t] = acc[t] + v;
+            }
+    }
     // D of a 16x16 tile: lane l holds rows 4 (l / 16) + v of column l % 16
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -205,10 +243,10 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if (lora) {
-                    const int j = (rb - row_blocks) * kSkRows + wave * 16 + 4 * g + v;
+                    const int j = (rb - row_blocks) * kSkRows + rg * 16 + 4 * g + v;
                     if (j < a.r_pad) a.part_a[(static_cast<int64_t>(sp) * a.d_seq + tok) * a.r_pad + j] = acc[t][v];
                 } else {
-                    const int orow = rb * kSkRows + wave * 16 + 4 * g + v;
+                    const int orow = rb * kSkRows + rg * 16 + 4 * g + v;
                     a.part[(static_cast<int64_t>(sp) * a.d_seq + tok) * a.d_out + orow] = acc[t][v];
                 }
             }
@@ -330,10 +368,10 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
     const dim3 grid(static_cast<unsigned>(blocks * a.splits));
     const NF4Tables& tab = tables();
     switch ((d_seq + 15) / 16) {
-        case 1: QN_LAUNCH("skinny_nf4", st, skinny_nf4<1>, grid, dim3(256), 0, st, a, tab); break;
-        case 2: QN_LAUNCH("skinny_nf4", st, skinny_nf4<2>, grid, dim3(256), 0, st, a, tab); break;
-        case 3: QN_LAUNCH("skinny_nf4", st, skinny_nf4<3>, grid, dim3(256), 0, st, a, tab); break;
-        case 4: QN_LAUNCH("skinny_nf4", st, skinny_nf4<4>, grid, dim3(256), 0, st, a, tab); break;
+        case 1: QN_LAUNCH("skinny_nf4", st, skinny_nf4<1>, grid, dim3(kSkThreads), 0, st, a, tab); break;
+        case 2: QN_LAUNCH("skinny_nf4", st, skinny_nf4<2>, grid, dim3(kSkThreads), 0, st, a, tab); break;
+        case 3: QN_LAUNCH("skinny_nf4", st, skinny_nf4<3>, grid, dim3(kSkThreads), 0, st, a, tab); break;
+        case 4: QN_LAUNCH("skinny_nf4", st, skinny_nf4<4>, grid, dim3(kSkThreads), 0, st, a, tab); break;
         default: return hipErrorInvalidValue;
     }
     // as many partial loads per output as there are splits (4 or 8), not 8 at clamped addresses
