@@ -432,7 +432,10 @@ void prologue_kernel(PrologueArgs a, NF4Tables tab) {
 // (cols <= 256, ld_dst % 8 == 0, src 16-byte aligned). A workgroup takes 64 source rows,
 // one contiguous span of 64 cols elements starting 128 cols bytes into src, so 16-byte
 // aligned: it is read with 16-byte loads (all issued before any is used) into LDS, then
-// written as cols destination segments of 64 elements, 16 bytes per thread.
+// written as cols destination segments of 64 elements, 16 bytes per thread. When cols is
+// a multiple of 8, a 16-byte piece lies within one source row and goes to LDS as it is
+// (row pitch cols + 8 elements keeps the pieces 16-byte aligned); otherwise element by
+// element.
 constexpr int kTpRows = 64;
 constexpr int kTpMaxCols = 256;
 constexpr int kTpPer = kTpRows * kTpMaxCols / 8 / 256;      // 16-byte pieces per thread at most
@@ -440,7 +443,7 @@ constexpr int kTpPer = kTpRows * kTpMaxCols / 8 / 256;      // 16-byte pieces pe
 __global__ __launch_bounds__(256)
 void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_t cols,
                           uint16_t* __restrict__ dst, int64_t ld_dst) {
-    __shared__ uint16_t t[kTpRows * (kTpMaxCols + 2)];
+    __shared__ __align__(16) uint16_t t[kTpRows * (kTpMaxCols + 8)];
     const int tid = threadIdx.x;
     const int nc = static_cast<int>(cols);
     const int pitch = nc + 2;
@@ -448,6 +451,43 @@ void transpose_pad_kernel(const uint16_t* __restrict__ src, int64_t rows, int64_
     const int nrow = static_cast<int>(std::min<int64_t>(kTpRows, std::max<int64_t>(0, rows - i0)));
     const int total = nrow * nc;                                  // elements of the span
     const uint16_t* sp = src + i0 * cols;
+    if (nc % 8 == 0) {
+        const int cpr = nc / 8;                                   // pieces per source row
+        const int tpitch = nc + 8;
+        uint4 v[kTpPer];
+#pragma unroll
+        for (int k = 0; k < kTpPer; ++k) {
+            const int e0 = 8 * (tid + 256 * k);
+            v[k] = e0 < total ? *reinterpret_cast<const uint4*>(sp + e0) : uint4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int k = 0; k < kTpPer; ++k) {
+            const int p = tid + 256 * k;
+            if (8 * p < total) {
+                const int row = p / cpr, c8 = p - row * cpr;
+                *reinterpret_cast<uint4*>(&t[row * tpitch + 8 * c8]) = v[k];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kTpPer; ++k) {
+            const int p = tid + 256 * k;
+            const int j = p >> 3, q8 = 8 * (p & 7);
+            if (j < nc && i0 + q8 < ld_dst) {
+                uint32_t w[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const int a = q8 + 2 * h, b = a + 1;
+                    const uint32_t lo = a < nrow ? t[a * tpitch + j] : 0u;
+                    const uint32_t hi = b < nrow ? t[b * tpitch + j] : 0u;
+                    w[h] = lo | (hi << 16);
+                }
+                *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(j) * ld_dst + i0 + q8) =
+                    uint4{w[0], w[1], w[2], w[3]};
+            }
+        }
+        return;
+    }
     uint4 v[kTpPer];
 #pragma unroll
     for (int k = 0; k < kTpPer; ++k) {
