@@ -198,10 +198,11 @@ void lora_grad_mfma(GradArgs g) {
 
 // dB: one output per thread, dB[n, j] at idx = n r + j, its slice partials idx + s d_out r.
 // dA [r, d_in] (n fastest) from partials [S][d_in][r] (j fastest): workgroup b - nbB sums
-// the contiguous partials of 32 columns n (32 r floats per slice, read in order), keeps
-// them in LDS (row pitch r + 1) and writes 32 contiguous columns of each of the r rows
-// of dA. Each output is the same ordered sum over the slices either way.
-constexpr int kRdCols = 32;
+// the contiguous partials of c = rd_cols(r) columns n (c r <= 256 floats per slice, read
+// in order; one output per thread, so every thread's slice loads go out together),
+// keeps them in LDS (row pitch r + 1) and writes c contiguous columns of each of the r
+// rows of dA. Each output is the same ordered sum over the slices either way.
+int rd_cols(int r) { return std::max(1, std::min(32, 256 / r)); }
 
 // the ordered slice sum with as many loads in flight as there are slices (up to 16): the
 // loads past the last slice would re-read it for nothing
@@ -213,8 +214,9 @@ __device__ __forceinline__ float slice_sum(const float* p, int64_t stride, int n
 
 __global__ __launch_bounds__(256)
 void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __restrict__ partA, int SA,
-                      int64_t d_out, int64_t d_in, int r, int nbB, float* __restrict__ dA, float* __restrict__ dB) {
-    extern __shared__ float tile[];                    // kRdCols x (r + 1)
+                      int64_t d_out, int64_t d_in, int r, int cols, int nbB, float* __restrict__ dA,
+                      float* __restrict__ dB) {
+    extern __shared__ float tile[];                    // cols x (r + 1)
     const int tid = threadIdx.x;
     if (static_cast<int>(blockIdx.x) < nbB) {
         const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + tid;
@@ -222,8 +224,8 @@ void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __re
         if (idx < nB) dB[idx] = slice_sum(partB + idx, nB, SB);
         return;
     }
-    const int64_t n0 = static_cast<int64_t>(static_cast<int>(blockIdx.x) - nbB) * kRdCols;
-    const int ncol = static_cast<int>(min<int64_t>(kRdCols, d_in - n0));
+    const int64_t n0 = static_cast<int64_t>(static_cast<int>(blockIdx.x) - nbB) * cols;
+    const int ncol = static_cast<int>(min<int64_t>(cols, d_in - n0));
     const int64_t nA = d_in * r;
     const int cnt = ncol * r;
     for (int e = tid; e < cnt; e += 256) {
@@ -231,8 +233,8 @@ void lora_grad_reduce(const float* __restrict__ partB, int SB, const float* __re
         tile[nn * (r + 1) + j] = slice_sum(partA + n0 * r + e, nA, SA);
     }
     __syncthreads();
-    for (int e = tid; e < r * kRdCols; e += 256) {
-        const int j = e / kRdCols, nn = e % kRdCols;
+    for (int e = tid; e < r * cols; e += 256) {
+        const int j = e / cols, nn = e % cols;
         if (nn < ncol) dA[static_cast<int64_t>(j) * d_in + n0 + nn] = tile[nn * (r + 1) + j];
     }
 }
@@ -281,9 +283,10 @@ hipError_t launch_lora_grads(const uint16_t* X, int64_t ldx, const uint16_t* dY,
         QN_LAUNCH("lora_grad_mfma", st, lora_grad_mfma<2>, grid, dim3(256), 0, st, g);
     }
     const int nbB = static_cast<int>((d_out * r + 255) / 256);
-    const int nbA = static_cast<int>((d_in + kRdCols - 1) / kRdCols);
+    const int cols = rd_cols(r);
+    const int nbA = static_cast<int>((d_in + cols - 1) / cols);
     QN_LAUNCH("lora_grad_reduce", st, lora_grad_reduce, dim3(static_cast<unsigned>(nbB + nbA)), dim3(256),
-              static_cast<unsigned>(4 * kRdCols * (r + 1)), st, jB.part, jB.S, jA.part, jA.S, d_out, d_in, r, nbB,
+              static_cast<unsigned>(4 * cols * (r + 1)), st, jB.part, jB.S, jA.part, jA.S, d_out, d_in, r, cols, nbB,
               dA, dB);
     return hipGetLastError();
 }
