@@ -257,12 +257,15 @@ void skinny_nf4(SkArgs a, NF4Tables tab) {
 // Y[t, o] = bf16( sum_split part + sum_j T'[t, j] B[o, j] ) for kRdRows rows o per
 // workgroup, T'[t, j] = bf16(s * sum_split part_a). Thread tid takes the (token, row)
 // pairs tid + 256 q; the rank sums go through LDS in chunks of 64 rank entries (rows
-// of odd pitch, so a row of B and a row of T' fall in different banks). Every load of
-// a chunk is issued before any of them is used (split indices past `splits` re-read
-// the last split and are masked out), so a chunk costs one memory round trip.
+// of odd pitch, so a row of B and a row of T' fall in different banks), added chunk by
+// chunk, and the ordered split sum is added to them last. Every load of a chunk is
+// issued before any of them is used (split indices past `splits` re-read the last
+// split and are masked out), and the split partials' loads go out first and are not
+// waited for before the first chunk's, so r <= 64 costs one memory round trip.
 constexpr int kRdRows = 16;
 
-template <int SPL>   // SPL >= splits loads per output issued at once (clamped)
+// SPL >= splits loads per output issued at once (clamped); kOne: r <= 64 (one chunk)
+template <int SPL, bool kOne>
 __global__ __launch_bounds__(256)
 void skinny_reduce(const float* __restrict__ part, const float* __restrict__ part_a, int splits, float s,
                    int r_pad, const uint16_t* __restrict__ B, int r, int d_out, int d_seq, uint16_t* __restrict__ Y,
@@ -284,10 +287,15 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
         for (int sp = 0; sp < SPL; ++sp)
             pv[q][sp] = part[static_cast<int64_t>(min(sp, splits - 1)) * d_seq * d_out + idx];
     }
-    float acc[kPairs];
+    // the rank term of each output, chunk by chunk; the split partials are added after
+    // it, so that no wait for them stands between their loads and the chunks' loads
+    float lacc[kPairs];
 #pragma unroll
-    for (int q = 0; q < kPairs; ++q) acc[q] = 0.0f;
-    for (int j0 = 0; j0 < r; j0 += kJ) {
+    for (int q = 0; q < kPairs; ++q) lacc[q] = 0.0f;
+    // one chunk (r <= 64) runs as straight-line code (its own instantiation): in a loop the
+    // compiler waits for every load in flight (the split partials too) where the loop starts,
+    // since the chunk's B loads write the same registers on each pass
+    auto chunk = [&](int j0) {
         const int nj = min(kJ, r - j0);
         // this chunk's loads: kBPer entries of B, then one (token, rank) entry of T' per
         // pass (all splits); the sums follow once they are in flight
@@ -318,13 +326,6 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
             const int e = tid + 256 * i;
             if (e < kRdRows * nj) s_b[(e / nj) * kP + e % nj] = __uint_as_float(static_cast<uint32_t>(bv[i]) << 16);
         }
-        if (j0 == 0) {
-#pragma unroll
-            for (int q = 0; q < kPairs; ++q) {
-#pragma unroll
-                for (int sp = 0; sp < SPL; ++sp) acc[q] += sp < splits ? pv[q][sp] : 0.0f;
-            }
-        }
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < kPairs; ++q) {
@@ -333,14 +334,24 @@ void skinny_reduce(const float* __restrict__ part, const float* __restrict__ par
                 const int t = e / kRdRows, ro = e % kRdRows;
                 float l = 0.0f;
                 for (int j = 0; j < nj; ++j) l += s_t[t * kP + j] * s_b[ro * kP + j];
-                acc[q] += l;
+                lacc[q] = j0 == 0 ? l : lacc[q] + l;
             }
         }
+    };
+    if constexpr (kOne) {
+        chunk(0);
+    } else {
+        for (int j0 = 0; j0 < r; j0 += kJ) chunk(j0);
     }
 #pragma unroll
     for (int q = 0; q < kPairs; ++q) {
         const int e = tid + 256 * q;
-        if (e < npairs) Y[static_cast<int64_t>(e / kRdRows) * ldy + o0 + e % kRdRows] = bf16_bits(acc[q]);
+        if (e < npairs) {
+            float d = 0.0f;
+#pragma unroll
+            for (int sp = 0; sp < SPL; ++sp) d += sp < splits ? pv[q][sp] : 0.0f;
+            Y[static_cast<int64_t>(e / kRdRows) * ldy + o0 + e % kRdRows] = bf16_bits(d + lacc[q]);
+        }
     }
 }
 
@@ -375,14 +386,17 @@ hipError_t launch_skinny_nf4(const uint8_t* codes, const BlockConsts& bc, int64_
         default: return hipErrorInvalidValue;
     }
     // as many partial loads per output as there are splits (4 or 8), not 8 at clamped addresses
+    const dim3 rgrid(static_cast<unsigned>(d_out / kRdRows));
+    const int o = static_cast<int>(d_out), t = static_cast<int>(d_seq);
+#define QN_RED(SPL, ONE) \
+    QN_LAUNCH("skinny_reduce", st, (skinny_reduce<SPL, ONE>), rgrid, dim3(256), 0, st, part, part_a, a.splits, s, \
+              r_pad, B, r, o, t, Y, ldy)
     if (a.splits <= 4) {
-        QN_LAUNCH("skinny_reduce", st, skinny_reduce<4>, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256), 0,
-                  st, part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y, ldy);
+        if (r <= 64) QN_RED(4, true); else QN_RED(4, false);
     } else {
-        QN_LAUNCH("skinny_reduce", st, skinny_reduce<kSkSplits>, dim3(static_cast<unsigned>(d_out / kRdRows)), dim3(256),
-                  0, st, part, part_a, a.splits, s, r_pad, B, r, static_cast<int>(d_out), static_cast<int>(d_seq), Y,
-                  ldy);
+        if (r <= 64) QN_RED(kSkSplits, true); else QN_RED(kSkSplits, false);
     }
+#undef QN_RED
     return hipGetLastError();
 }
 
