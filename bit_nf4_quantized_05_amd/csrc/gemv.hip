@@ -394,8 +394,12 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 // as gemv_nf4_kernel<1, kAx>, but one workgroup per CU walks many rows. Wave w of
 // workgroup b takes rows g * 16 + w for the row groups g = b, b + grid, ...; a row is
 // one unit per 4096-weight segment, and the loads of a wave's next unit (its code
-// words, block constants, and on a row's last segment its row of B) go out before the
-// current unit is computed, so a wave keeps two units in flight without any barrier.
+// words, block constants and its row of B) go out before the current unit is computed,
+// so a wave keeps two units in flight without any barrier. Every unit issues the same
+// loads (B on every segment, the unit past the last one re-issued clamped, the
+// block-constant select without a branch, mu by a scalar load), so the compiler waits
+// for the current unit's loads only: with a load count that depended on the path, it
+// had waited for all loads in flight (the next unit's too) before computing.
 // x (d_in <= kGvXMax) is staged in LDS whole, once, with the tables and s (A x), which
 // the one-launch form (r <= 16, d_in <= 4096) forms once per workgroup. Each row's
 // sums run in the order of gemv_nf4_kernel, so the outputs are the same bits. With one
@@ -410,7 +414,7 @@ struct GvUnit {
     uint4 cw[2];            // code words of the two chunks
     int8_t qv;              // second-level code of block l
     float sv;               // its group scale (a_j without a second level)
-    uint16_t bw[4];         // B[row, lane + 64 i] on a row's last segment (clamped, masked at use)
+    uint16_t bw[4];         // B[row, lane + 64 i] (clamped; used on a row's last segment, masked)
 };
 
 // T = 1, 2 or 3 tokens (x and y rows at strides ldx, ldy): each code-pair lookup serves
@@ -422,6 +426,7 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
                       const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ B, int r, float s,
                       const float* __restrict__ part, int nparts, const uint16_t* __restrict__ A,
                       uint16_t* __restrict__ y, int64_t ldy, NF4Tables tab) {
+    constexpr int kBw = kAx ? 1 : 4;              // 64-entry pieces of a row of B (r <= 16 in the one-launch form)
     constexpr int kX = T == 1 ? kGvXMax : kGvXMaxT;
     constexpr int kXPer = kX / 8 / 1024;          // 16-byte x chunks per thread and token
     __shared__ uint4 lut4[256 * kLutCopies / 4];
@@ -474,10 +479,8 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             const int col = S * kGvSeg + h * 2048 + lane * 32;
             k.cw[h] = codes[row_u + (col < d_in ? col / 32 : 0)];
         }
-        if (S == nseg - 1) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) k.bw[i] = B[static_cast<int64_t>(row) * r + min(lane + 64 * i, r - 1)];
-        }
+        for (int i = 0; i < kBw; ++i) k.bw[i] = B[static_cast<int64_t>(row) * r + min(lane + 64 * i, r - 1)];
     };
     // the first unit's loads: right behind x in the two-launch form, after the first
     // barrier when the workgroup also fetches the rows of A (as in gemv_nf4_kernel)
@@ -551,19 +554,22 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
 
     const char* lut = reinterpret_cast<const char*>(lut4);
     const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
-    const float mu = bc.mean[0];
+    typedef const __attribute__((address_space(4))) float cfloat;   // a scalar load
+    const float mu = *(cfloat*)(bc.mean);
     float acc[T];
 #pragma unroll
     for (int k = 0; k < T; ++k) acc[k] = 0.0f;
-    auto unit = [&](const GvUnit& cur, GvUnit& nxt, int u) {
-        if (u + 1 < nunits) {
-            unit_issue(nxt, u + 1);
+    auto unit = [&](const GvUnit& cur, GvUnit& nxt, int u, bool issue) {
+        if (issue) {
+            unit_issue(nxt, min(u + 1, nunits - 1));
             __builtin_amdgcn_sched_barrier(0);
         }
         const int gi = u / nseg;
         const int S = u - gi * nseg;
         const bool bok = S * 64 + lane < nbpr;
-        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? cur.sv : mu + cur.sv * qlut[cur.qv + 128];
+        const float qstep = qlut[cur.qv + 128];
+        const float ah_dq = mu + cur.sv * qstep;
+        const float ah = !bok ? 0.0f : bc.fmt == kDqNone ? cur.sv : ah_dq;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const float a = __shfl(ah, h * 32 + (lane >> 1));
@@ -604,7 +610,7 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             for (int k = 0; k < T; ++k) {
                 float v = acc[k];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < kBw; ++i) {
                     const int j = lane + 64 * i;
                     if (j < r) v += bf16_to_f32(cur.bw[i]) * s_t[(kAx ? 16 : r) * k + j];
                 }
@@ -615,9 +621,20 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             }
         }
     };
-    for (int u = 0; u < nunits; u += 2) {
-        unit(g0, g1, u);
-        if (u + 1 < nunits) unit(g1, g0, u + 1);
+    // three tokens keep the loop with path-dependent issue (two units' registers in
+    // flight there would exceed the 128 a lane has at 16 waves per CU)
+    if constexpr (T <= 2) {
+        int u = 0;
+        for (; u + 1 < nunits; u += 2) {
+            unit(g0, g1, u, true);
+            unit(g1, g0, u + 1, true);
+        }
+        if (u < nunits) unit(g0, g1, u, false);
+    } else {
+        for (int u = 0; u < nunits; u += 2) {
+            unit(g0, g1, u, u + 1 < nunits);
+            if (u + 1 < nunits) unit(g1, g0, u + 1, u + 2 < nunits);
+        }
     }
 }
 
