@@ -341,11 +341,11 @@ def tile_rounds_leg(qn, torch, WL, dev, reps: int = 5) -> dict:
                              device=dev)
             us, k = timed_calls(qn, torch, lambda i: qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws), reps)
             plan = gemm_plan(cfg.d_seq, d_out, d_in, 64)
-            main = sum(v for n, v in k.items() if n in ("gemm_nt_kernel", "gemm_nt_split"))
+            gemm_us = sum(v for n, v in k.items() if n in ("gemm_nt_kernel", "gemm_nt_split"))
             red = k.get("gemm_split_reduce", 0.0)
-            out[f"{d_out}x{d_in}"] = dict(plan, gemm_us=round(main, 2), reduce_us=round(red, 2),
-                                         us_per_critical_step=round(main / plan["critical_steps"], 3),
-                                         gemm_TFLOPs=round(cfg.fwd_flops() / ((main + red) * 1e-6) / 1e12, 1),
+            out[f"{d_out}x{d_in}"] = dict(plan, gemm_us=round(gemm_us, 2), reduce_us=round(red, 2),
+                                         us_per_critical_step=round(gemm_us / plan["critical_steps"], 3),
+                                         gemm_TFLOPs=round(cfg.fwd_flops() / ((gemm_us + red) * 1e-6) / 1e12, 1),
                                          call_us=round(us, 2))
             del q, A, B, X, Y, ws
             torch.cuda.empty_cache()
@@ -645,7 +645,7 @@ def main():
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    graph_call_us = 1e3 * e0.elapsed_time(e1) / (g_reps * len(copies))
+    dec_graph_us = 1e3 * e0.elapsed_time(e1) / (g_reps * len(copies))
     del graph
 
     # the floor of this access pattern on this machine: the decode kernel's own loads
@@ -661,9 +661,9 @@ def main():
     # value: GPU time per call from the graph replay (HIP events around many calls on the
     # launch stream, gaps between launches included); per-kernel events add about 2.5 us
     # of their own to a launch this short and are reported beside it
-    d_gbps = nbytes / (graph_call_us * 1e-6) / 1e9
+    d_gbps = nbytes / (dec_graph_us * 1e-6) / 1e9
     decode = {"metric": "effective GB/s (d_seq=1)", "value": round(d_gbps, 1),
-              "unit": "GB/s", "bytes_per_call": nbytes, "call_us_graph_replay": round(graph_call_us, 3),
+              "unit": "GB/s", "bytes_per_call": nbytes, "call_us_graph_replay": round(dec_graph_us, 3),
               "kernel_us_events": round(kern_us, 3), "gemv_kernel_us_events": round(1e3 * gv_ms / gv_n, 3),
               "call_us_back_to_back": round(1e6 * d_elapsed / args.decode_iters, 3),
               "copies": len(copies),
@@ -672,7 +672,7 @@ def main():
                            "unit": "GB/s", "frac": round(d_gbps / PEAK_HBM_GBPS, 4),
                            "traffic": measured_traffic(DECODE_TRAFFIC),
                            "floor_call_us": floor["code_stream_us"],
-                           "frac_of_floor": round(floor["code_stream_us"] / graph_call_us, 4)},
+                           "frac_of_floor": round(floor["code_stream_us"] / dec_graph_us, 4)},
               "floor": floor}
 
     # ---- adapter gradients (dA, dB) of the same layer, outside the timed step
