@@ -168,6 +168,7 @@ LINEAR_SMALL = [
     WL.custom("gemv_r64", 512, 1024, 1, 64, s=1.0),
     WL.custom("gemv_ragged", 320, 4160, 1, 3, s=2.0),       # 3 column chunks, the last 64 wide
     WL.custom("gemv_wide", 128, 11008, 1, 256, s=0.5),      # 6 column chunks, r = 256
+    WL.custom("gemv_k20480", 256, 20480, 1, 64, s=1.0),     # x beyond the persistent kernel's LDS: 5 segments per workgroup
     # one launch forms A x in every workgroup when r <= 16 and d_in <= 4096; else two launches
     WL.custom("gemv_one_r1_k64", 64, 64, 1, 1, s=2.0),
     WL.custom("gemv_one_r16_k4096", 192, 4096, 1, 16, s=1.5),
@@ -296,8 +297,9 @@ def test_decode_gemv_full_size():
 
 # layers of more than 4096 rows take the persistent decode kernel (one workgroup per CU
 # walking many 16-row groups); the first 4096 rows of such a layer, quantised as part of
-# it, form a layer of exactly 256 groups, which takes the one-group-per-workgroup kernel.
-# Both must give the same bits on those rows. Shapes: the one-launch A x form (r <= 16,
+# it, form a layer of exactly 256 groups, which takes the one-group-per-workgroup kernel
+# when a row is one segment (d_in <= 4096) and the persistent kernel with one group per
+# workgroup when it has several. Both must give the same bits on those rows. Shapes: the one-launch A x form (r <= 16,
 # d_in <= 4096), the two-launch form with 1, 2 (the second 64 wide) and 3 segments per
 # row, d_in = 64; 260 row groups (4 workgroups take two, the rest one), 272 (16 take two)
 # and 516 (4 take three, the rest two).
