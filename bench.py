@@ -206,9 +206,13 @@ def layer_leg(qn, torch, WL, name: str, dev) -> dict:
     g_us = graph_call_us(torch, lambda: [qn.linear_fwd(c, A, B, cfg.s, x1, out=y1, workspace=dws) for c in copies],
                          ncopy, max(1, 128 // ncopy))
     nbytes = decode_bytes(cfg)
+    # the floor on this layer: the GEMV's own loads alone and a plain read of the codes,
+    # graph-replayed over the same copies
+    floor = stream_floor(torch, copies, max(1, 128 // ncopy))
     out["decode"] = {"copies": ncopy, "bytes_per_call": nbytes, "call_us_graph_replay": round(g_us, 3),
                      "GBps": round(nbytes / (g_us * 1e-6) / 1e9, 1),
                      "frac_of_hbm_peak": round(nbytes / (g_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "floor": floor, "frac_of_floor": round(floor["code_stream_us"] / g_us, 4),
                      "call_us_back_to_back": round(call_us, 2), "kernel_us": dk}
     # the same with 2 tokens (the persistent GEMV on these layers)
     x2 = bf16(WL.make_x(cfg)[:2])

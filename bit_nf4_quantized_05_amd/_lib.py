@@ -45,6 +45,7 @@ SIGNATURES = {
     "nf4_quantize_ex": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp]),
     "nf4_double_dequant_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
     "qlora_set_fwd_gemm": (_c_int, [_c_int]),
+    "qlora_set_ax_wait": (_c_int, [_c_int]),
     "qlora_linear_fwd_ex": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
                                      _c_float, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i64, _c_vp]),
     "qlora_linear_fwd_noalloc": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int,
@@ -270,6 +271,15 @@ def set_fwd_gemm(form: int) -> int:
     rc = lib().qlora_set_fwd_gemm(int(form))
     if rc < 0:
         raise ValueError(f"unknown forward GEMM form {form}")
+    return rc
+
+
+def set_ax_wait(polls: int) -> int:
+    """qlora_set_ax_wait: polls a persistent one-token GEMV workgroup makes for each
+    published A x slice before forming the slices itself; returns the previous value."""
+    rc = lib().qlora_set_ax_wait(int(polls))
+    if rc < 0:
+        raise ValueError(f"polls must be >= 0, got {polls}")
     return rc
 
 

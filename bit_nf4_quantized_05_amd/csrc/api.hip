@@ -296,6 +296,12 @@ GradWs grad_ws(int64_t d_out, int64_t d_in, int64_t d_seq, int r) {
 }
 }  // namespace
 
+namespace qn {
+// polls a persistent one-token GEMV workgroup makes for each published A x slice word
+// before forming every slice itself (process-wide, gemv.hip); returns the previous value
+int set_ax_polls(int polls);
+}  // namespace qn
+
 // ---- scratch of the allocation-free forward ---------------------------------
 // One static device array (each device holds its own copy, from module load until the
 // process ends). Host code never uses the array's name as an address: the address of
@@ -500,6 +506,11 @@ int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float*
     if (rc) return rc;
     return linear_fwd_run(codes, bc, d_out, d_in, A, B, r, s, X, ldx, d_seq, Y, ldy, static_cast<char*>(workspace),
                           lw, static_cast<hipStream_t>(stream));
+}
+
+int qlora_set_ax_wait(int polls) {
+    if (polls < 0) return -1;
+    return qn::set_ax_polls(polls);
 }
 
 int qlora_set_fwd_gemm(int form) {

@@ -7,6 +7,7 @@
 #include "nf4_device.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace qn {
 namespace {
@@ -15,49 +16,44 @@ namespace {
 // d_seq = 1 (decode), and 2 or 3 tokens. When all of A fits one 4096-column segment
 // with r <= 16 (A <= 128 KB, read from L2 by every workgroup), one launch: each
 // gemv_nf4 workgroup forms s A x itself, wave j the dot product of row j of A with the
-// x segment (of each token) it has staged in LDS anyway. Otherwise (one token, or two
-// on layers of more than 4096 rows) two launches:
-//   lora_ax_partial: the 64-column blocks of x are split into nparts contiguous
-//     slices (nparts * tokens * r <= 1024); workgroup w writes, for every token t and
-//     rank row j, the dot product of A[j] and x_t over slice w to part[w][t][j] (fixed
-//     summation order).
-//   gemv_nf4 / gemv_nf4_persist: streams the packed codes once and adds B (s A x),
-//     summing the slice partials in a fixed order: y = W_hat x + B (s A x).
-// Both are deterministic, and every workgroup forms the same s A x bits.
+// x segment (of each token) it has staged in LDS anyway. Otherwise the 64-column
+// blocks of x are split into nparts contiguous slices (nparts * tokens * r <= 1024),
+// and the slice partial of every token t and rank row j (the dot product of A[j] and
+// x_t over the slice, fixed summation order) is formed
+//   - for one token on the persistent GEMV: inside the same launch, slice p by its
+//     workgroup p, published as 64-bit (value, tag) words that the other workgroups
+//     wait for (bounded, then forming the slices themselves);
+//   - otherwise by lora_ax_partial, launched first, into part[w][t][j].
+// gemv_nf4 / gemv_nf4_persist stream the packed codes once and add B (s A x), summing
+// the slice partials in slice order: y = W_hat x + B (s A x). Every path is
+// deterministic and forms the same s A x bits.
 // ---------------------------------------------------------------------------
 constexpr int kAxMaxParts = 16;
 
-// T tokens (rows of x at stride ldx): part[(w T + t) r + j] (the one-token layout for T = 1)
+// The A x slice of 64-column blocks [b_lo, b_hi): thread tid < 256 (of a workgroup of
+// 256 or more) accumulates, for rank row j = tid % r, the blocks b_lo + tid / r,
+// + 256 / r, ... of every token (x rows at stride ldx) in a fixed order; the slice sum
+// of row j is then ax_slice_sum over the 256 / r threads of row j, in thread order.
+// The slice kernel and the persistent GEMV's in-launch slices both run these two
+// functions, so they form the same bits.
 template <int T>
-__global__ __launch_bounds__(256)
-void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint16_t* __restrict__ x,
-                            int64_t ldx, int r, int blocks_per_part, float* __restrict__ part) {
-    __shared__ float red[T][256];
-    const int tid = threadIdx.x;
-    const int groups = 256 / r;                   // threads per rank row
-    const int nb64 = d_in / 64;
-    const int b_lo = blockIdx.x * blocks_per_part;
-    const int b_hi = min(b_lo + blocks_per_part, nb64);
-    float acc[T];
+__device__ __forceinline__ void ax_slice_acc(const uint16_t* __restrict__ A, int d_in, const uint16_t* __restrict__ x,
+                                             int64_t ldx, int r, int b_lo, int b_hi, int tid, float (&acc)[T]) {
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+    const int groups = 256 / r;                   // threads per rank row
     if (tid < groups * r) {
         const int j = tid % r;
         for (int b = b_lo + tid / r; b < b_hi; b += groups) {
             const uint4* ar = reinterpret_cast<const uint4*>(A + static_cast<int64_t>(j) * d_in + b * 64);
-            uint4 av[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) av[e] = ar[e];
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const uint4* xr = reinterpret_cast<const uint4*>(x + t * ldx + static_cast<int64_t>(b) * 64);
-                uint4 xv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xv[e] = xr[e];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t aw[4] = {av[e].x, av[e].y, av[e].z, av[e].w};
-                    const uint32_t xw[4] = {xv[e].x, xv[e].y, xv[e].z, xv[e].w};
+                    const uint4 av = ar[e], xv = xr[e];
+                    const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
+                    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         acc[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[q]),
@@ -66,16 +62,34 @@ void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint
             }
         }
     }
+}
+
+// red = the 256 accumulators of one token (LDS); rank row j < r
+__device__ __forceinline__ float ax_slice_sum(const float* red, int r, int j) {
+    float v = 0.0f;
+    for (int g = 0; g < 256 / r; ++g) v += red[g * r + j];
+    return v;
+}
+
+// T tokens (rows of x at stride ldx): part[(w T + t) r + j] (the one-token layout for T = 1)
+template <int T>
+__global__ __launch_bounds__(256)
+void lora_ax_partial_kernel(const uint16_t* __restrict__ A, int d_in, const uint16_t* __restrict__ x,
+                            int64_t ldx, int r, int blocks_per_part, float* __restrict__ part) {
+    __shared__ float red[T][256];
+    const int tid = threadIdx.x;
+    const int nb64 = d_in / 64;
+    const int b_lo = blockIdx.x * blocks_per_part;
+    const int b_hi = min(b_lo + blocks_per_part, nb64);
+    float acc[T];
+    ax_slice_acc<T>(A, d_in, x, ldx, r, b_lo, b_hi, tid, acc);
 #pragma unroll
     for (int t = 0; t < T; ++t) red[t][tid] = acc[t];
     __syncthreads();
     if (tid < r) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            float v = 0.0f;
-            for (int g = 0; g < groups; ++g) v += red[t][g * r + tid];
-            part[(static_cast<int64_t>(blockIdx.x) * T + t) * r + tid] = v;
-        }
+        for (int t = 0; t < T; ++t)
+            part[(static_cast<int64_t>(blockIdx.x) * T + t) * r + tid] = ax_slice_sum(red[t], r, tid);
     }
 }
 
@@ -402,7 +416,17 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 // for the current unit's loads only: with a load count that depended on the path, it
 // had waited for all loads in flight (the next unit's too) before computing.
 // x (d_in <= kGvXMax) is staged in LDS whole, once, with the tables and s (A x), which
-// the one-launch form (r <= 16, d_in <= 4096) forms once per workgroup. Each row's
+// the one-launch form (r <= 16, d_in <= 4096) forms once per workgroup. With one token
+// and larger A (kPub) the A x slices are formed in this launch: workgroup p < nparts
+// starts slice p before its staging barrier and stores each sum with its word's tag + 1
+// in one 64-bit agent-scope store; every thread notes at its start the tag of the word it
+// gathers, and at the first row end (the same unit for every wave of a workgroup) polls
+// it until the tag has advanced by one, which only this launch's producer does, so any
+// prior content of the words is harmless. A wait that runs out (a producer not yet
+// resident, or a word published before the tag was noted) makes the workgroup form every
+// slice itself, with the same arithmetic: the outputs are the same bits in every case.
+// (Against the slice kernel launched first: 11008 x 4096 and 4096 x 11008 at r = 64
+// 5-7 % faster per call, 28672 x 8192 within 1 %.) Each row's
 // sums run in the order of gemv_nf4_kernel, so the outputs are the same bits. With one
 // workgroup of 16 rows per CU and round, the kernel above waits out a full load
 // latency per round (28672 x 8192: 7 rounds, 54 us for 126 MB).
@@ -410,6 +434,8 @@ void gemv_nf4_kernel(const uint4* __restrict__ codes, BlockConsts bc,
 constexpr int kGvXMax = 16384;            // x held whole in LDS (32 KB), one token
 constexpr int kGvXMaxT = 8192;            // the same with 2 or 3 tokens (16 KB each)
 constexpr int kGvPersistWgs = 256;        // one workgroup per CU
+constexpr int kAxSpin = 64;               // default polls of a published A x word before forming the slices locally
+std::atomic<int> g_ax_polls{kAxSpin};
 
 struct GvUnit {
     uint4 cw[2];            // code words of the two chunks
@@ -421,11 +447,11 @@ struct GvUnit {
 // T = 1, 2 or 3 tokens (x and y rows at strides ldx, ldy): each code-pair lookup serves
 // every token, with per token the dot order of the one-token form; s (A x) per token
 // at s_t[16 t + j] (one-launch form) or s_t[t r + j] (from the T-token slice partials).
-template <int T, bool kAx>
+template <int T, bool kAx, bool kPub>
 __global__ __launch_bounds__(1024)
 void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out, int d_in,
                       const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ B, int r, float s,
-                      const float* __restrict__ part, int nparts, const uint16_t* __restrict__ A,
+                      float* __restrict__ part, int nparts, int per, int ax_polls, const uint16_t* __restrict__ A,
                       uint16_t* __restrict__ y, int64_t ldy, NF4Tables tab) {
     constexpr int kBw = kAx ? 1 : 4;              // 64-entry pieces of a row of B (r <= 16 in the one-launch form)
     constexpr int kX = T == 1 ? kGvXMax : kGvXMaxT;
@@ -435,6 +461,8 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
     __shared__ float tvs[1024];
     __shared__ float qlut[256];
     __shared__ float s_t[T * 256];
+    __shared__ float red[kPub ? T : 1][256];
+    __shared__ int ax_late;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -447,6 +475,27 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
     const int my_groups = (ngroups - static_cast<int>(blockIdx.x) + grid - 1) / grid;
     const int nunits = my_groups * nseg;
     const uint4* x4 = reinterpret_cast<const uint4*>(x);
+    // two-launch form: the slice partials of A x are formed in this launch (workgroup p <
+    // nparts forms slice p) and published as 64-bit words (value bits, tag) in part; each
+    // thread notes, at its start, the tag of the word it will gather (nw <= 1024 words)
+    // and waits for that tag + 1, which only this launch's producer writes (so any prior
+    // content of part is harmless)
+    uint64_t* words = reinterpret_cast<uint64_t*>(part);
+    const int nw = kPub ? nparts * T * r : 0;
+    const bool producer = kPub && static_cast<int>(blockIdx.x) < nparts;
+    uint32_t gtag = 0;
+    uint32_t ptag[T];
+    if constexpr (kPub) {
+        if (tid < nw)
+            gtag = static_cast<uint32_t>(__hip_atomic_load(words + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            ptag[t] = 0;
+            if (producer && tid < r)
+                ptag[t] = static_cast<uint32_t>(__hip_atomic_load(words + (blockIdx.x * T + t) * r + tid,
+                                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+        }
+    }
 
     // ---- x whole (chunk c of segment c / 512 at its swizzled place; zero past d_in),
     // A rows or the A x slice partials, tables
@@ -461,7 +510,8 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         const uint4* ar = reinterpret_cast<const uint4*>(A) + static_cast<int64_t>(min(wave, r - 1)) * nch;
 #pragma unroll
         for (int e = 0; e < 8; ++e) av[e] = ar[min(lane + 64 * e, nch - 1)];
-    } else {
+    } else if constexpr (!kPub) {
+        // the slice partials of the slice kernel (launched before this one)
         if (wave >= 10 && wave < 14)
             tst = reinterpret_cast<const uint4*>(part)[min(tid - 640, (nparts * T * r + 3) / 4 - 1)];
     }
@@ -490,6 +540,19 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
         unit_issue(g0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kPub) {
+        // slice p = blockIdx.x of A x from A and x in memory (the slice kernel's
+        // arithmetic), started before the staging barrier, which also orders red
+        if (producer) {
+            float pacc[T];
+            const int b_lo = static_cast<int>(blockIdx.x) * per;
+            ax_slice_acc<T>(A, d_in, x, ldx, r, b_lo, min(b_lo + per, nbpr), tid, pacc);
+            if (tid < 256) {
+#pragma unroll
+                for (int k = 0; k < T; ++k) red[k][tid] = pacc[k];
+            }
+        }
+    }
     {
         const int pr = tid >> 2;
         float lo = tab.code[0], hi = tab.code[0];
@@ -510,7 +573,8 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             const int c = tid + 1024 * i;
             if (c < nseg * (kGvSeg / 8)) xs[t][(c & ~511) + gv_xpos(c & 511)] = c < nch ? xr[t][i] : uint4{0, 0, 0, 0};
         }
-    if (!kAx && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
+    if (!kAx && !kPub && wave >= 10 && wave < 14) reinterpret_cast<uint4*>(tvs)[tid - 640] = tst;
+    if (tid == 0) ax_late = 0;
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     if constexpr (kAx) {
@@ -541,13 +605,24 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             if (lane == 0 && wave < r) s_t[16 * k + wave] = s * t;
             if constexpr (T > 1) __builtin_amdgcn_sched_barrier(0);
         }
-    } else {
+    } else if constexpr (!kPub) {
         if (tid < r) {
 #pragma unroll
             for (int k = 0; k < T; ++k) {
                 float t = 0.0f;
                 for (int p = 0; p < nparts; ++p) t += tvs[(p * T + k) * r + tid];
                 s_t[k * r + tid] = s * t;
+            }
+        }
+    } else if (producer) {
+        // the slice sums, published with their words' tags + 1 in one 64-bit store each
+        if (tid < r) {
+#pragma unroll
+            for (int k = 0; k < T; ++k) {
+                const float v = ax_slice_sum(red[k], r, tid);
+                const uint64_t w = (static_cast<uint64_t>(ptag[k] + 1u) << 32) | __float_as_uint(v);
+                __hip_atomic_store(words + (blockIdx.x * T + k) * r + tid, w, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -560,6 +635,64 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
     float acc[T];
 #pragma unroll
     for (int k = 0; k < T; ++k) acc[k] = 0.0f;
+    // two-launch form, at the first row end of the workgroup's waves (the same unit for
+    // all of them): gather the published slice words into LDS, each with a bounded wait;
+    // if any wait ran out (a producer not yet resident, or its word published before this
+    // workgroup noted the tag), the workgroup forms every slice itself. Then s (A x) as
+    // the slice partials' sum in slice order.
+    auto ax_gather = [&]() {
+        if (tid < nw) {
+            uint64_t w = 0;
+            for (int it = 0;; ++it) {
+                w = __hip_atomic_load(words + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (static_cast<uint32_t>(w >> 32) == gtag + 1u) break;
+                if (it >= ax_polls) {
+                    ax_late = 1;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+            tvs[tid] = __uint_as_float(static_cast<uint32_t>(w));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (__builtin_amdgcn_readfirstlane(ax_late)) {
+            for (int p = 0; p < nparts; ++p) {
+                // token by token (each token's sum runs in the same order as in the
+                // producers' all-token pass)
+                for (int k = 0; k < T; ++k) {
+                    float pacc[1];
+                    ax_slice_acc<1>(A, d_in, x + k * ldx, ldx, r, p * per, min(p * per + per, nbpr), tid, pacc);
+                    if (tid < 256) red[k][tid] = pacc[0];
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                if (tid < r) {
+#pragma unroll
+                    for (int k = 0; k < T; ++k) tvs[(p * T + k) * r + tid] = ax_slice_sum(red[k], r, tid);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+        }
+        if (tid < r) {
+#pragma unroll
+            for (int k = 0; k < T; ++k) {
+                float t = 0.0f;
+                for (int p = 0; p < nparts; ++p) t += tvs[(p * T + k) * r + tid];
+                s_t[k * r + tid] = s * t;
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // rank-r term of a row, row sum, store (the order of gemv_nf4_kernel)
+    auto finish_row = [&](float v, const uint16_t (&bw)[4], int row, int k) {
+#pragma unroll
+        for (int i = 0; i < kBw; ++i) {
+            const int j = lane + 64 * i;
+            if (j < r) v += bf16_to_f32(bw[i]) * s_t[(kAx ? 16 : r) * k + j];
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (lane == 0 && row < d_out) y[k * ldy + row] = bf16_bits(v);
+    };
     auto unit = [&](const GvUnit& cur, GvUnit& nxt, int u, bool issue) {
         if (issue) {
             unit_issue(nxt, min(u + 1, nunits - 1));
@@ -605,19 +738,15 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
             }
         }
         if (S == nseg - 1) {
-            // rank-r term of the row, row sum, store (the order of gemv_nf4_kernel)
             const int row = (static_cast<int>(blockIdx.x) + gi * grid) * kGvWaves + wave;
+            if constexpr (kPub) {
+                if (gi == 0) ax_gather();
+            }
+            finish_row(acc[0], cur.bw, row, 0);
+            acc[0] = 0.0f;
 #pragma unroll
-            for (int k = 0; k < T; ++k) {
-                float v = acc[k];
-#pragma unroll
-                for (int i = 0; i < kBw; ++i) {
-                    const int j = lane + 64 * i;
-                    if (j < r) v += bf16_to_f32(cur.bw[i]) * s_t[(kAx ? 16 : r) * k + j];
-                }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-                if (lane == 0 && row < d_out) y[k * ldy + row] = bf16_bits(v);
+            for (int k = 1; k < T; ++k) {
+                finish_row(acc[k], cur.bw, row, k);
                 acc[k] = 0.0f;
             }
         }
@@ -641,6 +770,8 @@ void gemv_nf4_persist(const uint4* __restrict__ codes, BlockConsts bc, int d_out
 
 }  // namespace
 
+int set_ax_polls(int polls) { return g_ax_polls.exchange(polls); }
+
 bool gemv_takes_tokens(int64_t d_seq, int64_t d_out, int64_t d_in, int r) {
     if (d_seq == 1) return true;
     if (d_seq > kGemvMaxTokens) return false;
@@ -652,7 +783,9 @@ bool gemv_takes_tokens(int64_t d_seq, int64_t d_out, int64_t d_in, int r) {
 }
 
 int64_t gemv_part_floats(int64_t d_seq, int64_t d_in, int r) {
-    return std::min<int64_t>(1024, std::max<int64_t>(1, d_in / 64) * r * d_seq);
+    // up to 1024 slice partials: floats for the slice kernel, 64-bit words (value, tag)
+    // for the persistent GEMV's in-launch slices
+    return 2 * std::min<int64_t>(1024, std::max<int64_t>(1, d_in / 64) * r * d_seq);
 }
 
 hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t d_out, int64_t d_in,
@@ -669,16 +802,25 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
     const bool one_launch = r <= kGvWaves && d_in <= kGvSeg;
     const bool persist = (ngroups > kGvPersistWgs || (nt == 1 && d_in > kGvSeg)) &&
                          d_in <= (nt == 1 ? kGvXMax : kGvXMaxT);
-    const dim3 pgrid(static_cast<unsigned>(std::min<int64_t>(ngroups, kGvPersistWgs)));
+    // (at least one workgroup per A x slice in the two-launch form: a workgroup past the
+    // row groups only forms its slice)
+    const int64_t want_wgs = std::min<int64_t>(ngroups, kGvPersistWgs);
     const uint4* c4 = reinterpret_cast<const uint4*>(codes);
     const int dout = static_cast<int>(d_out), din = static_cast<int>(d_in);
-#define QN_GVP_LAUNCH(TT, AX, NP) \
-    QN_LAUNCH("gemv_nf4_persist", st, (gemv_nf4_persist<TT, AX>), pgrid, dim3(64 * kGvWaves), 0, st, c4, bc, dout, \
-              din, x, ldx, B, r, s, ws_part, NP, A, y, ldy, tables())
+    // slices of A x: at most 16, and nparts * d_seq * r <= 1024 partials in all
+    // (gemv_part_floats); two tokens only in the persistent form
+    const int nb64 = static_cast<int>(d_in / 64);
+    const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / (r * nt)}));
+    const int per = (nb64 + want - 1) / want;
+    const int nparts = (nb64 + per - 1) / per;   // <= want
+    const dim3 pgrid(static_cast<unsigned>(one_launch || nt != 1 ? want_wgs : std::max<int64_t>(want_wgs, nparts)));
+#define QN_GVP_LAUNCH(TT, AX, PUB, NP, PER) \
+    QN_LAUNCH("gemv_nf4_persist", st, (gemv_nf4_persist<TT, AX, PUB>), pgrid, dim3(64 * kGvWaves), 0, st, c4, bc, dout, \
+              din, x, ldx, B, r, s, ws_part, NP, PER, g_ax_polls.load(std::memory_order_relaxed), A, y, ldy, tables())
     if (persist && one_launch) {
-        if (nt == 1) QN_GVP_LAUNCH(1, true, 0);
-        else if (nt == 2) QN_GVP_LAUNCH(2, true, 0);
-        else QN_GVP_LAUNCH(3, true, 0);
+        if (nt == 1) QN_GVP_LAUNCH(1, true, false, 0, 0);
+        else if (nt == 2) QN_GVP_LAUNCH(2, true, false, 0, 0);
+        else QN_GVP_LAUNCH(3, true, false, 0, 0);
         return hipGetLastError();
     }
     if (one_launch) {
@@ -693,22 +835,21 @@ hipError_t launch_gemv_nf4(const uint8_t* codes, const BlockConsts& bc, int64_t 
 #undef QN_GV_LAUNCH
         return hipGetLastError();
     }
-    // slices of A x: at most 16, and nparts * d_seq * r <= 1024 partials in all
-    // (gemv_part_floats); two tokens only in the persistent form
-    const int nb64 = static_cast<int>(d_in / 64);
-    const int want = std::max(1, std::min({kAxMaxParts, nb64, 1024 / (r * nt)}));
-    const int per = (nb64 + want - 1) / want;
-    const int nparts = (nb64 + per - 1) / per;   // <= want
+    if (nt > 2) return hipErrorInvalidValue;
+    if (persist && nt == 1) {
+        // one token: the slices are formed inside the persistent launch (workgroups
+        // 0 .. nparts - 1)
+        QN_GVP_LAUNCH(1, false, true, nparts, per);
+        return hipGetLastError();
+    }
 #define QN_AX_LAUNCH(TT) \
     QN_LAUNCH("lora_ax_partial_kernel", st, lora_ax_partial_kernel<TT>, dim3(nparts), dim3(256), 0, st, A, din, x, \
               ldx, r, per, ws_part)
-    if (nt > 2) return hipErrorInvalidValue;
     if (nt == 1) QN_AX_LAUNCH(1);
     else QN_AX_LAUNCH(2);
 #undef QN_AX_LAUNCH
     if (persist) {
-        if (nt == 1) QN_GVP_LAUNCH(1, false, nparts);
-        else QN_GVP_LAUNCH(2, false, nparts);
+        QN_GVP_LAUNCH(2, false, false, nparts, per);
         return hipGetLastError();
     }
 #undef QN_GVP_LAUNCH

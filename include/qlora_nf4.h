@@ -158,7 +158,7 @@ int nf4_double_dequant_ex(const uint8_t* codes, const int8_t* qconst, const floa
 
 /* Workspace bytes of qlora_linear_fwd(_ex) and of qlora_linear_bwd_x(_ex) for the given
  * sizes (0 on bad sizes). The forward with d_seq <= 64 streams the packed codes and needs
- * only partial sums (at most 4 KB at d_seq = 1); every other call dequantises W
+ * only partial sums (at most 8 KB at d_seq = 1); every other call dequantises W
  * into the workspace (2 bytes per weight). qlora_linear_workspace_bytes is the larger
  * of the two, enough for either call. */
 int64_t qlora_linear_workspace_bytes(int64_t d_out, int64_t d_in, int64_t d_seq, int r);
@@ -206,6 +206,20 @@ int qlora_linear_fwd(const uint8_t* codes, const int8_t* qconst, const float* qs
 #define QN_FWD_GEMM_STAGED 1
 #define QN_FWD_GEMM_FUSED 2
 int qlora_set_fwd_gemm(int form);
+
+/*
+ * qlora_set_ax_wait - how long a one-token forward on the persistent GEMV waits for s (A x)
+ *   [whoami-wesleyyou.top "LoRA": y = W0 x + s B (A x), the rank term of every row]
+ * When the rank term needs the A x slice sums (r > 16 or d_in > 4096) and the layer takes
+ * the persistent GEMV (more than 4096 rows, or rows of several 4096-weight segments), the
+ * first workgroups of the same launch form the slices and publish them; every workgroup
+ * polls for them at most `polls` times per word (default 64, about 20 us) and past that forms every
+ * slice itself. The outputs are the same bits either way (0 makes every workgroup that does
+ * not find the slices already published form them itself: slower, for tests). Process-wide,
+ * for calls made after it returns. Returns the previous value, or -1 (nothing changed) for
+ * polls < 0.
+ */
+int qlora_set_ax_wait(int polls);
 
 /* qlora_linear_fwd for a weight quantised in format dq. */
 int qlora_linear_fwd_ex(const uint8_t* codes, const int8_t* qconst, const float* qscale,

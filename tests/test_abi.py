@@ -209,6 +209,18 @@ def test_profile_durations_validation():
         assert lib.qn_profile_enable(0) == 0
 
 
+def test_ax_wait_setter():
+    """qlora_set_ax_wait returns the previous poll limit and rejects negative values."""
+    prev = qn.set_ax_wait(7)
+    try:
+        assert prev >= 0
+        assert qn.set_ax_wait(0) == 7
+        assert _lib.lib().qlora_set_ax_wait(-1) == -1
+        assert qn.set_ax_wait(prev) == 0
+    finally:
+        qn.set_ax_wait(prev)
+
+
 def test_forward_form_switch():
     """qlora_set_fwd_gemm returns the previous form and rejects unknown values."""
     prev = qn.set_fwd_gemm(qn.FWD_GEMM_STAGED)

@@ -305,6 +305,8 @@ def test_decode_gemv_full_size():
 # and 516 (4 take three, the rest two).
 PERSIST = [
     (4160, 4096, 16, "int8"),
+    (4160, 4096, 64, "int8"),
+    (4160, 2048, 33, "fp8"),
     (4160, 64, 1, "int8"),
     (4352, 4160, 3, "fp8"),
     (4160, 11008, 64, "int8"),
@@ -465,3 +467,70 @@ def test_kernel_timing_records_each_launch_and_changes_no_result():
     assert qn.profile_durations(gemm[0]) == []
     for y in ys:
         assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+
+
+# One token on the persistent GEMV with the A x slices formed in the same launch (r > 16
+# or d_in > 4096): the first workgroups publish each slice as (value, tag) words that the
+# others wait for. Shapes: 512 x 8192 (32 row groups, 16 slices), 64 x 8192 (4 row groups:
+# 12 workgroups only form a slice), 4352 x 4160 at r = 200 (5 slices of 200 ranks), and the
+# MLP down-projection shape. For each: any prior workspace content, HIP graph replays with
+# new x and A in place, and the fallback where every workgroup forms the slices itself (no
+# polling) must give the eager call's bits; the output is checked against float64.
+PUBLISHED_AX = [(512, 8192, 64, "int8"), (64, 8192, 64, "int8"), (4352, 4160, 200, "none"), (4096, 11008, 64, "int8")]
+
+
+@pytest.mark.parametrize("shape", PUBLISHED_AX, ids=[f"{s[0]}x{s[1]}_r{s[2]}_{s[3]}" for s in PUBLISHED_AX])
+def test_decode_with_published_ax_slices(shape):
+    d_out, d_in, r, dq = shape
+    _say(f"[gemv published A x] {d_out}x{d_in} r={r} dq={dq}")
+    cfg = WL.custom("pub_ax", d_out, d_in, 1, r, s=1.25)
+    w = WL.make_weight(cfg)
+    a, b = WL.make_lora(cfg)
+    q = qn.quantize(to_gpu_f32(w), dq=dq)
+    A, B = to_gpu_bf16(a), to_gpu_bf16(b)
+    X = torch.empty(1, d_in, dtype=torch.bfloat16, device=dev())
+    X.copy_(to_gpu_bf16(WL.make_x(cfg)))
+    want = qn.linear_fwd(q, A, B, cfg.s, X).clone()
+    torch.cuda.synchronize()
+    ref = O.quantize(w, dq=dq)
+    wh = O.double_dequant(ref["codes"], ref["qconst"], ref["qscale"], ref["qmean"], d_out, d_in, dq=dq)
+    check_close(bf16_f64(want), O.linear_fwd(wh, a, b, cfg.s, WL.make_x(cfg)), f"decode {d_out}x{d_in} r={r}")
+
+    need = qn.linear_fwd_workspace_bytes(d_out, d_in, 1, r)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev())
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    fills = [lambda t: t.zero_(), lambda t: t.fill_(0xFF),
+             lambda t: t.copy_(torch.randint(0, 256, (need,), generator=gen, dtype=torch.uint8))]
+    for k, fill in enumerate(fills):
+        fill(ws)
+        for i in range(3):
+            got = qn.linear_fwd(q, A, B, cfg.s, X, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"fill {k} call {i}"
+
+    prev = qn.set_ax_wait(0)
+    try:
+        for i in range(2):
+            got = qn.linear_fwd(q, A, B, cfg.s, X, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"no polling, call {i}"
+    finally:
+        qn.set_ax_wait(prev)
+
+    Y = torch.empty(1, d_out, dtype=torch.bfloat16, device=dev())
+    qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qn.linear_fwd(q, A, B, cfg.s, X, out=Y, workspace=ws)
+    tg = torch.Generator(device="cpu").manual_seed(11)
+    for i in range(4):
+        X.copy_(torch.randn(1, d_in, generator=tg).to(torch.bfloat16))
+        A.copy_((torch.randn(r, d_in, generator=tg) * 0.01).to(torch.bfloat16))
+        g.replay()
+        torch.cuda.synchronize()
+        got = Y.clone()
+        eager = qn.linear_fwd(q, A, B, cfg.s, X)                  # eager, its own workspace
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), eager.view(torch.int16)), f"replay {i}"
+    del g
